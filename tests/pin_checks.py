@@ -1,0 +1,326 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check takes the oracle function(s) under test as arguments, so that the
+mutation tests can hand in a deliberately broken copy and confirm the check
+catches it. The checks rely only on: values printed on the pages, hand-worked
+fixtures, closed forms derived from the mask equation, brute force on tiny
+inputs, and library routines (torch CPU attention / softmax, exact integer
+arithmetic in Python).
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_mask_fixture(name: str) -> np.ndarray:
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([c == "1" for c in line])
+    return np.array(rows, dtype=bool)
+
+
+# ---------------------------------------------------------------- mask -----
+
+def zero_based_visible(a: int, c: int, L: int, B: int) -> bool:
+    """The 0-based interval form of the mask, written independently of the oracle."""
+    if a < L:
+        return c <= a
+    t = a - L
+    blk = t // B
+    if c < L:
+        return c < blk * B
+    return blk * B <= c - L <= t
+
+
+def check_mask_fixtures(build):
+    for name, L, B in (("mask_L4_B2.txt", 4, 2), ("mask_L5_B2.txt", 5, 2)):
+        want = load_mask_fixture(name)
+        got = build(L, B)
+        assert got.shape == want.shape, name
+        assert np.array_equal(got, want), name
+
+
+def check_mask_bruteforce(build, max_L: int = 24):
+    for L in range(1, max_L + 1):
+        for B in range(1, L + 1):
+            M = build(L, B)
+            n = 2 * L
+            ref = np.array([[zero_based_visible(a, c, L, B) for c in range(n)]
+                            for a in range(n)], dtype=bool)
+            assert np.array_equal(M, ref), (L, B)
+
+
+def check_mask_closed_forms(build, cases=((7, 3), (16, 4), (33, 8), (64, 16), (12, 1), (9, 9))):
+    for L, B in cases:
+        M = build(L, B)
+        counts = M.sum(axis=1)
+        # clean row a sees a + 1 keys; mask row t sees t + 1 keys, for every B
+        assert np.array_equal(counts[:L], np.arange(1, L + 1)), (L, B)
+        assert np.array_equal(counts[L:], np.arange(1, L + 1)), (L, B)
+        assert int(M.sum()) == L * (L + 1)
+        # the diagonal is always visible; no clean row ever sees the mask stream
+        assert M.diagonal().all()
+        assert not M[:L, L:].any()
+
+
+def check_mask_b1(build, L: int = 11):
+    M = build(L, 1)
+    for t in range(L):
+        vis = np.flatnonzero(M[L + t])
+        want = list(range(t)) + [L + t]  # strictly earlier clean tokens, plus itself
+        assert list(vis) == want, t
+
+
+def check_mask_bL(build, L: int = 10):
+    M = build(L, L)
+    assert not M[L:, :L].any()
+    assert np.array_equal(M[L:, L:], np.tril(np.ones((L, L), dtype=bool)))
+
+
+# ------------------------------------------------------------ attention ----
+
+def sdpa_causal(q, k, v, scale):
+    """Library reference: torch CPU scaled_dot_product_attention, causal, float64."""
+    Q = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))[None]
+    K = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float64))[None]
+    V = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64))[None]
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=scale)
+    return o[0].numpy()
+
+
+def rand_qkv(seed, b, L, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, 2 * L, Hq, d)), rng.standard_normal((b, 2 * L, Hkv, d)),
+            rng.standard_normal((b, 2 * L, Hkv, d)))
+
+
+def check_clean_half_is_causal(attn, L=24, B=4, Hq=4, Hkv=2, d=16):
+    q, k, v = rand_qkv(1, 2, L, Hq, Hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    outs, _ = attn(q, k, v, L, B)
+    g = Hq // Hkv
+    for (bi, h), o in outs.items():
+        ref = sdpa_causal(q[bi, :L, h], k[bi, :L, h // g], v[bi, :L, h // g], scale)
+        np.testing.assert_allclose(o[:L], ref, atol=1e-12, rtol=0)
+
+
+def check_bL_mask_half_is_causal(attn, L=16, Hq=2, Hkv=1, d=8):
+    q, k, v = rand_qkv(2, 1, L, Hq, Hkv, d)
+    scale = 1.0 / np.sqrt(d)
+    outs, _ = attn(q, k, v, L, L)
+    for (bi, h), o in outs.items():
+        ref = sdpa_causal(q[bi, L:, h], k[bi, L:, 0], v[bi, L:, 0], scale)
+        np.testing.assert_allclose(o[L:], ref, atol=1e-12, rtol=0)
+
+
+def check_rows_by_gather(attn, L=20, B=3, Hq=6, Hkv=2, d=8, mask_mode=0):
+    """Each output row equals torch.softmax attention over the keys it may see."""
+    q, k, v = rand_qkv(3, 2, L, Hq, Hkv, d)
+    scale = 0.37
+    outs, lses = attn(q, k, v, L, B, scale=scale, mask_mode=mask_mode)
+    g = Hq // Hkv
+    for (bi, h), o in outs.items():
+        for a in range(2 * L):
+            if mask_mode == 0:
+                keys = [c for c in range(2 * L) if zero_based_visible(a, c, L, B)]
+            else:
+                keys = list(range(a + 1))
+            Q = torch.from_numpy(q[bi, a, h])
+            K = torch.from_numpy(k[bi, keys, h // g])
+            Vv = torch.from_numpy(v[bi, keys, h // g])
+            s = (K @ Q) * scale
+            ref = torch.softmax(s, dim=0) @ Vv
+            np.testing.assert_allclose(o[a], ref.numpy(), atol=1e-12, rtol=0)
+            np.testing.assert_allclose(lses[(bi, h)][a], torch.logsumexp(s, 0).item(),
+                                       atol=1e-12, rtol=0)
+
+
+def check_single_key_rows(attn, L=12, B=4, d=8):
+    """Clean row 0 and mask row t = 0 see exactly one key: their output is V there."""
+    q, k, v = rand_qkv(4, 1, L, 1, 1, d)
+    outs, _ = attn(q, k, v, L, B)
+    o = outs[(0, 0)]
+    np.testing.assert_allclose(o[0], v[0, 0, 0], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(o[L], v[0, L, 0], atol=1e-14, rtol=0)
+
+
+def check_gqa_head_map(attn, L=8, B=2, d=4):
+    """q-head h reads KV head h // (Hq / Hkv): equals the run with K/V repeated per head."""
+    q, k, v = rand_qkv(7, 1, L, 6, 2, d)
+    rep = lambda x: np.repeat(x, 3, axis=2)  # kv head j serves q heads 3j, 3j+1, 3j+2
+    a, _ = attn(q, k, v, L, B)
+    b, _ = attn(q, rep(k), rep(v), L, B)
+    for key in a:
+        np.testing.assert_allclose(a[key], b[key], atol=1e-14, rtol=0)
+
+
+# ------------------------------------------------------------- decode ------
+
+def paged_layout(kv_rows: np.ndarray, page_size: int, seed: int, total_pages: int | None = None):
+    """Scatter logical rows [n, Hkv, d] into pages; returns (K pages, V^T pages, table)."""
+    n, Hkv, d = kv_rows.shape
+    pages_needed = max(1, -(-n // page_size))
+    total = total_pages or pages_needed + 3
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(total)[:pages_needed]
+    K = rng.standard_normal((total, Hkv, page_size, d))
+    for pos in range(n):
+        K[table[pos // page_size], :, pos % page_size, :] = kv_rows[pos]
+    return K, table
+
+
+def check_decode_matches_causal_sdpa(decode, S=3, B=4, Hq=4, Hkv=2, d=8, page=4):
+    rng = np.random.default_rng(5)
+    lens = np.array([0, 5, 13])[:S]
+    max_pages = 5
+    num_pages = S * max_pages
+    table = rng.permutation(num_pages).reshape(S, max_pages).astype(np.int32)
+    Kc = rng.standard_normal((num_pages, Hkv, page, d))
+    Vc = rng.standard_normal((num_pages, Hkv, d, page))
+    q = rng.standard_normal((S, B, Hq, d))
+    kn = rng.standard_normal((S, B, Hkv, d))
+    vn = rng.standard_normal((S, B, Hkv, d))
+    out = decode(q, kn, vn, Kc, Vc, table, lens, page)
+    g = Hq // Hkv
+    for s in range(S):
+        n = int(lens[s])
+        for h in range(Hq):
+            kv = h // g
+            keys = [Kc[table[s, p // page], kv, p % page] for p in range(n)]
+            vals = [Vc[table[s, p // page], kv, :, p % page] for p in range(n)]
+            Kall = np.array(keys + list(kn[s, :, kv])).reshape(n + B, d)
+            Vall = np.array(vals + list(vn[s, :, kv])).reshape(n + B, d)
+            # queries sit at positions n..n+B-1 of the sequence [prefix; new]
+            Qall = np.concatenate([np.zeros((n, d)), q[s, :, h]], axis=0)
+            ref = sdpa_causal(Qall, Kall, Vall, 1.0 / np.sqrt(d))[n:]
+            np.testing.assert_allclose(out[s, :, h], ref, atol=1e-12, rtol=0)
+
+
+def check_decode_equals_two_stream(attn, decode, L=24, B=4, Hq=4, Hkv=2, d=8, page=4):
+    """Mask rows of block b == decode over cache = clean K/V[0:bB] + that block's rows."""
+    q, k, v = rand_qkv(6, 1, L, Hq, Hkv, d)
+    outs, _ = attn(q, k, v, L, B)
+    nblk = L // B
+    for blk in range(nblk):
+        n = blk * B
+        Kc, table = paged_layout(k[0, :n], page, seed=blk)
+        Vrows, _ = paged_layout(v[0, :n], page, seed=blk)
+        Vc = np.ascontiguousarray(Vrows.transpose(0, 1, 3, 2))
+        rows = slice(L + blk * B, L + blk * B + B)
+        out = decode(q[0, rows][None], k[0, rows][None], v[0, rows][None], Kc, Vc,
+                     table[None].astype(np.int32), np.array([n]), page)
+        for h in range(Hq):
+            np.testing.assert_allclose(out[0, :, h], outs[(0, h)][rows], atol=1e-12, rtol=0)
+
+
+# --------------------------------------------------------- confidence ------
+
+def check_confidence_closed_forms(conf_row):
+    V = 1000
+    i, p = conf_row(np.zeros(V))
+    assert i == 0 and abs(p - 1.0 / V) < 1e-15
+    for a, pos in ((3.0, 17), (-2.0, 999), (10.0, 0), (-1.0, 0)):
+        row = np.zeros(V)
+        row[pos] = a
+        i, p = conf_row(row)
+        if a > 0:
+            want_i, want_p = pos, np.exp(a) / (np.exp(a) + V - 1)
+        else:
+            want_i, want_p = (0 if pos != 0 else 1), 1.0 / (V - 1 + np.exp(a))
+        assert i == want_i, (a, pos, i)
+        assert abs(p - want_p) < 1e-14
+    row = np.random.default_rng(0).standard_normal(V)
+    row[[5, 600]] = row.max() + 1.0
+    assert conf_row(row)[0] == 5  # ties go to the lowest id
+
+
+def check_confidence_vs_torch(conf_row, seed=0):
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        row = rng.standard_normal(5000) * rng.uniform(0.1, 6.0) + rng.uniform(-50, 50)
+        i, p = conf_row(row)
+        t = torch.from_numpy(row)
+        assert i == int(torch.argmax(t))
+        assert abs(p - torch.softmax(t, 0).max().item()) < 1e-14
+
+
+# --------------------------------------------------------- acceptance -------
+
+def leading_run_by_string(flags) -> int:
+    s = "".join("1" if f else "0" for f in flags)
+    return len(s) - len(s.lstrip("1"))
+
+
+def check_accept_truth_table(accept_count, max_B=8):
+    for B in range(1, max_B + 1):
+        for flags in itertools.product((False, True), repeat=B):
+            p = [0.95 if f else 0.85 for f in flags]
+            want = max(1, leading_run_by_string(flags))
+            assert accept_count(p, 0.9) == want, (B, flags)
+
+
+def check_accept_rules(accept_count):
+    assert accept_count([0.9, 0.9, 0.9], 0.9) == 3       # p == tau is accepted (>=)
+    assert accept_count([0.95, 0.97, 0.5, 0.99], 0.9) == 2  # stop at the first miss
+    assert accept_count([0.2, 0.99, 0.99], 0.9) == 1     # the first token is forced
+    assert accept_count([0.999999, 0.9999], 1.0) == 1    # tau = 1 behaves as plain AR
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        p = rng.random(8)
+        assert accept_count(p, float(p.min())) == 8      # tau <= min p accepts all B
+        taus = np.sort(rng.random(10))
+        ns = [accept_count(p, t) for t in taus]
+        assert all(a >= b for a, b in zip(ns, ns[1:]))   # non-increasing in tau
+
+
+# ------------------------------------------------------------ commit --------
+
+def check_commit_example(commit):
+    with open(os.path.join(GOLDEN, "commit_example.json")) as f:
+        ex = json.load(f)
+    P, ps, Hkv, d, B = 4, ex["page_size"], 2, 3, ex["B"]
+    rng = np.random.default_rng(0)
+    kc = rng.standard_normal((P, Hkv, ps, d))
+    vc = rng.standard_normal((P, Hkv, d, ps))
+    kn = rng.standard_normal((1, B, Hkv, d))
+    vn = rng.standard_normal((1, B, Hkv, d))
+    table = np.array([ex["block_table"]], dtype=np.int32)
+    k2, v2, ln, pos = commit(kc, vc, table, np.array([ex["cache_len"]]), kn, vn,
+                             np.array([ex["n_accepted"]]), ps)
+    assert list(pos[0]) == ex["commit_pos"]
+    assert int(ln[0]) == ex["cache_len_after"]
+    touched = set()
+    for r, (pg, sl) in enumerate(zip(ex["page_of_row"], ex["slot_of_row"])):
+        np.testing.assert_array_equal(k2[pg, :, sl, :], kn[0, r])
+        np.testing.assert_array_equal(v2[pg, :, :, sl], vn[0, r])
+        touched.add((pg, sl))
+    for pg in range(P):
+        for sl in range(ps):
+            if (pg, sl) not in touched:
+                np.testing.assert_array_equal(k2[pg, :, sl, :], kc[pg, :, sl, :])
+                np.testing.assert_array_equal(v2[pg, :, :, sl], vc[pg, :, :, sl])
+
+
+# ------------------------------------------------------------ LM head -------
+
+def check_lmhead_exact_integers(lmhead):
+    rng = np.random.default_rng(0)
+    N, D, V = 3, 7, 5
+    h = rng.integers(-8, 9, size=(N, D))
+    w = rng.integers(-8, 9, size=(V, D))
+    got = lmhead(h.astype(np.float32), w.astype(np.float32))
+    assert got.shape == (N, V)
+    for n in range(N):
+        for vv in range(V):
+            assert got[n, vv] == sum(int(h[n, k]) * int(w[vv, k]) for k in range(D))

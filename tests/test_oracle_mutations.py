@@ -1,0 +1,181 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+
+Each mutant is a copy of an oracle function with one deliberate error: an
+off-by-one in the block index, a dropped or loosened mask case, the wrong GQA
+head map, a strict comparison, a missing floor, a shifted commit position, the
+wrong tie-break, a transposed operand. Every one must be rejected by at least
+one of the pin checks that the oracle itself passes.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mars_oracle as om
+from tests import pin_checks as pc
+
+_build_mask = om.build_mask  # the unmutated original, captured before any patching
+
+
+def _fails(check, *args, **kw):
+    try:
+        check(*args, **kw)
+    except (AssertionError, IndexError, ValueError):
+        return True
+    return False
+
+
+# -- mask mutants ------------------------------------------------------------
+
+def mask_ceil_on_zero_based(L, B):
+    n = 2 * L
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    bi, bjm, bjc = -(-(i - L) // B), -(-(j - L) // B), -(-j // B)  # 0-based with ceil
+    return (((i < L) & (j < L) & (j <= i)) | ((i >= L) & (j >= L) & (bi == bjm) & (j <= i))
+            | ((i >= L) & (j < L) & (bjc < bi)))
+
+
+def mask_case3_le(L, B):
+    M = _build_mask(L, B)
+    n = 2 * L
+    for i in range(L + 1, n + 1):
+        for j in range(1, L + 1):
+            if om.beta(j, B) <= om.beta(i - L, B):
+                M[i - 1, j - 1] = True
+    return M
+
+
+def mask_bidirectional_block(L, B):
+    M = _build_mask(L, B)
+    n = 2 * L
+    for i in range(L + 1, n + 1):
+        for j in range(L + 1, n + 1):
+            if om.beta(i - L, B) == om.beta(j - L, B):
+                M[i - 1, j - 1] = True
+    return M
+
+
+def mask_no_self(L, B):
+    M = _build_mask(L, B)
+    for a in range(L, 2 * L):
+        M[a, a] = False
+    return M
+
+
+@pytest.mark.parametrize("mutant", [mask_ceil_on_zero_based, mask_case3_le,
+                                    mask_bidirectional_block, mask_no_self])
+def test_mask_mutants_are_caught(mutant):
+    caught = (_fails(pc.check_mask_fixtures, mutant)
+              or _fails(pc.check_mask_bruteforce, mutant, max_L=8)
+              or _fails(pc.check_mask_closed_forms, mutant))
+    assert caught
+
+
+# -- attention mutants ---------------------------------------------------------
+
+def test_wrong_gqa_map_is_caught(monkeypatch):
+    def attn_mod_heads(q, k, v, L, B, scale=None, mask_mode=0, pairs=None, **kw):
+        b, n, Hq, d = q.shape
+        Hkv = k.shape[2]
+        outs, lses = {}, {}
+        for bi in range(b):
+            for h in range(Hq):
+                kk = np.repeat(k[:, :, [h % Hkv]], Hq, axis=2)  # h % Hkv instead of h // g
+                vv = np.repeat(v[:, :, [h % Hkv]], Hq, axis=2)
+                o, l = oracle.attn_two_stream(q, kk, vv, L, B, scale, mask_mode, pairs=[(bi, h)])
+                outs[(bi, h)], lses[(bi, h)] = o[(bi, h)], l[(bi, h)]
+        return outs, lses
+    assert _fails(pc.check_clean_half_is_causal, attn_mod_heads)
+
+
+def test_missing_scale_is_caught():
+    def attn_noscale(q, k, v, L, B, scale=None, mask_mode=0, **kw):
+        return oracle.attn_two_stream(q, k, v, L, B, scale=1.0, mask_mode=mask_mode, **kw)
+    assert _fails(pc.check_clean_half_is_causal, attn_noscale)
+
+
+def test_attention_with_mutant_mask_is_caught(monkeypatch):
+    monkeypatch.setattr(om, "build_mask", mask_bidirectional_block)
+    assert _fails(pc.check_rows_by_gather, oracle.attn_two_stream)
+
+
+def test_decode_without_causal_new_rows_is_caught():
+    def decode_full_block(q, k_new, v_new, k_cache, v_cache, table, lens, page, scale=None, seqs=None):
+        S, B, Hq, d = q.shape
+        Hkv = k_new.shape[2]
+        g = Hq // Hkv
+        out = np.empty((S, B, Hq, d))
+        for s in range(S):
+            n = int(lens[s])
+            for kv in range(Hkv):
+                Kp = om.gather_prefix(k_cache, table, s, n, page, kv, False)
+                Vp = om.gather_prefix(v_cache, table, s, n, page, kv, True)
+                K = np.concatenate([Kp, k_new[s, :, kv]])
+                V = np.concatenate([Vp, v_new[s, :, kv]])
+                for h in range(kv * g, (kv + 1) * g):
+                    out[s, :, h], _ = om._softmax_attend(q[s, :, h], K, V, np.ones((B, n + B), bool),
+                                                          1 / np.sqrt(d))
+        return out
+    assert _fails(pc.check_decode_matches_causal_sdpa, decode_full_block)
+
+
+def test_decode_reading_v_untransposed_is_caught():
+    def decode_v_as_k_layout(q, k_new, v_new, k_cache, v_cache, table, lens, page, **kw):
+        vc = np.ascontiguousarray(v_cache.reshape(k_cache.shape))  # ignores the V^T page layout
+        vt = np.ascontiguousarray(vc.transpose(0, 1, 3, 2))
+        return oracle.attn_block_decode(q, k_new, v_new, k_cache, vt, table, lens, page)
+    assert _fails(pc.check_decode_matches_causal_sdpa, decode_v_as_k_layout)
+
+
+# -- confidence / acceptance / commit / lm-head mutants -------------------------
+
+def test_last_index_tie_break_is_caught():
+    def conf_last(row):
+        row = np.asarray(row, dtype=np.float64)
+        m = row.max()
+        return int(np.flatnonzero(row == m)[-1]), float(1 / np.exp(row - m).sum())
+    assert _fails(pc.check_confidence_closed_forms, conf_last)
+
+
+def test_softmax_without_max_subtraction_in_log_domain_is_caught():
+    def conf_wrong(row):
+        row = np.asarray(row, dtype=np.float64)
+        return int(np.argmax(row)), float(np.exp(row.max()) / np.exp(row).sum() * 1.0001)
+    assert _fails(pc.check_confidence_vs_torch, conf_wrong)
+
+
+def accept_strict(p, tau):
+    n = 0
+    while n < len(p) and p[n] > tau:
+        n += 1
+    return max(n, 1)
+
+
+def accept_no_floor(p, tau):
+    n = 0
+    while n < len(p) and p[n] >= tau:
+        n += 1
+    return n
+
+
+def accept_force_then_scan(p, tau):
+    n = 1
+    while n < len(p) and p[n] >= tau:
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("mutant", [accept_strict, accept_no_floor, accept_force_then_scan])
+def test_accept_mutants_are_caught(mutant):
+    assert _fails(pc.check_accept_truth_table, mutant) or _fails(pc.check_accept_rules, mutant)
+
+
+def test_commit_off_by_one_is_caught():
+    def commit_shifted(kc, vc, table, lens, kn, vn, n, ps):
+        return oracle.commit(kc, vc, table, np.asarray(lens) + 1, kn, vn, n, ps)
+    assert _fails(pc.check_commit_example, commit_shifted)
+
+
+def test_lmhead_transposed_is_caught():
+    assert _fails(pc.check_lmhead_exact_integers, lambda h, w: (np.asarray(w, np.float64) @ np.asarray(h, np.float64).T))
