@@ -1,0 +1,176 @@
+"""Thin torch-facing binding of the four MARS entry points.
+
+Each function checks that the tensors are on the GPU, contiguous and of the
+expected dtype, allocates outputs when the caller did not pass them, and calls
+the C function of the same name on the current HIP stream. All arithmetic
+happens in the library's kernels; nothing here computes a result.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import MARS_BF16, MARS_F32, check
+
+_DT = {torch.float32: MARS_F32, torch.bfloat16: MARS_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+
+
+def mars_attn_two_stream(q, k, v, L: int, B: int, *, o=None, lse=None, return_lse=False,
+                         softmax_scale: float = 0.0, mask_mode: int = 0, stream=None):
+    """Two-stream MARS attention over z = [x; x~].
+
+    q [b, 2L, Hq, d], k/v [b, 2L, Hkv, d] (bf16 or fp32). Returns o (and lse
+    [b, Hq, 2L] fp32 when return_lse or lse is given).
+    """
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, 4)
+    b, n2, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if n2 != 2 * L or k.shape != (b, n2, Hkv, d) or v.shape != k.shape:
+        raise ValueError("shapes must be q [b,2L,Hq,d], k/v [b,2L,Hkv,d]")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", dt)
+    if lse is None and return_lse:
+        lse = torch.empty((b, Hq, n2), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    code = _lib.lib().mars_attn_two_stream(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, L, B, Hq, Hkv, d,
+        _DT.get(dt, -1), float(softmax_scale), int(mask_mode), _stream(stream))
+    check("mars_attn_two_stream", code)
+    return (o, lse) if lse is not None else o
+
+
+def mars_decode_workspace_bytes(S, B, n_q_heads, n_kv_heads, head_dim, page_size, max_pages):
+    return int(_lib.lib().mars_decode_workspace_bytes(S, B, n_q_heads, n_kv_heads, head_dim,
+                                                      page_size, max_pages))
+
+
+def mars_attn_block_decode(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, *,
+                           o=None, workspace=None, status=None, softmax_scale: float = 0.0,
+                           stream=None):
+    """Block-decode attention. q [S,B,Hq,d]; k_new/v_new [S,B,Hkv,d]; K cache
+    [pages,Hkv,page,d]; V cache [pages,Hkv,d,page]; block_table [S,max_pages];
+    cache_len [S] (all on the GPU). Returns o [S,B,Hq,d]."""
+    dt = q.dtype
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, n, dt, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    S, B, Hq, d = q.shape
+    Hkv = k_new.shape[2]
+    num_pages, _, page, _ = k_cache.shape
+    max_pages = block_table.shape[1]
+    if v_cache.shape != (num_pages, Hkv, d, page) or k_cache.shape != (num_pages, Hkv, page, d):
+        raise ValueError("K cache must be [pages,Hkv,page,d] and V cache [pages,Hkv,d,page]")
+    if o is None:
+        o = torch.empty_like(q)
+    need = mars_decode_workspace_bytes(S, B, Hq, Hkv, d, page, max_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    code = _lib.lib().mars_attn_block_decode(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(cache_len), _ptr(o), S, B, Hq, Hkv, d, page, max_pages, num_pages,
+        _DT.get(dt, -1), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(status),
+        _stream(stream))
+    check("mars_attn_block_decode", code)
+    return o
+
+
+def mars_lmhead_workspace_bytes(N, V):
+    return int(_lib.lib().mars_lmhead_workspace_bytes(N, V))
+
+
+def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None,
+                           workspace=None, status=None, stream=None, N=None, V=None):
+    """LM head + confidence. With hidden [N,D] bf16 and w_lm [V,D] bf16, writes fp32
+    logits [N,V]; with hidden None, `logits` is the input. Returns
+    (logits, top_id int32 [N], p_max fp32 [N])."""
+    if hidden is not None:
+        _need(hidden, "hidden", torch.bfloat16, 2)
+        _need(w_lm, "w_lm", torch.bfloat16, 2)
+        N, D = hidden.shape
+        V = w_lm.shape[0]
+        if w_lm.shape[1] != D:
+            raise ValueError("w_lm must be [V, D]")
+        if logits is None:
+            logits = torch.empty((N, V), dtype=torch.float32, device=hidden.device)
+    else:
+        if logits is None:
+            raise ValueError("logits are required when hidden is None")
+        D = 0
+    _need(logits, "logits", torch.float32, 2)
+    N, V = logits.shape
+    dev = logits.device
+    if top_id is None:
+        top_id = torch.empty(N, dtype=torch.int32, device=dev)
+    if p_max is None:
+        p_max = torch.empty(N, dtype=torch.float32, device=dev)
+    need = mars_lmhead_workspace_bytes(N, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    code = _lib.lib().mars_lmhead_confidence(
+        _ptr(hidden), _ptr(w_lm), _ptr(logits), N, D, V, _ptr(top_id), _ptr(p_max),
+        _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))
+    check("mars_lmhead_confidence", code)
+    return logits, top_id, p_max
+
+
+def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
+                       cache_len, *, n_accepted=None, accepted_ids=None, commit_pos=None,
+                       status=None, stream=None):
+    """Acceptance + KV commit. p_max [S,B] fp32, top_id [S,B] int32, tau [S] fp32,
+    k_new/v_new [S,B,Hkv,d]; caches as for decode; cache_len updated in place.
+    Returns (n_accepted [S], accepted_ids [S,B], commit_pos [S,B])."""
+    _need(p_max, "p_max", torch.float32, 2)
+    _need(top_id, "top_id", torch.int32, 2)
+    _need(tau, "tau", torch.float32, 1)
+    dt = k_new.dtype
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, dt, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    S, B = p_max.shape
+    _, _, Hkv, d = k_new.shape
+    num_pages, _, page, _ = k_cache.shape
+    max_pages = block_table.shape[1]
+    dev = p_max.device
+    if n_accepted is None:
+        n_accepted = torch.empty(S, dtype=torch.int32, device=dev)
+    if accepted_ids is None:
+        accepted_ids = torch.empty((S, B), dtype=torch.int32, device=dev)
+    if commit_pos is None:
+        commit_pos = torch.empty((S, B), dtype=torch.int32, device=dev)
+    code = _lib.lib().mars_accept_commit(
+        _ptr(p_max), _ptr(top_id), _ptr(tau), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), _ptr(cache_len), _ptr(n_accepted), _ptr(accepted_ids),
+        _ptr(commit_pos), S, B, Hkv, d, page, max_pages, num_pages, _DT.get(dt, -1),
+        _ptr(status), _stream(stream))
+    check("mars_accept_commit", code)
+    return n_accepted, accepted_ids, commit_pos

@@ -1,0 +1,180 @@
+// Left-to-right acceptance + KV commit for gfx950.
+//
+// Acceptance follows the papernotes.org notes on "MARS: Enabling Autoregressive
+// Models Multi-Token Generation", key design 3 (关键设计 3), and the
+// gist.science explainer, section 2C: scan the B positions left to right,
+// accept while the max-probability is at least tau, stop at the first position
+// below tau, and always accept the first. The accepted tokens then join the
+// persistent prefix KV cache (notes, key design 4 / 关键设计 4).
+//
+// One workgroup per sequence. Lane 0 makes the (tiny, sequential) decision and
+// resolves the destination page of each committed row; then the whole
+// workgroup copies the accepted rows: K rows as 16-byte vectors into the
+// [page][head][slot][d] pages, V rows element-wise into the transposed
+// [page][head][d][slot] pages, with consecutive threads on consecutive slots.
+#include "mars_common.hpp"
+
+using namespace mars;
+
+namespace {
+
+constexpr int kMaxB = 64;
+
+struct CommitArgs {
+  const float* p_max;
+  const int32_t* top_id;
+  const float* tau;
+  const char* k_new;
+  const char* v_new;
+  char* k_cache;
+  char* v_cache;
+  const int32_t* block_table;
+  int32_t* cache_len;
+  int32_t* n_accepted;
+  int32_t* accepted_ids;
+  int32_t* commit_pos;
+  int32_t* status;
+  int S, B, Hkv, D, page_size, max_pages, num_pages;
+};
+
+template <int ES>  // element size in bytes (2 = bf16, 4 = fp32)
+__global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
+  __shared__ int sh_page[kMaxB];
+  __shared__ int sh_len, sh_nc;
+  const int s = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) {
+    const float tau = p.tau[s];
+    const float* pr = p.p_max + (size_t)s * p.B;
+    int n = 0;
+    while (n < p.B && pr[n] >= tau) ++n;  // NaN compares false
+    if (n < 1) n = 1;
+    const int len = p.cache_len[s];
+    const long long cap = (long long)p.max_pages * p.page_size;
+    int nc = 0;
+    int32_t flags = 0;
+    for (int r = 0; r < n; ++r) {
+      const long long pos = (long long)len + r;
+      if (len < 0 || pos >= cap) {
+        flags |= MARS_STATUS_CACHE_OVERFLOW;
+        break;
+      }
+      const int pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
+      if (pg < 0 || pg >= p.num_pages) {
+        flags |= MARS_STATUS_BAD_PAGE;
+        break;
+      }
+      sh_page[r] = pg;
+      ++nc;
+    }
+    if (flags) status_or(p.status, flags);
+    p.n_accepted[s] = n;
+    for (int r = 0; r < p.B; ++r) {
+      p.accepted_ids[(size_t)s * p.B + r] = r < n ? p.top_id[(size_t)s * p.B + r] : -1;
+      p.commit_pos[(size_t)s * p.B + r] = r < nc ? len + r : -1;
+    }
+    sh_len = len;
+    sh_nc = nc;
+  }
+  __syncthreads();
+  const int len = sh_len, nc = sh_nc;
+  const int rowbytes = p.D * ES;   // one head's row
+  const int chunks = rowbytes / 16;
+
+  // K: [page][head][slot][d], 16-byte chunks
+  for (int idx = tid; idx < nc * p.Hkv * chunks; idx += 256) {
+    const int ch = idx % chunks;
+    const int kvh = (idx / chunks) % p.Hkv;
+    const int r = idx / (chunks * p.Hkv);
+    const int pos = len + r;
+    const size_t src = (((size_t)s * p.B + r) * p.Hkv + kvh) * rowbytes + ch * 16;
+    const size_t dst =
+        (((size_t)sh_page[r] * p.Hkv + kvh) * p.page_size + pos % p.page_size) * rowbytes +
+        ch * 16;
+    *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_new + src);
+  }
+  // V: [page][head][d][slot], one element per thread, slot fastest
+  for (int idx = tid; idx < nc * p.Hkv * p.D; idx += 256) {
+    const int r = idx % nc;
+    const int d = (idx / nc) % p.D;
+    const int kvh = idx / (nc * p.D);
+    const int pos = len + r;
+    const size_t src = ((((size_t)s * p.B + r) * p.Hkv + kvh) * p.D + d) * ES;
+    const size_t dst =
+        ((((size_t)sh_page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
+    if (ES == 2)
+      *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_new + src);
+    else
+      *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_new + src);
+  }
+  __syncthreads();
+  if (tid == 0) p.cache_len[s] = len + nc;
+}
+
+}  // namespace
+
+extern "C" int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* tau,
+                                  const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const int32_t* block_table, int32_t* cache_len,
+                                  int32_t* n_accepted, int32_t* accepted_ids,
+                                  int32_t* commit_pos, int32_t S, int32_t B, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t page_size, int32_t max_pages,
+                                  int32_t num_pages, int32_t dtype, int32_t* status,
+                                  void* stream) {
+  MARS_REQUIRE(p_max && top_id && tau && k_new && v_new && k_cache && v_cache && block_table &&
+                   cache_len && n_accepted && accepted_ids && commit_pos,
+               MARS_ERR_NULL);
+  MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
+  MARS_REQUIRE(S >= 1 && S <= (1 << 30) && B >= 1 && B <= kMaxB, MARS_ERR_SHAPE);
+  MARS_REQUIRE(n_kv_heads >= 1 && head_dim >= 8 && head_dim % 8 == 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(page_size >= 1 && max_pages >= 1 && num_pages >= 1, MARS_ERR_SHAPE);
+  MARS_REQUIRE((long long)max_pages * page_size <= (1LL << 30), MARS_ERR_SHAPE);
+  MARS_REQUIRE(mars_aligned16(p_max) && mars_aligned16(top_id) && mars_aligned16(tau) &&
+                   mars_aligned16(k_new) && mars_aligned16(v_new) && mars_aligned16(k_cache) &&
+                   mars_aligned16(v_cache) && mars_aligned16(block_table) &&
+                   mars_aligned16(cache_len) && mars_aligned16(n_accepted) &&
+                   mars_aligned16(accepted_ids) && mars_aligned16(commit_pos),
+               MARS_ERR_ALIGN);
+  CommitArgs a;
+  a.p_max = p_max;
+  a.top_id = top_id;
+  a.tau = tau;
+  a.k_new = (const char*)k_new;
+  a.v_new = (const char*)v_new;
+  a.k_cache = (char*)k_cache;
+  a.v_cache = (char*)v_cache;
+  a.block_table = block_table;
+  a.cache_len = cache_len;
+  a.n_accepted = n_accepted;
+  a.accepted_ids = accepted_ids;
+  a.commit_pos = commit_pos;
+  a.status = status;
+  a.S = S;
+  a.B = B;
+  a.Hkv = n_kv_heads;
+  a.D = head_dim;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == MARS_BF16)
+    hipLaunchKernelGGL(accept_commit_kernel<2>, dim3(S), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(accept_commit_kernel<4>, dim3(S), dim3(256), 0, st, a);
+  return mars_launch_status();
+}
+
+extern "C" const char* mars_strerror(int code) {
+  switch (code) {
+    case MARS_OK: return "ok";
+    case MARS_ERR_NULL: return "a required pointer is NULL";
+    case MARS_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case MARS_ERR_DTYPE: return "unknown dtype code";
+    case MARS_ERR_UNSUPPORTED: return "valid but unsupported configuration";
+    case MARS_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case MARS_ERR_WORKSPACE: return "workspace missing or too small";
+    case MARS_ERR_LAUNCH: return "HIP launch error";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int mars_version(void) { return 100; }

@@ -1,0 +1,276 @@
+// LM-head GEMM + per-position confidence for gfx950.
+//
+// MARS reuses the unchanged LM head to score all B mask positions in one
+// forward, and the confidence of a position is its maximum softmax
+// probability max_v p(x_t = v) (gist.science explainer on "MARS: Enabling
+// Autoregressive Models Multi-Token Generation", sections 2C and 3;
+// papernotes.org notes, key design 3 / 关键设计 3).
+//
+//  * lmhead_gemm_kernel: logits[N, V] = hidden[N, D] . W[V, D]^T on the
+//    32x32x16 bf16 MFMA with fp32 accumulation. A 512-thread workgroup owns
+//    all of up to 256 rows and 128 vocabulary entries, so each weight row is
+//    read from HBM once; K is staged through double-buffered LDS 32 at a time.
+//  * conf_partial_kernel: a row is cut into chunks; each workgroup streams one
+//    chunk once, keeping per-thread (max, first argmax, sum of exp relative to
+//    the running max), and reduces them in the workgroup (sums in fp64).
+//  * conf_merge_kernel: combines the chunks of a row in a fixed order:
+//    top_id = lowest index attaining the maximum, p_max = 1 / sum exp(l - m).
+#include <algorithm>
+
+#include "mars_common.hpp"
+
+using namespace mars;
+
+namespace {
+
+// ------------------------------------------------------------------ GEMM ----
+constexpr int GM = 256;  // rows (positions) per workgroup
+constexpr int GN = 128;  // vocabulary entries per workgroup
+constexpr int GK = 32;   // K per stage
+constexpr int GST = GK + 8;  // LDS row stride (elements)
+
+struct GemmArgs {
+  const bf16_t* hidden;
+  const bf16_t* w;
+  float* logits;
+  int N, D, V;
+};
+
+__global__ __launch_bounds__(512) void lmhead_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][GM * GST];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][GN * GST];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+  const int wn = w >> 1, wv = w & 1;  // 4 x 2 waves, each 64 rows x 64 entries
+  const int v0 = blockIdx.x * GN;
+  const int n0 = blockIdx.y * GM;
+
+  // global -> register staging: A 2 x 16 B per thread, B 1 x 16 B per thread
+  u32x4 areg[2], breg;
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
+      const int row = idx >> 2, ch = idx & 3;
+      const int n = n0 + row;
+      areg[i] = n < p.N ? *(const u32x4*)(p.hidden + (size_t)n * p.D + k0 + ch * 8) : u32x4{};
+    }
+    {
+      const int row = tid >> 2, ch = tid & 3;
+      const int v = v0 + row;
+      breg = v < p.V ? *(const u32x4*)(p.w + (size_t)v * p.D + k0 + ch * 8) : u32x4{};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
+      *(u32x4*)(&As[buf][(idx >> 2) * GST + (idx & 3) * 8]) = areg[i];
+    }
+    *(u32x4*)(&Bs[buf][(tid >> 2) * GST + (tid & 3) * 8]) = breg;
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  const int nk = p.D / GK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load((kt + 1) * GK);
+    const bf16_t* A = As[kt & 1];
+    const bf16_t* Bm = Bs[kt & 1];
+#pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
+        bfr[t] = *(const bf16x8*)(Bm + (wv * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+    }
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // lane (j, hf) holds C[8*(r/4) + 4*hf + r%4][j]: rows = positions, j = vocab
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int v = v0 + wv * 64 + 32 * b + j;
+      if (v >= p.V) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = n0 + wn * 64 + 32 * a + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (n < p.N) p.logits[(size_t)n * p.V + v] = acc[a][b][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------ confidence ----
+struct ConfPart {
+  float m;
+  int32_t idx;
+  double s;  // sum of exp(l - m) over the chunk
+};
+
+struct ConfArgs {
+  const float* logits;
+  int32_t* top_id;
+  float* p_max;
+  ConfPart* part;
+  int32_t* status;
+  int N, V, nchunk, chunk;  // chunk: elements per chunk, multiple of 4
+};
+
+// Combine (m1, i1, s1) with (m2, i2, s2); ties in m keep the lower index.
+__device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, float m2, int i2,
+                                             double s2) {
+  const float M = fmaxf(m1, m2);
+  const double w1 = m1 == -INFINITY ? 0.0 : (double)fast_exp2((m1 - M) * kLog2e);
+  const double w2 = m2 == -INFINITY ? 0.0 : (double)fast_exp2((m2 - M) * kLog2e);
+  const int idx = m1 > m2 ? i1 : (m2 > m1 ? i2 : min(i1, i2));
+  s1 = s1 * w1 + s2 * w2;
+  m1 = M;
+  i1 = idx;
+}
+
+__global__ __launch_bounds__(256) void conf_partial_kernel(ConfArgs p) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lo = c * p.chunk;
+  const int hi = min(p.V, lo + p.chunk);
+  const float* L = p.logits + (size_t)row * p.V;
+
+  float m = -INFINITY;
+  int idx = 0x7FFFFFFF;
+  float s = 0.f;
+  bool bad = false;
+  for (int i = lo + 4 * tid; i < hi; i += 4 * 256) {
+    const f32x4 x = *(const f32x4*)(L + i);
+    bad |= !(isfinite(x[0]) && isfinite(x[1]) && isfinite(x[2]) && isfinite(x[3]));
+    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (bm > m) {
+      s = m == -INFINITY ? 0.f : s * fast_exp2((m - bm) * kLog2e);
+      m = bm;
+      idx = x[0] == bm ? i : (x[1] == bm ? i + 1 : (x[2] == bm ? i + 2 : i + 3));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += fast_exp2((x[e] - m) * kLog2e);
+  }
+  if (bad) status_or(p.status, MARS_STATUS_NONFINITE);
+
+  double sd = (double)s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(idx, o);
+    const double s2 = __shfl_xor(sd, o);
+    conf_combine(m, idx, sd, m2, i2, s2);
+  }
+  __shared__ float sm[4];
+  __shared__ int si[4];
+  __shared__ double ss[4];
+  const int wv = tid >> 6;
+  if ((tid & 63) == 0) {
+    sm[wv] = m;
+    si[wv] = idx;
+    ss[wv] = sd;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = sm[0];
+    int I = si[0];
+    double S = ss[0];
+    for (int k = 1; k < 4; ++k) conf_combine(M, I, S, sm[k], si[k], ss[k]);
+    ConfPart out;
+    out.m = M;
+    out.idx = I;
+    out.s = S;
+    p.part[(size_t)row * p.nchunk + c] = out;
+  }
+}
+
+__global__ __launch_bounds__(256) void conf_merge_kernel(ConfArgs p) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= p.N) return;
+  const ConfPart* pr = p.part + (size_t)row * p.nchunk;
+  float M = pr[0].m;
+  int I = pr[0].idx;
+  double S = pr[0].s;
+  for (int c = 1; c < p.nchunk; ++c) conf_combine(M, I, S, pr[c].m, pr[c].idx, pr[c].s);
+  p.top_id[row] = I == 0x7FFFFFFF ? 0 : I;
+  p.p_max[row] = (float)(1.0 / S);
+}
+
+void conf_layout(int N, int V, int* nchunk, int* chunk) {
+  int c = std::max(1, std::min(32, (2048 + N - 1) / N));
+  c = std::min(c, std::max(1, (V + 1023) / 1024));
+  int ch = (V + c - 1) / c;
+  ch = (ch + 3) & ~3;
+  c = (V + ch - 1) / ch;
+  *nchunk = c;
+  *chunk = ch;
+}
+
+}  // namespace
+
+extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
+  if (N < 1 || V < 4 || V % 4) return 0;
+  int nchunk, chunk;
+  conf_layout(N, V, &nchunk, &chunk);
+  return (size_t)N * nchunk * sizeof(ConfPart);
+}
+
+extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits,
+                                      int32_t N, int32_t D, int32_t V, int32_t* top_id,
+                                      float* p_max, void* workspace, size_t workspace_bytes,
+                                      int32_t* status, void* stream) {
+  MARS_REQUIRE(logits && top_id && p_max, MARS_ERR_NULL);
+  MARS_REQUIRE(!hidden || w_lm, MARS_ERR_NULL);
+  MARS_REQUIRE(N >= 1 && V >= 4 && V % 4 == 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(N <= 65535, MARS_ERR_SHAPE);  // confidence grid: one row per gridDim.y
+  MARS_REQUIRE((double)N * V < 9.0e18, MARS_ERR_SHAPE);
+  if (hidden) MARS_REQUIRE(D >= GK && D % GK == 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(mars_aligned16(hidden) && mars_aligned16(w_lm) && mars_aligned16(logits) &&
+                   mars_aligned16(top_id) && mars_aligned16(p_max) &&
+                   mars_aligned16(workspace),
+               MARS_ERR_ALIGN);
+  const size_t need = mars_lmhead_workspace_bytes(N, V);
+  MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
+  hipStream_t st = (hipStream_t)stream;
+
+  if (hidden) {
+    GemmArgs g;
+    g.hidden = (const bf16_t*)hidden;
+    g.w = (const bf16_t*)w_lm;
+    g.logits = logits;
+    g.N = N;
+    g.D = D;
+    g.V = V;
+    dim3 grid((V + GN - 1) / GN, (N + GM - 1) / GM);
+    hipLaunchKernelGGL(lmhead_gemm_kernel, grid, dim3(512), 0, st, g);
+  }
+  ConfArgs c;
+  c.logits = logits;
+  c.top_id = top_id;
+  c.p_max = p_max;
+  c.part = (ConfPart*)workspace;
+  c.status = status;
+  c.N = N;
+  c.V = V;
+  conf_layout(N, V, &c.nchunk, &c.chunk);
+  hipLaunchKernelGGL(conf_partial_kernel, dim3(c.nchunk, N), dim3(256), 0, st, c);
+  hipLaunchKernelGGL(conf_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, c);
+  return mars_launch_status();
+}

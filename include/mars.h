@@ -1,0 +1,213 @@
+/*
+ * mars.h — C ABI of the MARS hot-path library (libmars.so, gfx950 / MI355X).
+ *
+ * MARS ("MARS: Enabling Autoregressive Models Multi-Token Generation", Jin,
+ * Wang, Luo, Sun) trains an unchanged autoregressive transformer on a
+ * two-stream input z = [x; x~] under a structured 2L x 2L attention mask, and
+ * at inference appends B [MASK] queries per sequence, scores them with the
+ * ordinary LM head and accepts a left-to-right prefix whose max-probability
+ * stays at or above a threshold tau. This library holds the data-parallel hot
+ * path of that method:
+ *
+ *   mars_attn_two_stream    two-stream masked attention forward (training form)
+ *   mars_attn_block_decode  B mask queries against a paged block-level KV cache
+ *   mars_lmhead_confidence  LM-head GEMM + per-position argmax / max-softmax
+ *   mars_accept_commit      left-to-right acceptance + KV commit of the prefix
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *    allocates no device memory and keeps no state between calls; scratch
+ *    space, where needed, is a caller-provided `workspace` whose size the
+ *    matching *_workspace_bytes() helper returns.
+ *  - Tensors are dense, row-major (C order), in the layouts stated per call.
+ *    Every tensor pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work: they never synchronise the host, never print and
+ *    never allocate. Results are deterministic run to run (no atomics whose
+ *    order could change a value).
+ *  - Return value: MARS_OK (0) or a negative MARS_ERR_* code, checked on the
+ *    host before anything is enqueued (argument errors) or right after the
+ *    launch (MARS_ERR_LAUNCH). A non-zero return means nothing was written.
+ *  - Errors that only the device can see (a cache position beyond the pages a
+ *    sequence owns, a block-table entry outside [0, num_pages), a non-finite
+ *    logit) are OR-ed as bit flags into an optional caller-owned int32
+ *    `status` word (pass NULL to ignore them). Kernels never read or write out
+ *    of bounds because of such input: the affected keys are dropped, the
+ *    affected rows are not written, and the flag is raised.
+ *  - softmax_scale <= 0 selects 1/sqrt(head_dim).
+ */
+#ifndef MARS_H_
+#define MARS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes */
+#define MARS_OK               0
+#define MARS_ERR_NULL        -1  /* a required pointer is NULL                         */
+#define MARS_ERR_SHAPE       -2  /* a size is out of range or sizes disagree           */
+#define MARS_ERR_DTYPE       -3  /* unknown dtype code                                 */
+#define MARS_ERR_UNSUPPORTED -4  /* valid but not built (e.g. this head_dim)           */
+#define MARS_ERR_ALIGN       -5  /* a tensor pointer is not 16-byte aligned            */
+#define MARS_ERR_WORKSPACE   -6  /* workspace NULL or smaller than required            */
+#define MARS_ERR_LAUNCH      -7  /* the HIP runtime reported an error at launch        */
+
+/* dtype codes (element type of Q/K/V/O and of the KV cache) */
+#define MARS_F32  0
+#define MARS_BF16 1
+
+/* Device status bit flags (sticky; OR-ed into *status) */
+#define MARS_STATUS_CACHE_OVERFLOW 1  /* a position reached max_pages * page_size     */
+#define MARS_STATUS_BAD_PAGE       2  /* a block_table entry outside [0, num_pages)   */
+#define MARS_STATUS_NONFINITE      4  /* a logit row held NaN or +-Inf                */
+
+/*
+ * Two-stream MARS attention forward (training form).
+ *
+ * Defines: the 2L x 2L mask M over z = [x; x~] of the papernotes.org notes,
+ * key design 1 (关键设计 1), equation M_ij, with block index
+ * beta(t) = ceil(t / B) on 1-based t: clean rows attend causally to the clean
+ * stream; a mask row attends causally inside its own block of the mask stream
+ * and to the clean tokens of strictly earlier blocks. One forward pass over z,
+ * as in the notes' overall framework (整体框架).
+ * In 0-based form, for query a and key c in [0, 2L), t = a - L, b = t / B:
+ *   a <  L : visible iff c <= a
+ *   a >= L : visible iff c < b*B  or  L + b*B <= c <= a
+ * mask_mode = 1 replaces M by plain causal attention over all 2L positions
+ * (the dense comparison the mask is measured against).
+ *
+ * q   [batch, 2L, n_q_heads,  head_dim]   dtype
+ * k,v [batch, 2L, n_kv_heads, head_dim]   dtype
+ * o   [batch, 2L, n_q_heads,  head_dim]   dtype (written)
+ * lse [batch, n_q_heads, 2L] float32, natural-log sum-exp of the scaled,
+ *     masked scores per row (written); may be NULL.
+ * Query head h reads KV head h / (n_q_heads / n_kv_heads).
+ * Supported: dtype MARS_BF16 with head_dim 64 or 128 (MFMA path);
+ *            dtype MARS_F32  with head_dim 32, 64 or 128.
+ * Limits: 1 <= B <= L, 2L <= 2^30, n_q_heads % n_kv_heads == 0.
+ */
+int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int32_t batch, int32_t L, int32_t B, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                         float softmax_scale, int32_t mask_mode, void* stream);
+
+/*
+ * Block-decode attention (inference form).
+ *
+ * Defines: each sequence appends B [MASK] queries; a single forward scores all
+ * B positions (gist.science explainer, section 2C; papernotes.org notes, key
+ * design 3), with the B mask queries reading the block-level prefix KV cache
+ * (notes, key design 4 (关键设计 4); explainer, section 2D). Row r of sequence
+ * s attends to cache positions 0 .. cache_len[s]-1 and, causally, to the new
+ * rows 0 .. r of the same step.
+ *
+ * q        [S, B, n_q_heads,  head_dim]  bf16
+ * k_new    [S, B, n_kv_heads, head_dim]  bf16  (K of the B new rows)
+ * v_new    [S, B, n_kv_heads, head_dim]  bf16
+ * k_cache  [num_pages, n_kv_heads, page_size, head_dim]  bf16
+ * v_cache  [num_pages, n_kv_heads, head_dim, page_size]  bf16 (V is stored
+ *          transposed inside each page)
+ * block_table [S, max_pages] int32: cache position p of sequence s lives in
+ *          page block_table[s, p / page_size], slot p % page_size.
+ * cache_len   [S] int32 (device): cached prefix length per sequence.
+ * o        [S, B, n_q_heads, head_dim]  bf16 (written)
+ * workspace: >= mars_decode_workspace_bytes(...) bytes of device memory
+ *          (split-K partial results; contents on entry are ignored).
+ * status   optional: MARS_STATUS_CACHE_OVERFLOW if cache_len[s] exceeds
+ *          max_pages * page_size (the excess is ignored), MARS_STATUS_BAD_PAGE
+ *          for a table entry outside [0, num_pages) (its keys are dropped).
+ * Supported: dtype MARS_BF16, head_dim 64 or 128, page_size a multiple of 16,
+ *          1 <= B <= 32, (n_q_heads / n_kv_heads) * B <= 128.
+ */
+int mars_attn_block_decode(const void* q, const void* k_new, const void* v_new,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* cache_len, void* o,
+                           int32_t S, int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, int32_t page_size, int32_t max_pages,
+                           int32_t num_pages, int32_t dtype, float softmax_scale,
+                           void* workspace, size_t workspace_bytes, int32_t* status,
+                           void* stream);
+
+/* Workspace bytes mars_attn_block_decode needs for these sizes (0 on bad sizes). */
+size_t mars_decode_workspace_bytes(int32_t S, int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t max_pages);
+
+/*
+ * LM-head GEMM + confidence.
+ *
+ * Defines: the unchanged LM head produces logits for all B positions in one
+ * forward (gist.science explainer, sections 2C and 3); the confidence of a
+ * position is max_v p(x_t = v) under the softmax of its logits (papernotes.org
+ * notes, key design 3 (关键设计 3)). Per row: m = max_v l_v, top_id = the
+ * smallest v with l_v = m, p_max = 1 / sum_v exp(l_v - m).
+ *
+ * hidden  [N, D] bf16, or NULL: then `logits` is an INPUT and only the
+ *         confidence step runs.
+ * w_lm    [V, D] bf16 (one row per vocabulary entry); ignored if hidden NULL.
+ * logits  [N, V] float32: written (= hidden . w_lm^T, fp32 accumulation) when
+ *         hidden != NULL, read otherwise.
+ * top_id  [N] int32, p_max [N] float32 (written).
+ * workspace >= mars_lmhead_workspace_bytes(N, V) bytes.
+ * status  optional: MARS_STATUS_NONFINITE if a row held NaN/Inf (that row's
+ *         p_max is then NaN or 0).
+ * Limits: D % 32 == 0 when hidden != NULL; V % 4 == 0; N >= 1.
+ */
+int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits, int32_t N,
+                           int32_t D, int32_t V, int32_t* top_id, float* p_max,
+                           void* workspace, size_t workspace_bytes, int32_t* status,
+                           void* stream);
+
+/* Workspace bytes mars_lmhead_confidence needs (0 on bad sizes). */
+size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V);
+
+/*
+ * Left-to-right acceptance + KV commit of the accepted prefix.
+ *
+ * Defines: tokens are accepted from left to right while p_max >= tau, up to
+ * the first position below tau, and at least the first token is always
+ * accepted (papernotes.org notes, key design 3 (关键设计 3); gist.science
+ * explainer, section 2C; tau = 1 gives one token per step). tau is per
+ * sequence and may change between calls (explainer, sections 2C and 5). The
+ * accepted tokens join the persistent prefix cache (notes, key design 4).
+ * Per sequence s:
+ *   n = max(1, length of the leading run of p_max[s, r] >= tau[s])
+ *   accepted_ids[s, r] = top_id[s, r] for r < n, else -1
+ *   rows r < n of k_new/v_new go to cache positions cache_len[s] + r
+ *   commit_pos[s, r] = that position, or -1; cache_len[s] += rows written.
+ *
+ * p_max [S, B] float32, top_id [S, B] int32, tau [S] float32 (device).
+ * k_new, v_new [S, B, n_kv_heads, head_dim] dtype; caches as in
+ * mars_attn_block_decode (K [pages, Hkv, page, d], V [pages, Hkv, d, page]).
+ * cache_len [S] int32, read and updated in place.
+ * n_accepted [S], accepted_ids [S, B], commit_pos [S, B] int32 (written).
+ * status optional: a row that would pass max_pages * page_size is not written
+ * (MARS_STATUS_CACHE_OVERFLOW); a row whose page id is outside [0, num_pages)
+ * is not written (MARS_STATUS_BAD_PAGE); cache_len then advances only by the
+ * rows written before the first such row.
+ * NaN p_max compares false (the scan stops there).
+ * Limits: 1 <= B <= 64; dtype MARS_BF16 or MARS_F32; head_dim % 8 == 0.
+ */
+int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* tau,
+                       const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       const int32_t* block_table, int32_t* cache_len, int32_t* n_accepted,
+                       int32_t* accepted_ids, int32_t* commit_pos, int32_t S, int32_t B,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t max_pages, int32_t num_pages, int32_t dtype, int32_t* status,
+                       void* stream);
+
+/* Human-readable text for a MARS_* return code. */
+const char* mars_strerror(int code);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int mars_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MARS_H_ */

@@ -1,0 +1,147 @@
+"""The C-ABI library: loads, exports every declared symbol, rejects bad arguments
+on the host (no GPU needed: every call here fails its checks before any launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_masked_causal_amd as mars
+from block_masked_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mars.h")
+
+# A fake, 16-byte-aligned device address. It is only ever passed to calls that
+# must be rejected by a host-side check before any kernel is enqueued.
+FAKE = 0x7F0000000000
+MIS = FAKE + 8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mars_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 8
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must match the header"
+
+
+def test_version_and_strerror():
+    assert mars.lib().mars_version() >= 100
+    for code in range(0, -8, -1):
+        assert mars.strerror(code) != "unknown error code"
+    assert mars.strerror(-99) == "unknown error code"
+
+
+def ts(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, batch=1, L=64, B=4, Hq=2, Hkv=2, d=32,
+       dtype=0, mode=0):
+    return mars.lib().mars_attn_two_stream(q, k, v, o, lse, batch, L, B, Hq, Hkv, d, dtype,
+                                           0.0, mode, None)
+
+
+def test_two_stream_argument_checks():
+    assert ts(q=None) == _lib.MARS_ERR_NULL
+    assert ts(dtype=7) == _lib.MARS_ERR_DTYPE
+    assert ts(B=0) == _lib.MARS_ERR_SHAPE
+    assert ts(B=65) == _lib.MARS_ERR_SHAPE          # B > L
+    assert ts(Hq=3, Hkv=2) == _lib.MARS_ERR_SHAPE   # Hq % Hkv != 0
+    assert ts(mode=2) == _lib.MARS_ERR_SHAPE
+    assert ts(q=MIS) == _lib.MARS_ERR_ALIGN
+    assert ts(lse=MIS) == _lib.MARS_ERR_ALIGN
+    assert ts(d=48) == _lib.MARS_ERR_UNSUPPORTED
+    assert ts(d=32, dtype=1) == _lib.MARS_ERR_UNSUPPORTED  # bf16 path: d in {64, 128}
+
+
+def dec(S=2, B=4, Hq=4, Hkv=2, d=128, page=16, max_pages=4, num_pages=8, dtype=1, ws=FAKE,
+        ws_bytes=1 << 30, q=FAKE, table=FAKE):
+    return mars.lib().mars_attn_block_decode(q, FAKE, FAKE, FAKE, FAKE, table, FAKE, FAKE, S, B,
+                                             Hq, Hkv, d, page, max_pages, num_pages, dtype, 0.0,
+                                             ws, ws_bytes, None, None)
+
+
+def test_decode_argument_checks():
+    assert dec(q=None) == _lib.MARS_ERR_NULL
+    assert dec(dtype=5) == _lib.MARS_ERR_DTYPE
+    assert dec(B=33) == _lib.MARS_ERR_SHAPE
+    assert dec(Hq=28, Hkv=4, B=32) == _lib.MARS_ERR_SHAPE  # 7 * 32 packed rows > 128
+    assert dec(page=8) == _lib.MARS_ERR_SHAPE
+    assert dec(page=24) == _lib.MARS_ERR_SHAPE
+    assert dec(num_pages=0) == _lib.MARS_ERR_SHAPE
+    assert dec(dtype=0) == _lib.MARS_ERR_UNSUPPORTED
+    assert dec(d=96) == _lib.MARS_ERR_UNSUPPORTED
+    assert dec(table=MIS) == _lib.MARS_ERR_ALIGN
+    need = mars.mars_decode_workspace_bytes(2, 4, 4, 2, 128, 16, 4)
+    assert need > 0
+    assert dec(ws_bytes=need - 1) == _lib.MARS_ERR_WORKSPACE
+    assert dec(ws=None) == _lib.MARS_ERR_WORKSPACE
+    assert mars.mars_decode_workspace_bytes(2, 4, 4, 2, 96, 16, 4) == 0
+
+
+def test_decode_workspace_grows_with_capacity():
+    a = mars.mars_decode_workspace_bytes(64, 4, 28, 4, 128, 16, 64)
+    b = mars.mars_decode_workspace_bytes(64, 4, 28, 4, 128, 16, 257)
+    assert 0 < a < b
+
+
+def lm(hidden=FAKE, w=FAKE, logits=FAKE, N=16, D=64, V=1000, ws=FAKE, ws_bytes=1 << 20):
+    return mars.lib().mars_lmhead_confidence(hidden, w, logits, N, D, V, FAKE, FAKE, ws, ws_bytes,
+                                             None, None)
+
+
+def test_lmhead_argument_checks():
+    assert lm(logits=None) == _lib.MARS_ERR_NULL
+    assert lm(w=None) == _lib.MARS_ERR_NULL
+    assert lm(V=1002) == _lib.MARS_ERR_SHAPE      # V % 4 != 0
+    assert lm(D=48) == _lib.MARS_ERR_SHAPE        # D % 32 != 0 with an LM head
+    assert lm(N=0) == _lib.MARS_ERR_SHAPE
+    assert lm(logits=MIS) == _lib.MARS_ERR_ALIGN
+    need = mars.mars_lmhead_workspace_bytes(16, 1000)
+    assert need > 0
+    assert lm(ws_bytes=need - 1) == _lib.MARS_ERR_WORKSPACE
+    assert mars.mars_lmhead_workspace_bytes(16, 1001) == 0
+
+
+def ac(p=FAKE, S=4, B=4, Hkv=2, d=32, page=16, max_pages=4, num_pages=16, dtype=1, kc=FAKE):
+    return mars.lib().mars_accept_commit(p, FAKE, FAKE, FAKE, FAKE, kc, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, S, B, Hkv, d, page, max_pages, num_pages,
+                                         dtype, None, None)
+
+
+def test_accept_commit_argument_checks():
+    assert ac(p=None) == _lib.MARS_ERR_NULL
+    assert ac(dtype=3) == _lib.MARS_ERR_DTYPE
+    assert ac(B=0) == _lib.MARS_ERR_SHAPE
+    assert ac(B=65) == _lib.MARS_ERR_SHAPE
+    assert ac(d=12) == _lib.MARS_ERR_SHAPE
+    assert ac(num_pages=0) == _lib.MARS_ERR_SHAPE
+    assert ac(kc=MIS) == _lib.MARS_ERR_ALIGN
+
+
+def test_binding_rejects_cpu_tensors_before_calling():
+    import torch
+    q = torch.zeros(1, 8, 2, 32)
+    with pytest.raises(ValueError):
+        mars.mars_attn_two_stream(q, q, q, 4, 2)
+
+
+def test_oracle_is_not_imported_by_the_package():
+    import sys
+    for name in list(sys.modules):
+        if name == "oracle" or name.startswith("oracle."):
+            mod = sys.modules[name]
+            del mod
+    import importlib
+    importlib.reload(mars)
+    pkg_dir = os.path.dirname(mars.__file__)
+    for fn in os.listdir(pkg_dir):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg_dir, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn
