@@ -1,0 +1,430 @@
+#!/usr/bin/env python3
+"""Benchmark of the MARS hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+
+A step is one pass of the whole hot path over synthetic, Qwen2.5-shaped inputs
+that are resident in HBM before timing starts:
+  1. two-stream MARS attention forward: batch 8, L = 2048 (2L = 4096), B = 4,
+     14 query / 2 KV heads, head_dim 64, bf16;
+  2. one block-decode step at the Qwen2.5-7B shape: 64 sequences with cached
+     prefixes U[512, 4096], B = 4 mask queries, 28/4 heads, head_dim 128:
+     decode attention over the paged cache -> LM head (3584 x 152064, bf16
+     weights) + confidence -> acceptance (tau cycling 1.0 / 0.9 / 0.7) + KV
+     commit of the accepted prefix.
+
+The headline `value` is the useful (unmasked) TFLOP/s of the two-stream
+attention; `accepted_tokens_per_s` is the decode step's accepted tokens per
+second. Per-kernel times come from HIP events recorded on the stream the
+kernels run on. Extras (skippable with --no-extras): the tile-skipping benefit
+at the 7B two-stream shape, a 64-step batched decode loop with a live tau
+switch (accepted tokens/s), and the CPU oracle timed on a bounded sample.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# workload shapes
+TS = dict(batch=8, L=2048, B=4, Hq=14, Hkv=2, d=64)           # two-stream, 0.5B shape
+TS7 = dict(batch=4, L=4096, B=16, Hq=28, Hkv=4, d=128)        # two-stream, 7B shape
+DEC = dict(S=64, B=4, Hq=28, Hkv=4, d=128, lo=512, hi=4096, page=16)
+LM = dict(D=3584, V=152064)
+LOOP = dict(S=256, B=8, Hq=28, Hkv=4, d=128, lo=128, hi=2048, page=16, steps=64, switch=32)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def useful_two_stream_flops(batch, L, B, Hq, d, mask_mode=0):
+    """4*d flops per visible (query, key) pair per query head; every row of the
+    MARS mask sees a+1 (clean) or t+1 (mask) keys, L(L+1) pairs per head; dense
+    causal over 2L sees L(2L+1)."""
+    pairs = L * (L + 1) if mask_mode == 0 else L * (2 * L + 1)
+    return 4.0 * d * pairs * Hq * batch
+
+
+def decode_flops_bytes(cache_len, B, Hq, Hkv, d):
+    lens = np.asarray(cache_len, dtype=np.float64)
+    keys = (B * lens + B * (B + 1) / 2).sum()         # sum over rows of visible keys
+    flops = 4.0 * d * Hq * keys
+    S = lens.size
+    cache_bytes = lens.sum() * Hkv * d * 2 * 2         # K and V, bf16
+    io_bytes = S * B * (Hq * d * 2 * 2 + Hkv * d * 2 * 2)  # q + o, k_new + v_new
+    return flops, cache_bytes + io_bytes
+
+
+def to_dev(t, dev):
+    import torch
+    if getattr(t, "bits", None) is not None:
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(getattr(t, "f32", t))).to(dev)
+
+
+class Timer:
+    """Per-segment HIP event timing on the current stream."""
+
+    def __init__(self, names):
+        import torch
+        self.torch = torch
+        self.names = names
+        self.samples = {n: [] for n in names}
+        self.pending = []
+
+    def start(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.marks = [ev]
+
+    def mark(self):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.marks.append(ev)
+
+    def stop(self):
+        self.pending.append(self.marks)
+
+    def collect(self):
+        for marks in self.pending:
+            for i, n in enumerate(self.names):
+                self.samples[n].append(marks[i].elapsed_time(marks[i + 1]))
+        self.pending = []
+
+    def mean_ms(self, n):
+        return float(np.mean(self.samples[n]))
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def cpu_baseline(q, k, v, budget_s):
+    """The oracle's two-stream attention, timed on whole heads of the 0.5B shape."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    L, B, d = TS["L"], TS["B"], TS["d"]
+    t0 = time.perf_counter()
+    heads = 0
+    for pair in [(b, h) for b in range(TS["batch"]) for h in range(TS["Hq"])]:
+        oracle.attn_two_stream(q.f32, k.f32, v.f32, L, B, pairs=[pair])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = useful_two_stream_flops(1, L, B, heads, d)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {TS['batch'] * TS['Hq']} (batch, head) pairs of the "
+                      f"two-stream 0.5B-shape attention, all {2 * L} rows, float64 numpy "
+                      f"({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(the MARS hot path here is a single-GPU build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    import block_masked_causal_amd as mars
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    mars.lib()
+    t_setup = time.perf_counter()
+
+    # ---- inputs -------------------------------------------------------------
+    log("generating two-stream inputs (0.5B shape)")
+    q, k, v = synth.two_stream_qkv(1002, TS["batch"], TS["L"], TS["Hq"], TS["Hkv"], TS["d"])
+    Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    O = torch.empty_like(Q)
+
+    log("generating decode inputs (7B shape) and LM head")
+    total_steps = args.steps + args.warmup
+    di = synth.decode_inputs(1004, DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"],
+                             DEC["lo"], DEC["hi"], DEC["page"],
+                             extra_capacity=DEC["B"] * (total_steps + 2))
+    dq, dkn, dvn = to_dev(di.q, dev), to_dev(di.k_new, dev), to_dev(di.v_new, dev)
+    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+    bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
+    cl0 = cl.clone()
+    dO = torch.empty_like(dq)
+    dws = torch.empty(mars.mars_decode_workspace_bytes(DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"],
+                                                       DEC["d"], DEC["page"], di.max_pages),
+                      dtype=torch.uint8, device=dev)
+    N = DEC["S"] * DEC["B"]
+    h, w = synth.lmhead_inputs(1004, N, LM["D"], LM["V"])
+    H, W = to_dev(h, dev), to_dev(w, dev)
+    del w
+    logits = torch.empty((N, LM["V"]), dtype=torch.float32, device=dev)
+    top = torch.empty(N, dtype=torch.int32, device=dev)
+    pm = torch.empty(N, dtype=torch.float32, device=dev)
+    lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8,
+                      device=dev)
+    taus = [torch.full((DEC["S"],), t, dtype=torch.float32, device=dev) for t in (1.0, 0.9, 0.7)]
+    n_acc = torch.empty(DEC["S"], dtype=torch.int32, device=dev)
+    acc_ids = torch.empty((DEC["S"], DEC["B"]), dtype=torch.int32, device=dev)
+    cpos = torch.empty((DEC["S"], DEC["B"]), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    seg = ["two_stream", "decode_attn", "lmhead_conf", "accept_commit"]
+    timer = Timer(seg)
+    dec_lens = []
+
+    def step(i, timed):
+        if timed:
+            timer.start()
+        mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O)
+        if timed:
+            timer.mark()
+        mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO, workspace=dws,
+                                    status=status)
+        if timed:
+            timer.mark()
+        mars.mars_lmhead_confidence(H, W, logits, top_id=top, p_max=pm, workspace=lws,
+                                    status=status)
+        if timed:
+            timer.mark()
+        mars.mars_accept_commit(pm.view(DEC["S"], DEC["B"]), top.view(DEC["S"], DEC["B"]),
+                                taus[i % 3], dkn, dvn, kc, vc, bt, cl, n_accepted=n_acc,
+                                accepted_ids=acc_ids, commit_pos=cpos, status=status)
+        if timed:
+            timer.mark()
+            timer.stop()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    lens_before = cl.cpu().numpy().copy()
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect()
+    lens_after = cl.cpu().numpy()
+    accepted = int((lens_after - lens_before).sum())
+    st = int(status.item())
+    if st != 0:
+        log(f"WARNING: device status flags {st}")
+
+    ms_step = wall * 1e3 / args.steps
+    t_ts = timer.mean_ms("two_stream")
+    t_dec = timer.mean_ms("decode_attn")
+    t_lm = timer.mean_ms("lmhead_conf")
+    t_acc = timer.mean_ms("accept_commit")
+    ts_flops = useful_two_stream_flops(TS["batch"], TS["L"], TS["B"], TS["Hq"], TS["d"])
+    value = ts_flops / (t_ts * 1e-3) / 1e12
+    decode_ms = t_dec + t_lm + t_acc
+    acc_tok_s = accepted / (args.steps * decode_ms * 1e-3)
+
+    mean_len = 0.5 * (lens_before + lens_after)
+    dflops, dbytes = decode_flops_bytes(mean_len, DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"])
+    lm_flops = 2.0 * N * LM["D"] * LM["V"]
+    lm_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + N * LM["V"] * 4
+    commit_bytes = accepted / args.steps * DEC["Hkv"] * DEC["d"] * 2 * 2 * 2
+
+    kernels = {
+        "two_stream_attention": roofline("mfma", value, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "block_decode_attention": roofline("hbm", dbytes / (t_dec * 1e-3) / 1e9, PEAK_HBM_GBS,
+                                           "GB/s"),
+        "lmhead_gemm_plus_confidence": roofline(
+            "hbm", (lm_bytes + N * LM["V"] * 4) / (t_lm * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+        "accept_commit": roofline("hbm", commit_bytes / (t_acc * 1e-3) / 1e9, PEAK_HBM_GBS,
+                                  "GB/s"),
+    }
+    kernels["block_decode_attention"]["useful_tflops"] = round(dflops / (t_dec * 1e-3) / 1e12, 3)
+    kernels["lmhead_gemm_plus_confidence"]["useful_tflops"] = round(
+        lm_flops / (t_lm * 1e-3) / 1e12, 3)
+    times = {"two_stream_attention": t_ts, "block_decode_attention": t_dec,
+             "lmhead_gemm_plus_confidence": t_lm, "accept_commit": t_acc}
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N)
+
+    result = {
+        "metric": "MARS-mask attention useful TFLOP/s + accepted tokens/s per decode step",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V and caches, N(0,0.02) LM head; Qwen2.5 shapes)",
+        "config": {
+            "workload": "two-stream MARS attention fwd b=8 2L=4096 B=4 heads 14/2 d=64 "
+                        "+ block-decode step S=64 B=4 cache U[512,4096] heads 28/4 d=128 "
+                        "page 16, LM head 3584x152064, confidence, accept+commit",
+            "two_stream": TS, "decode": DEC, "lm_head": LM,
+        },
+        "accepted_tokens_per_s": round(acc_tok_s, 1),
+        "decode_step_ms": round(decode_ms, 4),
+        "kernel_ms": {k2: round(v2, 4) for k2, v2 in times.items()},
+        "roofline": kernels["two_stream_attention"],
+        "kernels": kernels,
+        "status_flags": st,
+    }
+    result.update(extras)
+    if not args.no_extras:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N):
+    out = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # confidence alone on the same logits: splits the LM-head call into GEMM + confidence
+    top = torch.empty(N, dtype=torch.int32, device=dev)
+    pm = torch.empty(N, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(10):
+        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws)
+    b.record()
+    torch.cuda.synchronize()
+    t_conf = a.elapsed_time(b) / 10
+    out["confidence_only"] = {
+        "rows": N, "vocab": LM["V"], "ms": round(t_conf, 4),
+        "roofline": roofline("hbm", N * LM["V"] * 4 / (t_conf * 1e-3) / 1e9, PEAK_HBM_GBS,
+                             "GB/s")}
+
+    # tile skipping at the 7B two-stream shape: MARS mask vs dense causal over 2L
+    log("two-stream 7B shape: MARS mask vs causal-2L")
+    q, k, v = synth.two_stream_qkv(1003, TS7["batch"], TS7["L"], TS7["Hq"], TS7["Hkv"], TS7["d"])
+    Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    del q, k, v
+    O = torch.empty_like(Q)
+    res = {}
+    for mode in (0, 1):
+        for _ in range(2):
+            mars.mars_attn_two_stream(Q, K, V, TS7["L"], TS7["B"], o=O, mask_mode=mode)
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(5):
+            mars.mars_attn_two_stream(Q, K, V, TS7["L"], TS7["B"], o=O, mask_mode=mode)
+        b.record()
+        torch.cuda.synchronize()
+        res[mode] = a.elapsed_time(b) / 5
+    f0 = useful_two_stream_flops(TS7["batch"], TS7["L"], TS7["B"], TS7["Hq"], TS7["d"], 0)
+    f1 = useful_two_stream_flops(TS7["batch"], TS7["L"], TS7["B"], TS7["Hq"], TS7["d"], 1)
+    out["two_stream_7b"] = {
+        "shape": TS7, "mars_ms": round(res[0], 4), "causal_2L_ms": round(res[1], 4),
+        "mars_useful_tflops": round(f0 / (res[0] * 1e-3) / 1e12, 2),
+        "causal_2L_useful_tflops": round(f1 / (res[1] * 1e-3) / 1e12, 2),
+        "skip_speedup": round(res[1] / res[0], 3)}
+    del Q, K, V, O
+    torch.cuda.empty_cache()
+
+    # batched decode loop with a live tau switch
+    out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
+    return out
+
+
+def decode_loop(mars, synth, torch, dev, status):
+    c = LOOP
+    log("decode loop: S=256 B=8, 64 steps, tau 0.9 -> 0.6 at step 32")
+    di = synth.decode_inputs(1005, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["lo"], c["hi"],
+                             c["page"], extra_capacity=c["steps"] * c["B"])
+    pool = synth.PeakedLogitsPool(1005, c["S"] * c["B"], LM["V"], taus=(0.9, 0.6))
+    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+    bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
+    del di.k_cache, di.v_cache
+    pool_dev = torch.from_numpy(pool.pool).to(dev)
+    logits = torch.empty_like(pool_dev)
+    N = c["S"] * c["B"]
+    rows = torch.arange(N, device=dev)
+    tau = torch.full((c["S"],), 0.9, dtype=torch.float32, device=dev)
+    o = torch.empty((c["S"], c["B"], c["Hq"], c["d"]), dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(mars.mars_decode_workspace_bytes(c["S"], c["B"], c["Hq"], c["Hkv"], c["d"],
+                                                       c["page"], bt.shape[1]),
+                      dtype=torch.uint8, device=dev)
+    lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8, device=dev)
+    top = torch.empty(N, dtype=torch.int32, device=dev)
+    pm = torch.empty(N, dtype=torch.float32, device=dev)
+    n_acc = torch.empty(c["S"], dtype=torch.int32, device=dev)
+    acc_ids = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+    cpos = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+    total_ms = 0.0
+    accepted = []
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for s in range(c["steps"]):
+        if s == c["switch"]:
+            tau.fill_(0.6)  # live threshold change: same buffers, no re-initialisation
+        q, kn, vn = synth.decode_step_tensors(1005, s, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"])
+        Q, KN, VN = to_dev(q, dev), to_dev(kn, dev), to_dev(vn, dev)
+        ids, peak, _ = pool.peaks(s)
+        logits.copy_(pool_dev)
+        logits[rows, torch.from_numpy(ids).to(dev)] = torch.from_numpy(peak).to(dev)
+        a, b = ev(), ev()
+        a.record()
+        mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, o=o, workspace=dws, status=status)
+        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws,
+                                    status=status)
+        mars.mars_accept_commit(pm.view(c["S"], c["B"]), top.view(c["S"], c["B"]), tau, KN, VN,
+                                kc, vc, bt, cl, n_accepted=n_acc, accepted_ids=acc_ids,
+                                commit_pos=cpos, status=status)
+        b.record()
+        torch.cuda.synchronize()
+        total_ms += a.elapsed_time(b)
+        accepted.append(int(n_acc.sum().item()))
+    acc = np.array(accepted, dtype=np.float64)
+    sw = c["switch"]
+    return {
+        "config": {k: c[k] for k in ("S", "B", "Hq", "Hkv", "d", "page", "steps")},
+        "accepted_tokens_per_s": round(acc.sum() / (total_ms * 1e-3), 1),
+        "ms_per_step": round(total_ms / c["steps"], 4),
+        "mean_accepted_per_seq_tau_0.9": round(acc[:sw].mean() / c["S"], 4),
+        "mean_accepted_per_seq_tau_0.6": round(acc[sw:].mean() / c["S"], 4),
+        "note": "per step: decode attention + confidence over 2048 x 152064 fp32 logits + "
+                "accept/commit; the synthetic logits are written outside the timed events",
+    }
+
+
+if __name__ == "__main__":
+    main()
