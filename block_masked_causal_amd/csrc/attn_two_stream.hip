@@ -26,6 +26,8 @@ struct TwoStreamArgs {
   float scale_log2;  // softmax_scale * log2(e): scores are kept in log2 units
   int mask_mode;     // 0 = MARS two-stream mask, 1 = causal over all 2L
   int nqt;           // query tiles per (batch, head)
+  int gh, nhc, rt, nw;  // bf16 path: heads per workgroup, head chunks per group,
+                        // 32-row tiles per workgroup, waves per workgroup
 };
 
 // Visible keys of row a: c < hi1, or lo2 <= c < hi2.
@@ -123,7 +125,6 @@ __global__ __launch_bounds__(64) void two_stream_f32_kernel(TwoStreamArgs p) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct Cfg {
-  static constexpr int BM = 128;      // query rows per workgroup
   static constexpr int BN = 64;       // keys per tile
   static constexpr int KST = D + 8;   // K tile row stride in LDS (elements)
   static constexpr int VST = BN + 4;  // V^T tile row stride in LDS (elements)
@@ -135,93 +136,218 @@ struct Cfg {
   static constexpr size_t LDS_BYTES = 2 * (KSZ + VSZ) * sizeof(bf16_t);
 };
 
+// V^T tiles are stored in groups of 4 keys (8 bytes); group cg of row `row`
+// sits at group position cg ^ vt_swizzle(row). Writers cover rows 8 apart and
+// readers 16 consecutive rows per LDS cycle; this XOR keeps both on distinct
+// banks (the unswizzled write pattern hit the same 2 of 32 banks).
+__device__ __forceinline__ int vt_swizzle(int row) { return (row >> 4) & 15; }
+
+// Rescaling of the running output is deferred until a row maximum grows by
+// more than 2^8: until then exp2(s - m) stays below 256, which neither fp32
+// nor bf16 minds, and the final O / l is unchanged by which m was used.
+constexpr float kLazyRescale = 8.0f;
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+// One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
+// O^T += V^T P^T. MASKED applies the per-element visibility test; unmasked
+// tiles are fully visible to every row of the wave.
+// Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its row, kb = c0 + 4hf.
+template <int D, bool MASKED>
+__device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
+                                          const bf16_t* __restrict__ Vt,
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                          float& m, float& l, float cs, int kb, int lo_a,
+                                          int hi_a, int lo_b, int hi_b, int j, int hf) {
+  using C = Cfg<D>;
+  f32x16 s[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    s[n] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 ka = *(const bf16x8*)(Ks + (32 * n + j) * C::KST + 16 * c + 8 * hf);
+      s[n] = mfma32(ka, qf[c], s[n]);
+    }
+  }
+  if (MASKED) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb + 32 * n + 8 * (r >> 2) + (r & 3);
+        const bool vis = ((c >= lo_a) & (c < hi_a)) | ((c >= lo_b) & (c < hi_b));
+        s[n][r] = vis ? s[n][r] : -INFINITY;
+      }
+  }
+  // row max of the raw scores (the scale is positive, so it commutes with max)
+  float mt = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[n][r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * cs;
+  const bool grow = mt > m + kLazyRescale;
+  if (__ballot(grow)) {
+    const float mnew = grow ? mt : m;
+    const float alpha = fast_exp2(m - mnew);  // 0 when m = -inf, 1 when unchanged
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+    m = mnew;
+  }
+  const float nm = m == -INFINITY ? 0.f : -m;
+  float rsum = 0.f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = fast_exp2(fmaf(s[n][r], cs, nm));
+      rsum += e;
+      pb[2 * n + (r >> 3)][r & 7] = (bf16_t)e;
+    }
+  l += rsum;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int row = 32 * i + j;
+    const bf16_t* vrow = Vt + row * C::VST;
+    const int sw = vt_swizzle(row);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const bf16x4 vlo = *(const bf16x4*)(vrow + 4 * ((4 * kc + hf) ^ sw));
+      const bf16x4 vhi = *(const bf16x4*)(vrow + 4 * ((4 * kc + 2 + hf) ^ sw));
+      const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
+      o[i] = mfma32(va, pb[kc], o[i]);
+    }
+  }
+}
+
+// Key ranges a block of query rows [a0, a_last] needs: r1 = [0, r1_hi) and
+// r2 = [r2_lo, r2_hi); keys below full_below are visible to every row.
+__device__ __forceinline__ void rows_key_ranges(int a0, int a_last, int L, int B, int mode,
+                                                int& r1_hi, int& r2_lo, int& r2_hi,
+                                                int& full_below) {
+  r2_lo = 0;
+  r2_hi = 0;
+  if (mode == 1 || a_last < L) {
+    r1_hi = a_last + 1;
+    full_below = a0 + 1;          // causal: fully visible iff every key <= a0
+  } else if (a0 >= L) {
+    const int t0 = a0 - L, t1 = a_last - L;
+    r1_hi = (t1 / B) * B;         // clean keys of strictly earlier blocks
+    full_below = (t0 / B) * B;
+    r2_lo = L + full_below;       // mask keys of the blocks these rows sit in
+    r2_hi = a_last + 1;
+  } else {
+    r1_hi = a_last + 1;           // rows straddle the stream boundary: test every key
+    full_below = 0;
+  }
+}
+
+// Workgroup = nw waves, each owning one (query head, 32-row tile). The heads
+// of one GQA group that share a K/V head sit side by side (gh heads x rt row
+// tiles = nw), so every K/V tile staged through LDS feeds 32 * nw query rows.
 template <int D>
-__global__ __launch_bounds__(256, 2) void two_stream_bf16_kernel(TwoStreamArgs p) {
+__global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  const int NT = 64 * p.nw;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
 
-  // ---- which (batch, head, query tile): heaviest query tiles first --------
-  const int bh_count = p.batch * p.Hq;
-  const int bh = blockIdx.x % bh_count;
-  const int rank = blockIdx.x / bh_count;
-  const int b = bh / p.Hq, h = bh % p.Hq;
+  // ---- which (batch, KV head, head chunk, query tile) ---------------------
+  // Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8).
+  // When the (batch, KV head) streams split evenly over the XCDs, each XCD owns
+  // whole streams, so every query head reading one K/V stream meets it in one
+  // L2. Within an XCD the streams run one after another, heaviest query tiles
+  // first, with the head chunks of one query tile dispatched side by side.
+  const int nkv = p.batch * p.Hkv;
+  int kvg, hc, rank;
+  if (nkv % kXcds == 0) {
+    const int k = blockIdx.x / kXcds;
+    const int per_stream = p.nhc * p.nqt;
+    kvg = blockIdx.x % kXcds + kXcds * (k / per_stream);
+    rank = (k % per_stream) / p.nhc;
+    hc = k % p.nhc;
+  } else {
+    hc = blockIdx.x % p.nhc;
+    kvg = (blockIdx.x / p.nhc) % nkv;
+    rank = blockIdx.x / (p.nhc * nkv);
+  }
+  const int b = kvg / p.Hkv;
+  const int kvh = kvg % p.Hkv;
+  const int h = kvh * p.group + hc * p.gh + w % p.gh;
+  const int bm = 32 * p.rt;
   int qt;
-  if (p.mask_mode == 0 && (p.L % C::BM) == 0) {
-    const int nqs = p.L / C::BM;  // tiles per stream; clean tile i and mask tile i cost alike
+  if (p.mask_mode == 0 && (p.L % bm) == 0) {
+    const int nqs = p.L / bm;  // tiles per stream; clean tile i and mask tile i cost alike
     qt = (rank & 1) * nqs + (nqs - 1 - (rank >> 1));
   } else {
     qt = p.nqt - 1 - rank;
   }
-  const int a0 = qt * C::BM;
-  const int a_last = min(a0 + C::BM, p.twoL) - 1;
-  const int kvh = h / p.group;
+  const int a0 = qt * bm;
+  const int a_last = min(a0 + bm, p.twoL) - 1;
 
-  // ---- key ranges this query tile needs, and which tiles are fully visible
-  int r1_hi, r2_lo = 0, r2_hi = 0, full_below;
-  if (p.mask_mode == 1 || a_last < p.L) {
-    r1_hi = a_last + 1;
-    full_below = a0 + 1;  // a tile is fully visible iff its last key <= a0
-  } else if (a0 >= p.L) {
-    const int t0 = a0 - p.L, t1 = a_last - p.L;
-    const int b0B = (t0 / p.B) * p.B, b1B = (t1 / p.B) * p.B;
-    r1_hi = b1B;          // clean keys of strictly earlier blocks
-    full_below = b0B;
-    r2_lo = p.L + b0B;    // mask keys of the blocks in this tile
-    r2_hi = a_last + 1;
-  } else {
-    r1_hi = a_last + 1;   // tile straddles the stream boundary: test every key
-    full_below = 0;
-  }
+  // key ranges of the whole workgroup (what gets staged) and of this wave
+  int r1_hi, r2_lo, r2_hi, full_below;
+  rows_key_ranges(a0, a_last, p.L, p.B, p.mask_mode, r1_hi, r2_lo, r2_hi, full_below);
   const int n1 = (r1_hi + C::BN - 1) / C::BN;
   const int n2 = r2_hi > r2_lo ? (r2_hi - r2_lo + C::BN - 1) / C::BN : 0;
   const int ntiles = n1 + n2;
+  const int wa0 = a0 + 32 * (w / p.gh);
+  const bool wave_live = wa0 < p.twoL;
+  const int wa_last = wave_live ? min(wa0 + 31, p.twoL - 1) : wa0;
+  int w1_hi, w2_lo, w2_hi, w_full;
+  rows_key_ranges(wa0, wa_last, p.L, p.B, p.mask_mode, w1_hi, w2_lo, w2_hi, w_full);
 
-  // ---- this lane's query row ----------------------------------------------
-  const int a = a0 + w * 32 + j;
+  // ---- this lane's query row and its visible key intervals ---------------
+  const int a = wa0 + j;
   int hi1, lo2, hi2;
   row_intervals(a, p.L, p.B, p.mask_mode, hi1, lo2, hi2);
-  const bf16_t* Qg = (const bf16_t*)p.q;
+
+  // buffer views: reads past the end of this (batch, head) slice return 0
+  const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
+  const rsrc_t rq = make_rsrc((const bf16_t*)p.q + (size_t)b * p.twoL * qs + (size_t)h * D,
+                              (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t)));
+  const uint32_t kv_bytes = (uint32_t)(((p.twoL - 1) * rs + D) * sizeof(bf16_t));
+  const rsrc_t rk = make_rsrc((const bf16_t*)p.k + (size_t)b * p.twoL * rs + (size_t)kvh * D,
+                              kv_bytes);
+  const rsrc_t rv = make_rsrc((const bf16_t*)p.v + (size_t)b * p.twoL * rs + (size_t)kvh * D,
+                              kv_bytes);
+
   bf16x8 qf[D / 16];
-  if (a < p.twoL) {
-    const bf16_t* qrow = Qg + (((size_t)b * p.twoL + a) * p.Hq + h) * D + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qf[c] = *(const bf16x8*)(qrow + 16 * c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) qf[c] = bf16x8{};
-  }
+  for (int c = 0; c < D / 16; ++c)
+    qf[c] = __builtin_bit_cast(
+        bf16x8, buf_load16(rq, (uint32_t)((a * qs + 16 * c + 8 * hf) * sizeof(bf16_t))));
 
-  const size_t rs = (size_t)p.Hkv * D;  // element stride between consecutive keys
-  const bf16_t* Kg = (const bf16_t*)p.k + (size_t)b * p.twoL * rs + (size_t)kvh * D;
-  const bf16_t* Vg = (const bf16_t*)p.v + (size_t)b * p.twoL * rs + (size_t)kvh * D;
-
-  u32x4 kreg[C::KLOADS];
-  u32x4 vreg[C::VLOADS][4];
+  constexpr int KCH = C::BN * D / 8;                   // 16-byte chunks per K tile
+  constexpr int KMAX = (KCH + 5 * 64 - 1) / (5 * 64);  // per thread, at >= 5 waves
+  constexpr int VMAX = (C::VPATCH + 5 * 64 - 1) / (5 * 64);
+  u32x4 kreg[KMAX];
+  u32x4 vreg[VMAX][4];
 
   auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
 
   auto load_tile = [&](int it) {
     const int c0 = tile_c0(it);
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int idx = tid + 256 * i;
+    for (int i = 0; i < KMAX; ++i) {
+      const int idx = min(tid + NT * i, KCH - 1);
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      const int c = c0 + row;
-      kreg[i] = c < p.twoL ? *(const u32x4*)(Kg + c * rs + ch * 8) : u32x4{};
+      kreg[i] = buf_load16(rk, (uint32_t)(((c0 + row) * rs + ch * 8) * sizeof(bf16_t)));
     }
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int pi = tid + 256 * i;
+    for (int i = 0; i < VMAX; ++i) {
+      const int pi = min(tid + NT * i, C::VPATCH - 1);
       const int dg = pi % (D / 8), kg = pi / (D / 8);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int c = c0 + 4 * kg + rr;
-        vreg[i][rr] = (pi < C::VPATCH && c < p.twoL) ? *(const u32x4*)(Vg + c * rs + dg * 8)
-                                                      : u32x4{};
-      }
+      for (int rr = 0; rr < 4; ++rr)
+        vreg[i][rr] =
+            buf_load16(rv, (uint32_t)(((c0 + 4 * kg + rr) * rs + dg * 8) * sizeof(bf16_t)));
     }
   };
 
@@ -229,14 +355,16 @@ __global__ __launch_bounds__(256, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     bf16_t* Ks = lds + buf * (C::KSZ + C::VSZ);
     bf16_t* Vt = Ks + C::KSZ;
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      *(u32x4*)(Ks + row * C::KST + ch * 8) = kreg[i];
+    for (int i = 0; i < KMAX; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < KCH) {
+        const int row = idx / (D / 8), ch = idx % (D / 8);
+        *(u32x4*)(Ks + row * C::KST + ch * 8) = kreg[i];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int pi = tid + 256 * i;
+    for (int i = 0; i < VMAX; ++i) {
+      const int pi = tid + NT * i;
       if (pi >= C::VPATCH) continue;
       const int dg = pi % (D / 8), kg = pi / (D / 8);
 #pragma unroll
@@ -244,10 +372,14 @@ __global__ __launch_bounds__(256, 2) void two_stream_bf16_kernel(TwoStreamArgs p
         const uint32_t x0 = vreg[i][0][dw], x1 = vreg[i][1][dw];
         const uint32_t x2 = vreg[i][2][dw], x3 = vreg[i][3][dw];
         // dimension 8*dg + 2*dw: low halves; dimension 8*dg + 2*dw + 1: high halves
-        u32x2 lo = {(x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16)};
-        u32x2 hi = {(x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u)};
-        *(u32x2*)(Vt + (8 * dg + 2 * dw) * C::VST + 4 * kg) = lo;
-        *(u32x2*)(Vt + (8 * dg + 2 * dw + 1) * C::VST + 4 * kg) = hi;
+        // byte permutes: lo = {x0.lo16, x1.lo16}, hi = {x0.hi16, x1.hi16}
+        u32x2 lo = {__builtin_amdgcn_perm(x1, x0, 0x05040100u),
+                    __builtin_amdgcn_perm(x3, x2, 0x05040100u)};
+        u32x2 hi = {__builtin_amdgcn_perm(x1, x0, 0x07060302u),
+                    __builtin_amdgcn_perm(x3, x2, 0x07060302u)};
+        const int r0 = 8 * dg + 2 * dw, r1 = r0 + 1;
+        *(u32x2*)(Vt + r0 * C::VST + 4 * (kg ^ vt_swizzle(r0))) = lo;
+        *(u32x2*)(Vt + r1 * C::VST + 4 * (kg ^ vt_swizzle(r1))) = hi;
       }
     }
   };
@@ -261,83 +393,40 @@ __global__ __launch_bounds__(256, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     load_tile(0);
     store_tile(0);
   }
+  // The query fragments must have landed before the loop: otherwise the
+  // wait-count bookkeeping treats them as in flight on every iteration and
+  // each tile would stall on its own prefetch.
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) load_tile(it + 1);
+    // keep the prefetch issued before the compute, and its LDS stores after it
+    __builtin_amdgcn_sched_barrier(0);
 
     const bf16_t* Ks = lds + (it & 1) * (C::KSZ + C::VSZ);
     const bf16_t* Vt = Ks + C::KSZ;
     const int c0 = tile_c0(it);
     const bool in_r1 = it < n1;
-    const int lim_lo = in_r1 ? 0 : r2_lo;
+    const int lim_lo = in_r1 ? 0 : r2_lo;       // the staged range this tile belongs to
     const int lim_hi = in_r1 ? r1_hi : r2_hi;
-    const bool partial = !(in_r1 && c0 + C::BN - 1 < full_below);
-
-    // S^T for two 32-key sub-tiles
-    f32x16 s[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      s[n] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + (32 * n + j) * C::KST + 16 * c + 8 * hf);
-        s[n] = mfma32(ka, qf[c], s[n]);
+    // does this tile hold any key visible to this wave's rows?
+    const int t_lo = max(c0, lim_lo), t_hi = min(c0 + C::BN, lim_hi);
+    const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
+    if (need) {
+      if (in_r1 && c0 + C::BN - 1 < w_full) {
+        tile_step<D, false>(Ks, Vt, qf, o, m, l, p.scale_log2, 0, 0, 0, 0, 0, j, hf);
+      } else {
+        // the row's visible intervals, clipped to this tile's key range
+        const int lo_a = lim_lo, hi_a = min(hi1, lim_hi);
+        const int lo_b = max(lo2, lim_lo), hi_b = min(hi2, lim_hi);
+        tile_step<D, true>(Ks, Vt, qf, o, m, l, p.scale_log2, c0 + 4 * hf, lo_a, hi_a, lo_b,
+                           hi_b, j, hf);
       }
     }
 
-    float mt = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[n][r] * p.scale_log2;
-        if (partial) {
-          const int c = c0 + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = (c >= lim_lo) & (c < lim_hi) & in_rows(c, hi1, lo2, hi2);
-          x = vis ? x : -INFINITY;
-        }
-        s[n][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    const float mb = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mb);
-    float rsum = 0.f;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(s[n][r] - mb);
-        s[n][r] = e;
-        rsum += e;
-      }
-    }
-    l = l * alpha + rsum;
-    m = mnew;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[kc][e] = (bf16_t)s[kc >> 1][8 * (kc & 1) + e];
-    }
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16_t* vr = Vt + (32 * i + j) * C::VST + 16 * kc + 4 * hf;
-        const bf16x4 vlo = *(const bf16x4*)vr;
-        const bf16x4 vhi = *(const bf16x4*)(vr + 8);
-        const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-        o[i] = mfma32(va, pb[kc], o[i]);
-      }
-    }
-
+    __builtin_amdgcn_sched_barrier(0);
     if (it + 1 < ntiles) store_tile((it + 1) & 1);
     __syncthreads();
   }
@@ -358,19 +447,36 @@ __global__ __launch_bounds__(256, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   if (p.lse && hf == 0) p.lse[((size_t)b * p.Hq + h) * p.twoL + a] = (m + log2f(lt)) * kLn2;
 }
 
+// Heads per workgroup: the largest divisor of the GQA group size that is <= 8.
+inline int heads_per_wg(int group) {
+  for (int d = 8; d > 1; --d)
+    if (group % d == 0) return d;
+  return 1;
+}
+
 template <int D>
-int launch_bf16(const TwoStreamArgs& a, hipStream_t st) {
+int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   using C = Cfg<D>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)two_stream_bf16_kernel<D>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)C::LDS_BYTES) != hipSuccess)
-      return MARS_ERR_LAUNCH;
+    (void)hipFuncSetAttribute((const void*)two_stream_bf16_kernel<D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+    (void)hipGetLastError();
     attr_set = true;
   }
-  const int nblocks = a.batch * a.Hq * a.nqt;
-  hipLaunchKernelGGL(two_stream_bf16_kernel<D>, dim3(nblocks), dim3(256), C::LDS_BYTES, st, a);
+  // d = 64: one head x 4 row tiles per workgroup, so that three 4-wave
+  // workgroups share a CU (the kernel is bound by vector-ALU softmax work and
+  // needs the extra waves to hide latency). d = 128: the GQA heads sharing a
+  // K/V head side by side (K/V staging is the larger cost there).
+  a.gh = D == 64 ? 1 : heads_per_wg(a.group);
+  a.nhc = a.group / a.gh;
+  a.rt = D == 64 ? 4 : 8 / a.gh;
+  a.nw = a.gh * a.rt;
+  a.nqt = (a.twoL + 32 * a.rt - 1) / (32 * a.rt);
+  const double nblocks = (double)a.batch * a.Hkv * a.nhc * a.nqt;
+  if (nblocks >= 2147483647.0) return MARS_ERR_SHAPE;
+  hipLaunchKernelGGL(two_stream_bf16_kernel<D>, dim3((unsigned)nblocks), dim3(64 * a.nw),
+                     C::LDS_BYTES, st, a);
   return mars_launch_status();
 }
 
@@ -400,7 +506,8 @@ extern "C" int mars_attn_two_stream(const void* q, const void* k, const void* v,
   const int twoL = 2 * L;
   // Element offsets must fit the kernels' index arithmetic.
   MARS_REQUIRE((double)batch * twoL * n_q_heads * head_dim < 9.0e18, MARS_ERR_SHAPE);
-  MARS_REQUIRE((double)twoL * n_kv_heads * head_dim < 2147483647.0, MARS_ERR_SHAPE);
+  // Buffer loads address one (batch, head) slice with 32-bit byte offsets.
+  MARS_REQUIRE(((double)twoL + 64) * n_q_heads * head_dim * 4 < 2147483647.0, MARS_ERR_SHAPE);
 
   TwoStreamArgs a;
   a.q = q;
@@ -421,8 +528,6 @@ extern "C" int mars_attn_two_stream(const void* q, const void* k, const void* v,
   hipStream_t st = (hipStream_t)stream;
 
   if (dtype == MARS_BF16) {
-    a.nqt = (twoL + Cfg<64>::BM - 1) / Cfg<64>::BM;
-    MARS_REQUIRE((double)batch * n_q_heads * a.nqt < 2147483647.0, MARS_ERR_SHAPE);
     if (head_dim == 64) return launch_bf16<64>(a, st);
     if (head_dim == 128) return launch_bf16<128>(a, st);
     return MARS_ERR_UNSUPPORTED;
