@@ -43,8 +43,68 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// One 32-key step for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// Lane (j, hf) holds the scores of packed query row j against step keys
+// 8*(r/4) + 4*hf + r%4; MASKED keeps only the keys whose bit is set in `live`.
+// The query fragments live in LDS (one 16-byte slot per lane and chunk,
+// written once by the same wave), which keeps the register budget at two
+// waves per SIMD; re-reading them costs far less LDS traffic than the HBM
+// traffic of a step.
+template <int D, bool MASKED>
+__device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
+                                         const bf16x8* __restrict__ qlds, f32x16 (&o)[D / 32],
+                                         float& m, float& l, float cs, uint32_t live, int hf) {
+  f32x16 sc = f32x16{};
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) sc = mfma32(ka[c], qlds[64 * c], sc);
+  if (MASKED) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+      sc[r] = (live >> key) & 1u ? sc[r] : -INFINITY;
+    }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * cs;
+  // deferred rescaling: only when a row maximum grows by more than 2^8
+  const bool grow = mt > m + 8.0f;
+  if (__ballot(grow)) {
+    const float mnew = grow ? mt : m;
+    const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);  // -inf - -inf is NaN
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+    m = mnew;
+  }
+  const float nm = m == -INFINITY ? 0.f : -m;
+  float rsum = 0.f;
+  bf16x8 pb[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float e = fast_exp2(fmaf(sc[r], cs, nm));
+    rsum += e;
+    pb[r >> 3][r & 7] = (bf16_t)e;
+  }
+  l += rsum;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = mfma32(va[i][kc], pb[kc], o[i]);
+}
+
+// Keeps the first n (0..4) bf16 values of a 4-key V group, zeroes the rest.
+__device__ __forceinline__ u32x2 keep_first(u32x2 v, int n) {
+  if (n >= 4) return v;
+  if (n <= 0) return u32x2{};
+  if (n == 1) return u32x2{v[0] & 0xFFFFu, 0u};
+  if (n == 2) return u32x2{v[0], 0u};
+  return u32x2{v[0], v[1] & 0xFFFFu};
+}
+
 template <int D>
-__global__ __launch_bounds__(64 * kMaxQT) void decode_split_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs p) {
   const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
   const int j = lane & 31, hf = lane >> 5;
@@ -67,125 +127,89 @@ __global__ __launch_bounds__(64 * kMaxQT) void decode_split_kernel(DecodeArgs p)
   const bool qvalid = qi < nrows;
   const int qr = qvalid ? qi / p.group : 0;
   const int qh = kvh * p.group + (qvalid ? qi % p.group : 0);
-  bf16x8 qf[D / 16];
+  extern __shared__ bf16x8 qsh[];  // [waves][D / 16][64]
+  bf16x8* qlds = qsh + (size_t)wq * (D / 16) * 64 + lane;
   {
     const bf16_t* qrow = p.q + (((size_t)s * p.B + qr) * p.Hq + qh) * D + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) qf[c] = qvalid ? *(const bf16x8*)(qrow + 16 * c) : bf16x8{};
+    for (int c = 0; c < D / 16; ++c)
+      qlds[64 * c] = qvalid ? *(const bf16x8*)(qrow + 16 * c) : bf16x8{};
   }
 
-  const int32_t* table = p.block_table + (size_t)s * p.max_pages;
-  const size_t kpage = (size_t)p.Hkv * p.page_size * D;  // elements per page (all heads)
-  const bf16_t* kbase = p.k_cache + (size_t)kvh * p.page_size * D;
-  const bf16_t* vbase = p.v_cache + (size_t)kvh * D * p.page_size;
+  // Page ids of this chunk, one per lane (lane t: page k_lo / ps + t); -1 = bad.
+  const int ps = p.page_size;
+  const int pg0 = k_lo / ps;
+  const int npg = k_hi > k_lo ? (k_hi - 1) / ps - pg0 + 1 : 0;
+  int mypage = 0;
+  if (lane < npg) {
+    const int raw = p.block_table[(size_t)s * p.max_pages + pg0 + lane];
+    mypage = (raw >= 0 && raw < p.num_pages) ? raw : -1;
+  }
+  const bool chunk_bad = __ballot(mypage < 0) != 0;
+  if (chunk_bad && lane == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
+
+  const size_t kpage = (size_t)p.Hkv * ps * D;  // elements per page (all heads)
+  const bf16_t* kbase = p.k_cache + (size_t)kvh * ps * D;
+  const bf16_t* vbase = p.v_cache + (size_t)kvh * D * ps;
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;
-  bool bad_page = false;
 
-  auto page_of = [&](int pos, bool& ok) -> int {
-    const int pg = table[pos / p.page_size];
-    ok = (pg >= 0) & (pg < p.num_pages);
-    bad_page |= !ok;
-    return ok ? pg : 0;
-  };
-
-  // One 32-key step: S^T, online softmax, O^T update. `kmask(c)` says whether
-  // key slot c (0..31 within the step) is live for this lane's query.
-  auto step = [&](const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2], auto live) {
-    f32x16 sc = f32x16{};
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) sc = mfma32(ka[c], qf[c], sc);
-    float mt = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float x = live(c) ? sc[r] * p.scale_log2 : -INFINITY;
-      sc[r] = x;
-      mt = fmaxf(mt, x);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    const float mb = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mb);
-    float rsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(sc[r] - mb);
-      sc[r] = e;
-      rsum += e;
-    }
-    l = l * alpha + rsum;
-    m = mnew;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[kc][e] = (bf16_t)sc[8 * kc + e];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      o[i] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) o[i] = mfma32(va[i][kc], pb[kc], o[i]);
-    }
-  };
-
-  // ---- cached prefix keys [k_lo, k_hi) -------------------------------------
   for (int c0 = k_lo; c0 < k_hi; c0 += 32) {
+    // all of this step's K and V loads are issued before any arithmetic
+    const int pos = c0 + j;
+    const int pk = __shfl(mypage, pos / ps - pg0);
+    const int pv0 = __shfl(mypage, (c0 + 4 * hf) / ps - pg0);       // keys 4hf.. (+16kc)
+    const int pv1 = __shfl(mypage, (c0 + 16 + 4 * hf) / ps - pg0);
+    const int pw0 = __shfl(mypage, (c0 + 8 + 4 * hf) / ps - pg0);
+    const int pw1 = __shfl(mypage, (c0 + 24 + 4 * hf) / ps - pg0);
+    const bool full = c0 + 32 <= k_hi && !chunk_bad;
     bf16x8 ka[D / 16];
     {
-      const int pos = c0 + j;
-      bool ok = false;
-      const int pg = pos < k_hi ? page_of(pos, ok) : 0;
-      const bf16_t* kr = kbase + pg * kpage + (size_t)(pos % p.page_size) * D + 8 * hf;
+      const bf16_t* kr = kbase + (size_t)max(pk, 0) * kpage + (size_t)(pos % ps) * D + 8 * hf;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) ka[c] = ok ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
+      for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
     }
     bf16x8 va[D / 32][2];
+    {
+      // keys 16kc + 4hf + {0..3} (group g0) and 16kc + 8 + 4hf + {0..3} (group g1)
+      const int pgs[2][2] = {{pv0, pw0}, {pv1, pw1}};
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      // keys 16kc + 4hf + {0..3} and 16kc + 8 + 4hf + {0..3} of this step
-      const int p0 = c0 + 16 * kc + 4 * hf;
-      const int p1 = p0 + 8;
-      bool ok0 = false, ok1 = false;
-      const int pg0 = p0 < k_hi ? page_of(p0, ok0) : 0;
-      const int pg1 = p1 < k_hi ? page_of(p1, ok1) : 0;
-      const int n0 = min(4, k_hi - p0), n1 = min(4, k_hi - p1);  // live keys in each group
-      const bf16_t* v0 = vbase + pg0 * kpage + (p0 % p.page_size);
-      const bf16_t* v1 = vbase + pg1 * kpage + (p1 % p.page_size);
+      for (int kc = 0; kc < 2; ++kc) {
+        const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
+        const bf16_t* v0 = vbase + (size_t)max(pgs[kc][0], 0) * kpage + (k0 % ps);
+        const bf16_t* v1 = vbase + (size_t)max(pgs[kc][1], 0) * kpage + (k1 % ps);
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const int d = 32 * i + j;
-        u32x2 lo = ok0 ? *(const u32x2*)(v0 + (size_t)d * p.page_size) : u32x2{};
-        u32x2 hi = ok1 ? *(const u32x2*)(v1 + (size_t)d * p.page_size) : u32x2{};
-        // zero the slots past the end of the chunk (they may hold stale data)
-        if (n0 < 4) {
-          if (n0 <= 0) lo = u32x2{};
-          else if (n0 == 1) { lo[0] &= 0xFFFFu; lo[1] = 0; }
-          else if (n0 == 2) lo[1] = 0;
-          else lo[1] &= 0xFFFFu;
+        for (int i = 0; i < D / 32; ++i) {
+          const size_t dofs = (size_t)(32 * i + j) * ps;
+          u32x2 lo = *(const u32x2*)(v0 + dofs);
+          u32x2 hi = *(const u32x2*)(v1 + dofs);
+          if (!full) {
+            // past the chunk end or on a bad page: zero (stale slots may hold anything)
+            lo = keep_first(lo, pgs[kc][0] < 0 ? 0 : k_hi - k0);
+            hi = keep_first(hi, pgs[kc][1] < 0 ? 0 : k_hi - k1);
+          }
+          u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
+          va[i][kc] = __builtin_bit_cast(bf16x8, packed);
         }
-        if (n1 < 4) {
-          if (n1 <= 0) hi = u32x2{};
-          else if (n1 == 1) { hi[0] &= 0xFFFFu; hi[1] = 0; }
-          else if (n1 == 2) hi[1] = 0;
-          else hi[1] &= 0xFFFFu;
-        }
-        u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
-        va[i][kc] = __builtin_bit_cast(bf16x8, packed);
       }
     }
-    const int nlive = k_hi - c0;
-    step(ka, va, [&](int c) { return c < nlive; });
+    if (full) {
+      dec_step<D, false>(ka, va, qlds, o, m, l, p.scale_log2, 0u, hf);
+    } else {
+      const uint32_t live = (uint32_t)__ballot(pos < k_hi && pk >= 0);
+      dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
+    }
   }
 
   // ---- the B new rows, causal among themselves (chunk 0 only) --------------
   if (split == 0) {
     bf16x8 ka[D / 16];
     {
-      const bf16_t* kr = p.k_new + (((size_t)s * p.B + (j < p.B ? j : 0)) * p.Hkv + kvh) * D + 8 * hf;
+      const bf16_t* kr =
+          p.k_new + (((size_t)s * p.B + (j < p.B ? j : 0)) * p.Hkv + kvh) * D + 8 * hf;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) ka[c] = j < p.B ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
     }
@@ -203,10 +227,10 @@ __global__ __launch_bounds__(64 * kMaxQT) void decode_split_kernel(DecodeArgs p)
         }
       }
     }
-    step(ka, va, [&](int c) { return c <= qr && c < p.B; });
+    // new row n is visible to packed row j' iff n <= r(j'): a per-lane key bitmask
+    const uint32_t live = qr + 1 >= 32 ? 0xFFFFFFFFu : ((1u << (qr + 1)) - 1u);
+    dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
   }
-
-  if (bad_page) status_or(p.status, MARS_STATUS_BAD_PAGE);
 
   // ---- partial result for this chunk ---------------------------------------
   const float lt = l + __shfl_xor(l, 32);
@@ -358,10 +382,12 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   const int merge_waves = S * n_kv_heads * a.group * B;
   dim3 grid(nsplit, n_kv_heads, S);
   if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64 * nqt), 0, st, a);
+    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64 * nqt),
+                       (size_t)nqt * (128 / 16) * 64 * 16, st, a);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64 * nqt), 0, st, a);
+    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64 * nqt),
+                       (size_t)nqt * (64 / 16) * 64 * 16, st, a);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
   }
   return mars_launch_status();

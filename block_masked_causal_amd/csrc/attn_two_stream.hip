@@ -190,7 +190,8 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
   const bool grow = mt > m + kLazyRescale;
   if (__ballot(grow)) {
     const float mnew = grow ? mt : m;
-    const float alpha = fast_exp2(m - mnew);  // 0 when m = -inf, 1 when unchanged
+    // 1 when unchanged (also when still -inf), 0 when the first key arrives
+    const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);
     l *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] *= alpha;

@@ -42,4 +42,9 @@ def bf16_bits(x: torch.Tensor) -> np.ndarray:
 
 
 def max_abs(a, b) -> float:
-    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+    """Max |a - b|; +inf if either side holds a NaN or Inf (never silently dropped)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if not (np.isfinite(a).all() and np.isfinite(b).all()):
+        return float("inf")
+    return float(np.max(np.abs(a - b))) if a.size else 0.0

@@ -26,6 +26,7 @@ def run_case(seed, b, L, B, Hq, Hkv, d, dtype, mode=0, pairs=None, rows=None):
                                        return_lse=True)
     torch.cuda.synchronize()
     og, lg = from_dev(o), from_dev(lse)
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), "non-finite attention output"
     ref_o, ref_l = oracle.attn_two_stream(q.f32, k.f32, v.f32, L, B, mask_mode=mode, pairs=pairs,
                                           rows=rows)
     err_o = err_l = 0.0
@@ -56,6 +57,12 @@ def test_fp32_matches_oracle(b, L, B, Hq, Hkv, d):
     (1, 5, 2, 1, 1, 64, 0),      # a single partial tile
     (1, 200, 4, 4, 2, 128, 1),   # dense causal over 2L
     (2, 320, 8, 6, 3, 64, 1),
+    # first mask block: rows with no visible key in the first staged tile while
+    # other rows of the same wave do (regression: the deferred rescale once
+    # produced NaN there)
+    (1, 256, 4, 8, 2, 128, 0),
+    (1, 128, 4, 8, 2, 64, 0),
+    (1, 256, 16, 4, 1, 128, 0),
 ])
 def test_bf16_matches_oracle(b, L, B, Hq, Hkv, d, mode):
     eo, el, _ = run_case(2000 + L, b, L, B, Hq, Hkv, d, "bf16", mode=mode)
