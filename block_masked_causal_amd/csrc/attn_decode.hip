@@ -14,9 +14,11 @@
 //   * S^T = K Q^T: lane (key i, half hf) reads 16 bytes of its key's row.
 //   * O^T = V^T P^T: the V pages are stored transposed ([d][slot]), so the A
 //     operand of lane (dim, hf) is two 8-byte reads of consecutive slots.
-// The cache of one sequence is cut into chunks of kChunk keys (split-K); each
-// workgroup handles one (chunk, KV head, sequence) and writes an unnormalised
-// partial (O, running max, running sum); a merge kernel combines the chunks.
+// The cache of one sequence is cut into chunks (split-K): 256 keys, or 512
+// when there are already enough (sequence, KV head, query tile) items to fill
+// the GPU. Each workgroup handles one (chunk, KV head, sequence) and writes an
+// unnormalised partial (O, running max, running sum); a merge kernel combines
+// the chunks. A sequence that fits in one chunk is written out directly.
 // Chunk 0 also handles the B new rows (causal among themselves).
 #include "mars_common.hpp"
 
@@ -24,7 +26,11 @@ using namespace mars;
 
 namespace {
 
-constexpr int kChunk = 256;  // cache keys per split-K chunk (multiple of 32)
+// Split-K chunk (cache keys per workgroup): small when sequences x heads alone
+// cannot fill the GPU, larger otherwise (fewer partials to write and merge).
+inline int decode_chunk(int S, int Hkv, int nqt) {
+  return (long long)S * Hkv * nqt >= 1024 ? 512 : 256;
+}
 constexpr int kMaxQT = 4;    // at most 4 query tiles of 32 packed rows
 
 struct DecodeArgs {
@@ -39,24 +45,29 @@ struct DecodeArgs {
   float* part_o;   // [S][Hkv][nsplit][nrows_pad][D]
   float* part_ml;  // [S][Hkv][nsplit][nrows_pad][2]
   int32_t* status;
-  int S, B, Hq, Hkv, group, page_size, max_pages, num_pages, nsplit, nrows_pad;
+  int S, B, Hq, Hkv, group, page_size, max_pages, num_pages, nsplit, nrows_pad, chunk;
   float scale_log2;
 };
 
 // One 32-key step for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 // Lane (j, hf) holds the scores of packed query row j against step keys
 // 8*(r/4) + 4*hf + r%4; MASKED keeps only the keys whose bit is set in `live`.
-// The query fragments live in LDS (one 16-byte slot per lane and chunk,
-// written once by the same wave), which keeps the register budget at two
-// waves per SIMD; re-reading them costs far less LDS traffic than the HBM
-// traffic of a step.
-template <int D, bool MASKED>
-__device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
-                                         const bf16x8* __restrict__ qlds, f32x16 (&o)[D / 32],
-                                         float& m, float& l, float cs, uint32_t live, int hf) {
+// Scores of one 32-key step: lane (j, hf) gets packed query row j against
+// step keys 8*(r/4) + 4*hf + r%4.
+template <int D>
+__device__ __forceinline__ f32x16 dec_scores(const bf16x8 (&ka)[D / 16],
+                                             const bf16x8* __restrict__ qlds) {
   f32x16 sc = f32x16{};
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) sc = mfma32(ka[c], qlds[64 * c], sc);
+  return sc;
+}
+
+// Online softmax of one step; MASKED keeps only keys whose bit is set in `live`.
+template <int D, bool MASKED>
+__device__ __forceinline__ void dec_softmax(f32x16& sc, bf16x8 (&pb)[2], f32x16 (&o)[D / 32],
+                                            float& m, float& l, float cs, uint32_t live,
+                                            int hf) {
   if (MASKED) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -80,7 +91,6 @@ __device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x
   }
   const float nm = m == -INFINITY ? 0.f : -m;
   float rsum = 0.f;
-  bf16x8 pb[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const float e = fast_exp2(fmaf(sc[r], cs, nm));
@@ -88,10 +98,26 @@ __device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x
     pb[r >> 3][r & 7] = (bf16_t)e;
   }
   l += rsum;
+}
+
+template <int D>
+__device__ __forceinline__ void dec_pv(const bf16x8 (&va)[D / 32][2], const bf16x8 (&pb)[2],
+                                       f32x16 (&o)[D / 32]) {
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) o[i] = mfma32(va[i][kc], pb[kc], o[i]);
+}
+
+// One complete step (used for the B new rows).
+template <int D, bool MASKED>
+__device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x8 (&va)[D / 32][2],
+                                         const bf16x8* __restrict__ qlds, f32x16 (&o)[D / 32],
+                                         float& m, float& l, float cs, uint32_t live, int hf) {
+  f32x16 sc = dec_scores<D>(ka, qlds);
+  bf16x8 pb[2];
+  dec_softmax<D, MASKED>(sc, pb, o, m, l, cs, live, hf);
+  dec_pv<D>(va, pb, o);
 }
 
 // Keeps the first n (0..4) bf16 values of a 4-key V group, zeroes the rest.
@@ -103,7 +129,9 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int n) {
   return u32x2{v[0], v[1] & 0xFFFFu};
 }
 
-template <int D>
+// PS = the page size when it is a compile-time constant (16 or 32, the block
+// granularities the method uses), or 0 for any other multiple of 16.
+template <int D, int PS>
 __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs p) {
   const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
@@ -118,9 +146,10 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
     len = cap;
   }
   if (len < 0) len = 0;
-  const int k_lo = split * kChunk;
+  const int k_lo = split * p.chunk;
   if (split > 0 && k_lo >= len) return;
-  const int k_hi = min(len, k_lo + kChunk);
+  const int k_hi = min(len, k_lo + p.chunk);
+  const bool single = len <= p.chunk;  // the only chunk: write the final output
 
   // Packed query row of this lane: j' = r * g + head_in_group.
   const int qi = wq * 32 + j;
@@ -137,7 +166,7 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   }
 
   // Page ids of this chunk, one per lane (lane t: page k_lo / ps + t); -1 = bad.
-  const int ps = p.page_size;
+  const int ps = PS > 0 ? PS : p.page_size;
   const int pg0 = k_lo / ps;
   const int npg = k_hi > k_lo ? (k_hi - 1) / ps - pg0 + 1 : 0;
   int mypage = 0;
@@ -157,51 +186,82 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  for (int c0 = k_lo; c0 < k_hi; c0 += 32) {
-    // all of this step's K and V loads are issued before any arithmetic
+  // The step loop is rotated so that a wave always has loads in flight: the K
+  // rows of step s+1 are requested as soon as the score MFMAs of step s have
+  // consumed the K registers, and the V rows of step s+1 as soon as the PV
+  // MFMAs of step s have consumed the V registers.
+  bf16x8 ka[D / 16];
+  bf16x8 va[D / 32][2];
+  auto load_k = [&](int c0) {
     const int pos = c0 + j;
     const int pk = __shfl(mypage, pos / ps - pg0);
-    const int pv0 = __shfl(mypage, (c0 + 4 * hf) / ps - pg0);       // keys 4hf.. (+16kc)
-    const int pv1 = __shfl(mypage, (c0 + 16 + 4 * hf) / ps - pg0);
-    const int pw0 = __shfl(mypage, (c0 + 8 + 4 * hf) / ps - pg0);
-    const int pw1 = __shfl(mypage, (c0 + 24 + 4 * hf) / ps - pg0);
-    const bool full = c0 + 32 <= k_hi && !chunk_bad;
-    bf16x8 ka[D / 16];
-    {
-      const bf16_t* kr = kbase + (size_t)max(pk, 0) * kpage + (size_t)(pos % ps) * D + 8 * hf;
+    const bf16_t* kr = kbase + (size_t)max(pk, 0) * kpage + (size_t)(pos % ps) * D + 8 * hf;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
-    }
-    bf16x8 va[D / 32][2];
-    {
-      // keys 16kc + 4hf + {0..3} (group g0) and 16kc + 8 + 4hf + {0..3} (group g1)
-      const int pgs[2][2] = {{pv0, pw0}, {pv1, pw1}};
+    for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
+  };
+  // V group of 4 keys starting at step offset 16kc + 4hf (+ 8 for the second)
+  auto v_page = [&](int c0, int kc, int second) {
+    return __shfl(mypage, (c0 + 16 * kc + 8 * second + 4 * hf) / ps - pg0);
+  };
+  auto load_v = [&](int c0) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
-        const bf16_t* v0 = vbase + (size_t)max(pgs[kc][0], 0) * kpage + (k0 % ps);
-        const bf16_t* v1 = vbase + (size_t)max(pgs[kc][1], 0) * kpage + (k1 % ps);
+    for (int kc = 0; kc < 2; ++kc) {
+      const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
+      const bf16_t* v0 = vbase + (size_t)max(v_page(c0, kc, 0), 0) * kpage + (k0 % ps);
+      const bf16_t* v1 = vbase + (size_t)max(v_page(c0, kc, 1), 0) * kpage + (k1 % ps);
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-          const size_t dofs = (size_t)(32 * i + j) * ps;
-          u32x2 lo = *(const u32x2*)(v0 + dofs);
-          u32x2 hi = *(const u32x2*)(v1 + dofs);
-          if (!full) {
-            // past the chunk end or on a bad page: zero (stale slots may hold anything)
-            lo = keep_first(lo, pgs[kc][0] < 0 ? 0 : k_hi - k0);
-            hi = keep_first(hi, pgs[kc][1] < 0 ? 0 : k_hi - k1);
-          }
-          u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
-          va[i][kc] = __builtin_bit_cast(bf16x8, packed);
-        }
+      for (int i = 0; i < D / 32; ++i) {
+        const size_t dofs = (size_t)(32 * i + j) * ps;
+        const u32x2 lo = *(const u32x2*)(v0 + dofs);
+        const u32x2 hi = *(const u32x2*)(v1 + dofs);
+        const u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
+        va[i][kc] = __builtin_bit_cast(bf16x8, packed);
       }
     }
-    if (full) {
-      dec_step<D, false>(ka, va, qlds, o, m, l, p.scale_log2, 0u, hf);
-    } else {
-      const uint32_t live = (uint32_t)__ballot(pos < k_hi && pk >= 0);
-      dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
+  };
+  // past the chunk end or on a bad page: zero V (stale slots may hold anything)
+  auto zero_v_tail = [&](int c0) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
+      const int n0 = v_page(c0, kc, 0) < 0 ? 0 : k_hi - k0;
+      const int n1 = v_page(c0, kc, 1) < 0 ? 0 : k_hi - k1;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4 w = __builtin_bit_cast(u32x4, va[i][kc]);
+        const u32x2 lo = keep_first(u32x2{w[0], w[1]}, n0);
+        const u32x2 hi = keep_first(u32x2{w[2], w[3]}, n1);
+        const u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
+        va[i][kc] = __builtin_bit_cast(bf16x8, packed);
+      }
     }
+  };
+
+  if (k_lo < k_hi) {
+    load_k(k_lo);
+    load_v(k_lo);
+  }
+  for (int c0 = k_lo; c0 < k_hi; c0 += 32) {
+    const bool full = c0 + 32 <= k_hi && !chunk_bad;
+    const bool more = c0 + 32 < k_hi;
+    f32x16 sc = dec_scores<D>(ka, qlds);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_k(c0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pb[2];
+    if (full) {
+      dec_softmax<D, false>(sc, pb, o, m, l, p.scale_log2, 0u, hf);
+    } else {
+      const int pos = c0 + j;
+      const uint32_t live =
+          (uint32_t)__ballot(pos < k_hi && __shfl(mypage, pos / ps - pg0) >= 0);
+      dec_softmax<D, true>(sc, pb, o, m, l, p.scale_log2, live, hf);
+      zero_v_tail(c0);
+    }
+    dec_pv<D>(va, pb, o);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_v(c0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- the B new rows, causal among themselves (chunk 0 only) --------------
@@ -235,6 +295,19 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   // ---- partial result for this chunk ---------------------------------------
   const float lt = l + __shfl_xor(l, 32);
   if (!qvalid) return;
+  if (single) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    bf16_t* orow = p.o + (((size_t)s * p.B + qr) * p.Hq + qh) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 pk = {pack_bf16x2(o[i][4 * g] * inv, o[i][4 * g + 1] * inv),
+                    pack_bf16x2(o[i][4 * g + 2] * inv, o[i][4 * g + 3] * inv)};
+        *(u32x2*)(orow + 32 * i + 8 * g + 4 * hf) = pk;
+      }
+    return;
+  }
   const size_t prow = (((size_t)s * p.Hkv + kvh) * p.nsplit + split) * p.nrows_pad + qi;
   float* po = p.part_o + prow * D;
 #pragma unroll
@@ -263,7 +336,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
   const int s = wave / (nrows * p.Hkv);
   int len = p.cache_len[s];
   len = min(max(len, 0), p.max_pages * p.page_size);
-  const int nsp = max(1, (len + kChunk - 1) / kChunk);
+  const int nsp = max(1, (len + p.chunk - 1) / p.chunk);
+  if (nsp == 1) return;  // written directly by the split kernel
 
   const size_t base = (((size_t)s * p.Hkv + kvh) * p.nsplit) * p.nrows_pad + qi;
   const size_t stride = p.nrows_pad;
@@ -292,9 +366,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
 size_t decode_ws_bytes(int S, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
                        int* nsplit_out, int* nrows_pad_out) {
   const long long cap = (long long)max_pages * page_size;
-  const int nsplit = (int)std::max<long long>(1, (cap + kChunk - 1) / kChunk);
   const int nrows = (Hq / Hkv) * B;
   const int nrows_pad = ((nrows + 31) / 32) * 32;
+  const int chunk = decode_chunk(S, Hkv, nrows_pad / 32);
+  const int nsplit = (int)std::max<long long>(1, (cap + chunk - 1) / chunk);
   if (nsplit_out) *nsplit_out = nsplit;
   if (nrows_pad_out) *nrows_pad_out = nrows_pad;
   const size_t rows = (size_t)S * Hkv * nsplit * nrows_pad;
@@ -374,6 +449,7 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   a.num_pages = num_pages;
   a.nsplit = nsplit;
   a.nrows_pad = nrows_pad;
+  a.chunk = decode_chunk(S, n_kv_heads, nrows_pad / 32);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   a.scale_log2 = scale * kLog2e;
 
@@ -381,14 +457,21 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   const int nqt = nrows_pad / 32;
   const int merge_waves = S * n_kv_heads * a.group * B;
   dim3 grid(nsplit, n_kv_heads, S);
+  const size_t qlds = (size_t)nqt * (head_dim / 16) * 64 * 16;
+  const dim3 blk(64 * nqt);
+#define MARS_DECODE_LAUNCH(D_, PS_) \
+  hipLaunchKernelGGL((decode_split_kernel<D_, PS_>), grid, blk, qlds, st, a)
   if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(64 * nqt),
-                       (size_t)nqt * (128 / 16) * 64 * 16, st, a);
+    if (page_size == 16) MARS_DECODE_LAUNCH(128, 16);
+    else if (page_size == 32) MARS_DECODE_LAUNCH(128, 32);
+    else MARS_DECODE_LAUNCH(128, 0);
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(64 * nqt),
-                       (size_t)nqt * (64 / 16) * 64 * 16, st, a);
+    if (page_size == 16) MARS_DECODE_LAUNCH(64, 16);
+    else if (page_size == 32) MARS_DECODE_LAUNCH(64, 32);
+    else MARS_DECODE_LAUNCH(64, 0);
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
   }
+#undef MARS_DECODE_LAUNCH
   return mars_launch_status();
 }

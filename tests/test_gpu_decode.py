@@ -53,6 +53,17 @@ def test_decode_lengths_on_chunk_and_page_edges():
     assert err <= TOL and st == 0, (err, st)
 
 
+def test_decode_large_batch_uses_512_key_chunks_on_edges():
+    """130 sequences x 8 KV heads fill the GPU without splitting: 512-key chunks;
+    lengths sit on both sides of the chunk and single-chunk boundaries."""
+    rng = np.random.default_rng(3150)
+    lens = rng.integers(0, 1100, size=130)
+    lens[:10] = [0, 1, 511, 512, 513, 1023, 1024, 1025, 31, 32]
+    seqs = list(range(0, 130, 9))
+    err, st = run(3150, 130, 1, 8, 8, 64, 0, 1100, 16, seqs=seqs, lens=lens)
+    assert err <= TOL and st == 0, (err, st)
+
+
 def test_decode_equals_two_stream_mask_rows_on_gpu():
     """Mask rows of block b from the two-stream kernel == decode with cache = clean K/V[0:bB]."""
     L, B, Hq, Hkv, D = 256, 4, 8, 2, 128
