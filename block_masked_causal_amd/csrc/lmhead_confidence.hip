@@ -8,14 +8,16 @@
 //
 //  * lmhead_gemm_kernel: logits[N, V] = hidden[N, D] . W[V, D]^T on the
 //    32x32x16 bf16 MFMA with fp32 accumulation. A 512-thread workgroup owns
-//    all of up to 256 rows and 128 vocabulary entries, so each weight row is
-//    read from HBM once; K is staged through double-buffered LDS 32 at a time.
+//    all of up to 256 rows and 256 vocabulary entries, so each weight row is
+//    read from HBM once; K is staged through double-buffered LDS 64 (or 32)
+//    at a time, with the weight loads issued two stages ahead.
 //  * conf_partial_kernel: a row is cut into chunks; each workgroup streams one
 //    chunk once, keeping per-thread (max, first argmax, sum of exp relative to
 //    the running max), and reduces them in the workgroup (sums in fp64).
 //  * conf_merge_kernel: combines the chunks of a row in a fixed order:
 //    top_id = lowest index attaining the maximum, p_max = 1 / sum exp(l - m).
 #include <algorithm>
+#include <type_traits>
 
 #include "mars_common.hpp"
 
@@ -24,10 +26,27 @@ using namespace mars;
 namespace {
 
 // ------------------------------------------------------------------ GEMM ----
-constexpr int GM = 256;  // rows (positions) per workgroup
-constexpr int GN = 128;  // vocabulary entries per workgroup
-constexpr int GK = 32;   // K per stage
-constexpr int GST = GK + 8;  // LDS row stride (elements)
+// Workgroup tile: GM rows (all positions, up to 256) x GN vocabulary entries;
+// 8 waves as 4 (rows) x 2 (vocab), each wave 64 x 128 outputs, so each pair
+// of fragments read from LDS feeds eight MFMAs. K advances GK per stage
+// through two LDS buffers (GK = 64 when D allows it, else 32); weight rows
+// are requested kWRing = 2 stages ahead of their use.
+constexpr int GM = 256;
+constexpr int GN = 256;
+constexpr int GT = 512;            // threads per workgroup
+constexpr int WNT = GN / 64;       // 32-wide vocab MFMA tiles per wave
+constexpr int kWRing = 2;
+
+template <int GK>
+struct GemmCfg {
+  static constexpr int GST = GK + 8;        // LDS row stride (elements): 4 dwords mod 32 banks
+  static constexpr int CPR = GK / 8;        // 16-byte chunks per tile row
+  static constexpr int AL = GM * CPR / GT;  // hidden chunks per thread per stage
+  static constexpr int BL = GN * CPR / GT;  // weight chunks per thread per stage
+  static constexpr size_t LDS = 2 * (size_t)(GM + GN) * GST * sizeof(bf16_t);
+  static_assert(GK % 16 == 0 && (GM * CPR) % GT == 0 && (GN * CPR) % GT == 0, "tile shape");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
 
 struct GemmArgs {
   const bf16_t* hidden;
@@ -36,78 +55,120 @@ struct GemmArgs {
   int N, D, V;
 };
 
-__global__ __launch_bounds__(512) void lmhead_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][GM * GST];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][GN * GST];
+template <int GK>
+__global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
+  using C = GemmCfg<GK>;
+  constexpr int GST = C::GST, CPR = C::CPR, AL = C::AL, BL = C::BL;
+  extern __shared__ __attribute__((aligned(16))) bf16_t gl[];
+  auto As = [&](int buf) { return gl + buf * GM * GST; };
+  auto Bs = [&](int buf) { return gl + 2 * GM * GST + buf * GN * GST; };
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
-  const int wn = w >> 1, wv = w & 1;  // 4 x 2 waves, each 64 rows x 64 entries
+  const int wn = w >> 1, wv = w & 1;
   const int v0 = blockIdx.x * GN;
   const int n0 = blockIdx.y * GM;
+  const int nk = p.D / GK;
 
-  // global -> register staging: A 2 x 16 B per thread, B 1 x 16 B per thread
-  u32x4 areg[2], breg;
-  auto load = [&](int k0) {
+  u32x4 areg[AL];
+  u32x4 wring[kWRing][BL];
+  auto load_a = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 512 * i;
-      const int row = idx >> 2, ch = idx & 3;
+    for (int i = 0; i < AL; ++i) {
+      const int idx = tid + GT * i;
+      const int row = idx / CPR, ch = idx % CPR;
       const int n = n0 + row;
-      areg[i] = n < p.N ? *(const u32x4*)(p.hidden + (size_t)n * p.D + k0 + ch * 8) : u32x4{};
-    }
-    {
-      const int row = tid >> 2, ch = tid & 3;
-      const int v = v0 + row;
-      breg = v < p.V ? *(const u32x4*)(p.w + (size_t)v * p.D + k0 + ch * 8) : u32x4{};
+      areg[i] = n < p.N ? *(const u32x4*)(p.hidden + (size_t)n * p.D + kt * GK + ch * 8)
+                        : u32x4{};
     }
   };
-  auto store = [&](int buf) {
+  auto load_w = [&](int kt, u32x4 (&dst)[BL]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 512 * i;
-      *(u32x4*)(&As[buf][(idx >> 2) * GST + (idx & 3) * 8]) = areg[i];
+    for (int i = 0; i < BL; ++i) {
+      const int idx = tid + GT * i;
+      const int row = idx / CPR, ch = idx % CPR;
+      const int v = v0 + row;
+      dst[i] = v < p.V ? *(const u32x4*)(p.w + (size_t)v * p.D + kt * GK + ch * 8) : u32x4{};
     }
-    *(u32x4*)(&Bs[buf][(tid >> 2) * GST + (tid & 3) * 8]) = breg;
+  };
+  auto store = [&](int buf, const u32x4 (&wreg)[BL]) {
+    bf16_t* A = As(buf);
+    bf16_t* Bm = Bs(buf);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int idx = tid + GT * i;
+      *(u32x4*)(A + (idx / CPR) * GST + (idx % CPR) * 8) = areg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int idx = tid + GT * i;
+      *(u32x4*)(Bm + (idx / CPR) * GST + (idx % CPR) * 8) = wreg[i];
+    }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][WNT];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < WNT; ++b) acc[a][b] = f32x16{};
 
-  const int nk = p.D / GK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load((kt + 1) * GK);
-    const bf16_t* A = As[kt & 1];
-    const bf16_t* Bm = Bs[kt & 1];
+  auto compute = [&](int buf) {
+    const bf16_t* A = As(buf);
+    const bf16_t* Bm = Bs(buf);
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[2], bfr[WNT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
         af[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
-        bfr[t] = *(const bf16x8*)(Bm + (wv * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
-      }
+#pragma unroll
+      for (int t = 0; t < WNT; ++t)
+        bfr[t] = *(const bf16x8*)(Bm + (wv * (GN / 2) + 32 * t + j) * GST + 16 * ks + 8 * hf);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+        for (int b = 0; b < WNT; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
     }
-    if (kt + 1 < nk) store((kt + 1) & 1);
+  };
+
+  // prologue: weight stages 0 .. kWRing-1 in flight, stage 0 staged
+#pragma unroll
+  for (int u = 0; u < kWRing; ++u)
+    if (u < nk) load_w(u, wring[u]);
+  load_a(0);
+  store(0, wring[0]);
+  if (kWRing > 1 && kWRing < nk) load_w(kWRing, wring[0]);
+  __syncthreads();
+
+  // one K stage; the ring slot of stage kt + 1 is a compile-time constant
+  auto step = [&](int kt, auto u_tag) {
+    constexpr int un = (decltype(u_tag)::value + 1) % kWRing;
+    if (kt + 1 < nk) {
+      load_a(kt + 1);
+      if (kWRing == 1) load_w(kt + 1, wring[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      store((kt + 1) & 1, wring[un]);
+      if (kWRing > 1 && kt + 1 + kWRing < nk) load_w(kt + 1 + kWRing, wring[un]);
+    }
     __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += kWRing) {
+    step(kt, std::integral_constant<int, 0>{});
+    if constexpr (kWRing > 1) if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % kWRing>{});
+    if constexpr (kWRing > 2) if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2 % kWRing>{});
+    if constexpr (kWRing > 3) if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % kWRing>{});
   }
 
   // lane (j, hf) holds C[8*(r/4) + 4*hf + r%4][j]: rows = positions, j = vocab
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int v = v0 + wv * 64 + 32 * b + j;
+    for (int b = 0; b < WNT; ++b) {
+      const int v = v0 + wv * (GN / 2) + 32 * b + j;
       if (v >= p.V) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -225,6 +286,19 @@ void conf_layout(int N, int V, int* nchunk, int* chunk) {
 
 }  // namespace
 
+namespace {
+template <int GK>
+int launch_gemm(dim3 grid, hipStream_t st, const GemmArgs& g) {
+  // the workgroup tile needs more than the default 64 KiB of dynamic LDS
+  if (hipFuncSetAttribute((const void*)lmhead_gemm_kernel<GK>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)GemmCfg<GK>::LDS) != hipSuccess)
+    return MARS_ERR_LAUNCH;
+  hipLaunchKernelGGL(lmhead_gemm_kernel<GK>, grid, dim3(GT), GemmCfg<GK>::LDS, st, g);
+  return MARS_OK;
+}
+}  // namespace
+
 extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
   if (N < 1 || V < 4 || V % 4) return 0;
   int nchunk, chunk;
@@ -241,7 +315,7 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
   MARS_REQUIRE(N >= 1 && V >= 4 && V % 4 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(N <= 65535, MARS_ERR_SHAPE);  // confidence grid: one row per gridDim.y
   MARS_REQUIRE((double)N * V < 9.0e18, MARS_ERR_SHAPE);
-  if (hidden) MARS_REQUIRE(D >= GK && D % GK == 0, MARS_ERR_SHAPE);
+  if (hidden) MARS_REQUIRE(D >= 32 && D % 32 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(mars_aligned16(hidden) && mars_aligned16(w_lm) && mars_aligned16(logits) &&
                    mars_aligned16(top_id) && mars_aligned16(p_max) &&
                    mars_aligned16(workspace),
@@ -259,7 +333,8 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
     g.D = D;
     g.V = V;
     dim3 grid((V + GN - 1) / GN, (N + GM - 1) / GM);
-    hipLaunchKernelGGL(lmhead_gemm_kernel, grid, dim3(512), 0, st, g);
+    const int rc = D % 64 == 0 ? launch_gemm<64>(grid, st, g) : launch_gemm<32>(grid, st, g);
+    if (rc != MARS_OK) return rc;
   }
   ConfArgs c;
   c.logits = logits;
