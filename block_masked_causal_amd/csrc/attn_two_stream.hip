@@ -10,6 +10,8 @@
 // and a key c is visible iff it lies in one of them. Whole key tiles outside
 // a query tile's intervals are never loaded, and tiles entirely inside them
 // skip the per-element test.
+#include <type_traits>
+
 #include "mars_common.hpp"
 
 using namespace mars;
@@ -113,34 +115,32 @@ __global__ __launch_bounds__(64) void two_stream_f32_kernel(TwoStreamArgs p) {
 // ---------------------------------------------------------------------------
 // bfloat16 MFMA path.
 //
-// Workgroup = 4 waves = 128 query rows of one (batch, q-head); each wave owns
-// 32 rows. Scores are computed transposed, S^T = K Q^T, with the 32x32x16
-// MFMA: lane (j = l % 32, hf = l / 32) then holds query row j and 16 of the
-// keys of each 32-key sub-tile, so the row softmax needs one cross-lane
-// exchange (lane l <-> l ^ 32). The probabilities stay in registers and feed
-// O^T = V^T P^T directly as the B operand: K slot (hf, e) of a 16-key chunk
-// is mapped to key 4*hf + e (e < 4) or 8 + 4*hf + e - 4 (e >= 4), exactly the
-// keys the lane already holds. V is written to LDS transposed ([d][key]) so
-// that the A operand is two 8-byte LDS reads.
+// Each wave owns 32 query rows of one query head. Scores are computed
+// transposed, S^T = K Q^T, with the 32x32x16 MFMA: lane (j = l % 32,
+// hf = l / 32) then holds query row j and 16 of the keys of each 32-key
+// sub-tile, so a row reduction needs one exchange between the wave halves
+// (v_permlane32_swap). The probabilities stay in registers and feed
+// O^T = V^T P^T as the B operand: K slot (hf, e) of a 16-key chunk is key
+// 4*hf + e (e < 4) or 8 + 4*hf + e - 4 (e >= 4), exactly the keys the lane
+// holds. K and V tiles are plain row-major copies in LDS; the V^T fragments
+// of the A operand come from the transposing LDS read ds_read_b64_tr_b16,
+// which hands each lane one column (head dimension) of a 4-key x 16-column
+// block that 16 lanes read as rows.
 // ---------------------------------------------------------------------------
+#ifndef MARS_TS_VPAD
+#define MARS_TS_VPAD 16
+#endif
 template <int D>
 struct Cfg {
-  static constexpr int BN = 64;       // keys per tile
-  static constexpr int KST = D + 8;   // K tile row stride in LDS (elements)
-  static constexpr int VST = BN + 4;  // V^T tile row stride in LDS (elements)
+  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int KST = D + 8;             // K tile row stride in LDS (elements)
+  static constexpr int VST = D + MARS_TS_VPAD;  // V tile row stride in LDS (elements)
   static constexpr int KSZ = BN * KST;
-  static constexpr int VSZ = D * VST;
-  static constexpr int KLOADS = BN * D / 8 / 256;             // 16-byte K loads per thread
-  static constexpr int VPATCH = (BN / 4) * (D / 8);           // 4-key x 8-dim V patches
-  static constexpr int VLOADS = (VPATCH + 255) / 256;         // patches per thread
-  static constexpr size_t LDS_BYTES = 2 * (KSZ + VSZ) * sizeof(bf16_t);
+  static constexpr int VSZ = BN * VST;
+  static constexpr int STAGE = KSZ + VSZ;       // one K/V stage
+  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(bf16_t);
+  static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
 };
-
-// V^T tiles are stored in groups of 4 keys (8 bytes); group cg of row `row`
-// sits at group position cg ^ vt_swizzle(row). Writers cover rows 8 apart and
-// readers 16 consecutive rows per LDS cycle; this XOR keeps both on distinct
-// banks (the unswizzled write pattern hit the same 2 of 32 banks).
-__device__ __forceinline__ int vt_swizzle(int row) { return (row >> 4) & 15; }
 
 // Rescaling of the running output is deferred until a row maximum grows by
 // more than 2^8: until then exp2(s - m) stays below 256, which neither fp32
@@ -149,16 +149,45 @@ constexpr float kLazyRescale = 8.0f;
 
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
+// How a tile's keys are tested against a lane's visible intervals (both given
+// relative to the lane's first key kb = c0 + 4 hf). The first interval always
+// starts at or before the tile, so only its upper end matters.
+enum : int {
+  kMaskNone = 0,   // every key visible to every row of the wave
+  kMaskUpper = 1,  // key < hi_a
+  kMaskRange = 2,  // lo_b <= key < lo_b + wb
+  kMaskBoth = 3,   // either
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 4 keys x 1 column of a row-major LDS tile (see the lane mapping above)
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+}
+
+// max / sum of a value over the two halves of the wave (lanes l and l ^ 32)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
-// O^T += V^T P^T. MASKED applies the per-element visibility test; unmasked
-// tiles are fully visible to every row of the wave.
-// Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its row, kb = c0 + 4hf.
-template <int D, bool MASKED>
+// O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
+// row. kaddr / vaddr are the lane's K and V^T read offsets inside a stage.
+template <int D, int MASK>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
-                                          const bf16_t* __restrict__ Vt,
+                                          const bf16_t* __restrict__ Vs,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                          float& m, float& l, float cs, int kb, int lo_a,
-                                          int hi_a, int lo_b, int hi_b, int j, int hf) {
+                                          float& m, float& l, float cs, int hi_a, int lo_b,
+                                          int wb, int kaddr, int vaddr) {
   using C = Cfg<D>;
   f32x16 s[2];
 #pragma unroll
@@ -166,17 +195,27 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
     s[n] = f32x16{};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 ka = *(const bf16x8*)(Ks + (32 * n + j) * C::KST + 16 * c + 8 * hf);
+      const bf16x8 ka = *(const bf16x8*)(Ks + kaddr + 32 * n * C::KST + 16 * c);
       s[n] = mfma32(ka, qf[c], s[n]);
     }
   }
-  if (MASKED) {
+  if constexpr (MASK != kMaskNone) {
+    // tie the bounds to the scores so that the per-key tests are computed
+    // after the products, not hoisted above them with every result held live
+    asm volatile("" : "+v"(hi_a), "+v"(lo_b), "+v"(wb) : "v"(s[0]), "v"(s[1]));
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int c = kb + 32 * n + 8 * (r >> 2) + (r & 3);
-        const bool vis = ((c >= lo_a) & (c < hi_a)) | ((c >= lo_b) & (c < hi_b));
+        const int off = 32 * n + 8 * (r >> 2) + (r & 3);
+        bool vis;
+        if constexpr (MASK == kMaskUpper) {
+          vis = off < hi_a;
+        } else if constexpr (MASK == kMaskRange) {
+          vis = (uint32_t)(off - lo_b) < (uint32_t)wb;
+        } else {
+          vis = (off < hi_a) | ((uint32_t)(off - lo_b) < (uint32_t)wb);
+        }
         s[n][r] = vis ? s[n][r] : -INFINITY;
       }
   }
@@ -186,9 +225,9 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[n][r]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * cs;
+  mt = halves_max(mt) * cs;
   const bool grow = mt > m + kLazyRescale;
-  if (__ballot(grow)) {
+  if (__builtin_amdgcn_ballot_w64(grow)) {
     const float mnew = grow ? mt : m;
     // 1 when unchanged (also when still -inf), 0 when the first key arrives
     const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);
@@ -198,26 +237,23 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
     m = mnew;
   }
   const float nm = m == -INFINITY ? 0.f : -m;
-  float rsum = 0.f;
   bf16x8 pb[4];
+  float ls = 0.f;
 #pragma unroll
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float e = fast_exp2(fmaf(s[n][r], cs, nm));
-      rsum += e;
+      ls += e;
       pb[2 * n + (r >> 3)][r & 7] = (bf16_t)e;
     }
-  l += rsum;
+  l += ls;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
-    const int row = 32 * i + j;
-    const bf16_t* vrow = Vt + row * C::VST;
-    const int sw = vt_swizzle(row);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const bf16x4 vlo = *(const bf16x4*)(vrow + 4 * ((4 * kc + hf) ^ sw));
-      const bf16x4 vhi = *(const bf16x4*)(vrow + 4 * ((4 * kc + 2 + hf) ^ sw));
+      const bf16x4 vlo = lds_read_tr(Vs + vaddr + 16 * kc * C::VST + 32 * i);
+      const bf16x4 vhi = lds_read_tr(Vs + vaddr + (16 * kc + 8) * C::VST + 32 * i);
       const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
       o[i] = mfma32(va, pb[kc], o[i]);
     }
@@ -325,11 +361,9 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     qf[c] = __builtin_bit_cast(
         bf16x8, buf_load16(rq, (uint32_t)((a * qs + 16 * c + 8 * hf) * sizeof(bf16_t))));
 
-  constexpr int KCH = C::BN * D / 8;                   // 16-byte chunks per K tile
-  constexpr int KMAX = (KCH + 5 * 64 - 1) / (5 * 64);  // per thread, at >= 5 waves
-  constexpr int VMAX = (C::VPATCH + 5 * 64 - 1) / (5 * 64);
-  u32x4 kreg[KMAX];
-  u32x4 vreg[VMAX][4];
+  constexpr int KCH = C::BN * D / 8;                   // 16-byte chunks per K (or V) tile
+  constexpr int KMAX = (KCH + 4 * 64 - 1) / (4 * 64);  // per thread, at >= 4 waves
+  u32x4 kreg[KMAX], vreg[KMAX];
 
   auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
 
@@ -339,48 +373,21 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     for (int i = 0; i < KMAX; ++i) {
       const int idx = min(tid + NT * i, KCH - 1);
       const int row = idx / (D / 8), ch = idx % (D / 8);
-      kreg[i] = buf_load16(rk, (uint32_t)(((c0 + row) * rs + ch * 8) * sizeof(bf16_t)));
-    }
-#pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      const int pi = min(tid + NT * i, C::VPATCH - 1);
-      const int dg = pi % (D / 8), kg = pi / (D / 8);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        vreg[i][rr] =
-            buf_load16(rv, (uint32_t)(((c0 + 4 * kg + rr) * rs + dg * 8) * sizeof(bf16_t)));
+      const uint32_t off = (uint32_t)(((c0 + row) * rs + ch * 8) * sizeof(bf16_t));
+      kreg[i] = buf_load16(rk, off);
+      vreg[i] = buf_load16(rv, off);
     }
   };
 
-  auto store_tile = [&](int buf) {
-    bf16_t* Ks = lds + buf * (C::KSZ + C::VSZ);
-    bf16_t* Vt = Ks + C::KSZ;
+  auto store_tile = [&](bf16_t* Ks) {
+    bf16_t* Vs = Ks + C::KSZ;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       const int idx = tid + NT * i;
       if (idx < KCH) {
         const int row = idx / (D / 8), ch = idx % (D / 8);
         *(u32x4*)(Ks + row * C::KST + ch * 8) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      const int pi = tid + NT * i;
-      if (pi >= C::VPATCH) continue;
-      const int dg = pi % (D / 8), kg = pi / (D / 8);
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const uint32_t x0 = vreg[i][0][dw], x1 = vreg[i][1][dw];
-        const uint32_t x2 = vreg[i][2][dw], x3 = vreg[i][3][dw];
-        // dimension 8*dg + 2*dw: low halves; dimension 8*dg + 2*dw + 1: high halves
-        // byte permutes: lo = {x0.lo16, x1.lo16}, hi = {x0.hi16, x1.hi16}
-        u32x2 lo = {__builtin_amdgcn_perm(x1, x0, 0x05040100u),
-                    __builtin_amdgcn_perm(x3, x2, 0x05040100u)};
-        u32x2 hi = {__builtin_amdgcn_perm(x1, x0, 0x07060302u),
-                    __builtin_amdgcn_perm(x3, x2, 0x07060302u)};
-        const int r0 = 8 * dg + 2 * dw, r1 = r0 + 1;
-        *(u32x2*)(Vt + r0 * C::VST + 4 * (kg ^ vt_swizzle(r0))) = lo;
-        *(u32x2*)(Vt + r1 * C::VST + 4 * (kg ^ vt_swizzle(r1))) = hi;
+        *(u32x4*)(Vs + row * C::VST + ch * 8) = vreg[i];
       }
     }
   };
@@ -390,9 +397,16 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
+  // lane read offsets inside a stage: K rows for S^T, and the transposing
+  // V read (16-lane group g = lane / 16 reads keys 4 (g / 2) + lane % 16 / 4
+  // at columns 16 (g % 2) + 4 (lane % 4))
+  const int kaddr = j * C::KST + 8 * hf;
+  const int vaddr = (4 * hf + ((lane & 15) >> 2)) * C::VST + 16 * ((lane >> 4) & 1) +
+                    4 * (lane & 3);
+
   if (ntiles > 0) {
     load_tile(0);
-    store_tile(0);
+    store_tile(lds);
   }
   // The query fragments must have landed before the loop: otherwise the
   // wait-count bookkeeping treats them as in flight on every iteration and
@@ -401,13 +415,16 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // one tile; the LDS stage is a compile-time constant so that every LDS
+  // address is a lane offset plus an immediate
+  auto iteration = [&](int it, auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
     if (it + 1 < ntiles) load_tile(it + 1);
     // keep the prefetch issued before the compute, and its LDS stores after it
     __builtin_amdgcn_sched_barrier(0);
 
-    const bf16_t* Ks = lds + (it & 1) * (C::KSZ + C::VSZ);
-    const bf16_t* Vt = Ks + C::KSZ;
+    const bf16_t* Ks = lds + STG * C::STAGE;
+    const bf16_t* Vs = Ks + C::KSZ;
     const int c0 = tile_c0(it);
     const bool in_r1 = it < n1;
     const int lim_lo = in_r1 ? 0 : r2_lo;       // the staged range this tile belongs to
@@ -417,22 +434,43 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
     if (need) {
       if (in_r1 && c0 + C::BN - 1 < w_full) {
-        tile_step<D, false>(Ks, Vt, qf, o, m, l, p.scale_log2, 0, 0, 0, 0, 0, j, hf);
+        tile_step<D, kMaskNone>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, 0, 0, kaddr, vaddr);
       } else {
-        // the row's visible intervals, clipped to this tile's key range
-        const int lo_a = lim_lo, hi_a = min(hi1, lim_hi);
-        const int lo_b = max(lo2, lim_lo), hi_b = min(hi2, lim_hi);
-        tile_step<D, true>(Ks, Vt, qf, o, m, l, p.scale_log2, c0 + 4 * hf, lo_a, hi_a, lo_b,
-                           hi_b, j, hf);
+        // the row's visible intervals clipped to the staged range, relative
+        // to the lane's first key
+        const int kb = c0 + 4 * hf;
+        const int hi_a = min(hi1, lim_hi) - kb;
+        const int lo_b = max(lo2, lim_lo) - kb;
+        const int wb = max(min(hi2, lim_hi) - kb - lo_b, 0);
+        const bool any_a = __builtin_amdgcn_ballot_w64(hi_a > 0) != 0;
+        const bool any_b = __builtin_amdgcn_ballot_w64(wb > 0) != 0;
+        if (!any_b) {
+          tile_step<D, kMaskUpper>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, 0, 0, kaddr,
+                                   vaddr);
+        } else if (!any_a) {
+          tile_step<D, kMaskRange>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, lo_b, wb, kaddr,
+                                   vaddr);
+        } else {
+          tile_step<D, kMaskBoth>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, lo_b, wb, kaddr,
+                                  vaddr);
+        }
       }
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);
+    if (it + 1 < ntiles) store_tile(lds + (1 - STG) * C::STAGE);
     __syncthreads();
+  };
+#ifndef MARS_TS_NOUNROLL
+  for (int it = 0; it < ntiles; it += 2) {
+    iteration(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) iteration(it + 1, std::integral_constant<int, 1>{});
   }
+#else
+  for (int it = 0; it < ntiles; ++it) iteration(it, std::integral_constant<int, 0>{});
+#endif
 
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = halves_sum(l);
   if (a >= p.twoL) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   bf16_t* orow = (bf16_t*)p.o + (((size_t)b * p.twoL + a) * p.Hq + h) * D;
@@ -458,13 +496,10 @@ inline int heads_per_wg(int group) {
 template <int D>
 int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   using C = Cfg<D>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)two_stream_bf16_kernel<D>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    (void)hipGetLastError();
-    attr_set = true;
-  }
+  if (hipFuncSetAttribute((const void*)two_stream_bf16_kernel<D>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)C::LDS_BYTES) != hipSuccess)
+    return MARS_ERR_LAUNCH;
   // d = 64: one head x 4 row tiles per workgroup, so that three 4-wave
   // workgroups share a CU (the kernel is bound by vector-ALU softmax work and
   // needs the extra waves to hide latency). d = 128: the GQA heads sharing a
