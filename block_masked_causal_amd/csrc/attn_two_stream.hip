@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64) void two_stream_f32_kernel(TwoStreamArgs p) {
 // block that 16 lanes read as rows.
 // ---------------------------------------------------------------------------
 #ifndef MARS_TS_VPAD
-#define MARS_TS_VPAD 16
+#define MARS_TS_VPAD 32
 #endif
 template <int D>
 struct Cfg {
@@ -292,7 +292,9 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   const int NT = 64 * p.nw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // d = 128 keeps the wave index in a scalar register (fewer vector registers
+  // under its higher pressure); d = 64 measured faster with it in a VGPR
+  const int w = D == 128 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
 
   // ---- which (batch, KV head, head chunk, query tile) ---------------------
