@@ -127,20 +127,28 @@ __global__ __launch_bounds__(64) void two_stream_f32_kernel(TwoStreamArgs p) {
 // which hands each lane one column (head dimension) of a 4-key x 16-column
 // block that 16 lanes read as rows.
 // ---------------------------------------------------------------------------
-#ifndef MARS_TS_VPAD
-#define MARS_TS_VPAD 32
-#endif
 template <int D>
 struct Cfg {
-  static constexpr int BN = 64;                 // keys per tile
-  static constexpr int KST = D + 8;             // K tile row stride in LDS (elements)
-  static constexpr int VST = D + MARS_TS_VPAD;  // V tile row stride in LDS (elements)
-  static constexpr int KSZ = BN * KST;
-  static constexpr int VSZ = BN * VST;
-  static constexpr int STAGE = KSZ + VSZ;       // one K/V stage
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(bf16_t);
-  static_assert(LDS_BYTES <= 80 * 1024, "two workgroups per CU");
+  static constexpr int BN = 64;            // keys per tile
+  static constexpr int CPR = D / 8;        // 16-byte chunks per K or V row
+  static constexpr int TSZ = BN * D;       // one K (or V) tile, elements
+  static constexpr int NBLK = TSZ / 512;   // 1 KiB blocks per tile (one wave load each)
+  static constexpr int BMAX = (NBLK + 3) / 4;  // blocks per wave, at >= 4 waves
 };
+
+// K and V tiles sit in LDS unpadded (a direct global->LDS load writes 1 KiB
+// contiguously per wave), with the 16-byte chunks of each row permuted by an
+// XOR of the row so that the reads below hit all 64 banks:
+//  * K rows are read 16 at a time at one chunk (ds_read_b128);
+//  * V is read through ds_read_b64_tr_b16, 4 rows x 4 chunks per 32 lanes.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 64 ? (r >> 1) & 7 : r & 15;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
+}
 
 // Rescaling of the running output is deferred until a row maximum grows by
 // more than 2^8: until then exp2(s - m) stays below 256, which neither fp32
@@ -181,21 +189,21 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
 // O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
-// row. kaddr / vaddr are the lane's K and V^T read offsets inside a stage.
+// row. kad[c] / vad[i] are the lane's K and V^T read offsets inside a tile.
 template <int D, int MASK>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
                                           const bf16_t* __restrict__ Vs,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                           float& m, float& l, float cs, int hi_a, int lo_b,
-                                          int wb, int kaddr, int vaddr) {
-  using C = Cfg<D>;
+                                          int wb, const int (&kad)[D / 16],
+                                          const int (&vad)[D / 32]) {
   f32x16 s[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     s[n] = f32x16{};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 ka = *(const bf16x8*)(Ks + kaddr + 32 * n * C::KST + 16 * c);
+      const bf16x8 ka = *(const bf16x8*)(Ks + kad[c] + 32 * n * D);
       s[n] = mfma32(ka, qf[c], s[n]);
     }
   }
@@ -252,8 +260,8 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
   for (int i = 0; i < D / 32; ++i) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const bf16x4 vlo = lds_read_tr(Vs + vaddr + 16 * kc * C::VST + 32 * i);
-      const bf16x4 vhi = lds_read_tr(Vs + vaddr + (16 * kc + 8) * C::VST + 32 * i);
+      const bf16x4 vlo = lds_read_tr(Vs + vad[i] + 16 * kc * D);
+      const bf16x4 vhi = lds_read_tr(Vs + vad[i] + (16 * kc + 8) * D);
       const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
       o[i] = mfma32(va, pb[kc], o[i]);
     }
@@ -288,7 +296,10 @@ __device__ __forceinline__ void rows_key_ranges(int a0, int a_last, int L, int B
 template <int D>
 __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p) {
   using C = Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  // two K/V stages (K tile then V tile), separate objects so that reads of
+  // one stage are not ordered behind the direct loads filling the other
+  __shared__ __attribute__((aligned(16))) bf16_t stage0[2 * C::TSZ];
+  __shared__ __attribute__((aligned(16))) bf16_t stage1[2 * C::TSZ];
   const int NT = 64 * p.nw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -363,33 +374,24 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     qf[c] = __builtin_bit_cast(
         bf16x8, buf_load16(rq, (uint32_t)((a * qs + 16 * c + 8 * hf) * sizeof(bf16_t))));
 
-  constexpr int KCH = C::BN * D / 8;                   // 16-byte chunks per K (or V) tile
-  constexpr int KMAX = (KCH + 4 * 64 - 1) / (4 * 64);  // per thread, at >= 4 waves
-  u32x4 kreg[KMAX], vreg[KMAX];
-
   auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
 
-  auto load_tile = [&](int it) {
+  // Direct global -> LDS loads: wave w fills 1 KiB blocks w, w + nw, ... of
+  // the K and V tiles; lane l writes 16 bytes at block offset 16 l, which is
+  // chunk slot l % CPR of row (block * 64 + l) / CPR, holding the global chunk
+  // slot ^ swz(row). Rows past the end of the sequence read as zeros.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto issue_tile = [&](int it, bf16_t* st) {
     const int c0 = tile_c0(it);
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const int idx = min(tid + NT * i, KCH - 1);
-      const int row = idx / (D / 8), ch = idx % (D / 8);
-      const uint32_t off = (uint32_t)(((c0 + row) * rs + ch * 8) * sizeof(bf16_t));
-      kreg[i] = buf_load16(rk, off);
-      vreg[i] = buf_load16(rv, off);
-    }
-  };
-
-  auto store_tile = [&](bf16_t* Ks) {
-    bf16_t* Vs = Ks + C::KSZ;
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      const int idx = tid + NT * i;
-      if (idx < KCH) {
-        const int row = idx / (D / 8), ch = idx % (D / 8);
-        *(u32x4*)(Ks + row * C::KST + ch * 8) = kreg[i];
-        *(u32x4*)(Vs + row * C::VST + ch * 8) = vreg[i];
+    for (int i = 0; i < C::BMAX; ++i) {
+      const int blk = wu + p.nw * i;
+      if (blk < C::NBLK) {
+        const int u = blk * 64 + lane;
+        const int row = u / C::CPR, slot = u % C::CPR;
+        const uint32_t rowb = (uint32_t)(((c0 + row) * rs) * sizeof(bf16_t));
+        lds_load16(rk, st + blk * 512, rowb + 16 * (slot ^ swz_k<D>(row)));
+        lds_load16(rv, st + C::TSZ + blk * 512, rowb + 16 * (slot ^ swz_v<D>(row)));
       }
     }
   };
@@ -399,17 +401,22 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // lane read offsets inside a stage: K rows for S^T, and the transposing
-  // V read (16-lane group g = lane / 16 reads keys 4 (g / 2) + lane % 16 / 4
-  // at columns 16 (g % 2) + 4 (lane % 4))
-  const int kaddr = j * C::KST + 8 * hf;
-  const int vaddr = (4 * hf + ((lane & 15) >> 2)) * C::VST + 16 * ((lane >> 4) & 1) +
-                    4 * (lane & 3);
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(lds);
+  // lane read offsets inside a tile. K: row j (+ 32 n), chunk 2c + hf.
+  // V (transposing read): 16-lane group g = lane / 16 reads keys
+  // 4 (g / 2) + lane % 16 / 4 (+ 16 kc, + 8) at head-dimension columns
+  // 32 i + 16 (g % 2) + 4 (lane % 4), i.e. chunk 4 i + 2 (g % 2) + lane % 4 / 2.
+  int kad[D / 16], vad[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) kad[c] = j * D + 8 * ((2 * c + hf) ^ swz_k<D>(j));
+  {
+    const int vrow = 4 * hf + ((lane & 15) >> 2);
+    const int vlow = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+      vad[i] = vrow * D + 8 * ((4 * i + vlow) ^ swz_v<D>(vrow)) + 4 * (lane & 1);
   }
+
+  if (ntiles > 0) issue_tile(0, stage0);
   // The query fragments must have landed before the loop: otherwise the
   // wait-count bookkeeping treats them as in flight on every iteration and
   // each tile would stall on its own prefetch.
@@ -421,12 +428,12 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   // address is a lane offset plus an immediate
   auto iteration = [&](int it, auto stage_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (it + 1 < ntiles) load_tile(it + 1);
-    // keep the prefetch issued before the compute, and its LDS stores after it
+    if (it + 1 < ntiles) issue_tile(it + 1, STG == 0 ? stage1 : stage0);
+    // keep the prefetch issued before the compute
     __builtin_amdgcn_sched_barrier(0);
 
-    const bf16_t* Ks = lds + STG * C::STAGE;
-    const bf16_t* Vs = Ks + C::KSZ;
+    const bf16_t* Ks = STG == 0 ? stage0 : stage1;
+    const bf16_t* Vs = Ks + C::TSZ;
     const int c0 = tile_c0(it);
     const bool in_r1 = it < n1;
     const int lim_lo = in_r1 ? 0 : r2_lo;       // the staged range this tile belongs to
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
     if (need) {
       if (in_r1 && c0 + C::BN - 1 < w_full) {
-        tile_step<D, kMaskNone>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, 0, 0, kaddr, vaddr);
+        tile_step<D, kMaskNone>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, 0, 0, kad, vad);
       } else {
         // the row's visible intervals clipped to the staged range, relative
         // to the lane's first key
@@ -447,20 +454,20 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
         const bool any_a = __builtin_amdgcn_ballot_w64(hi_a > 0) != 0;
         const bool any_b = __builtin_amdgcn_ballot_w64(wb > 0) != 0;
         if (!any_b) {
-          tile_step<D, kMaskUpper>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, 0, 0, kaddr,
-                                   vaddr);
+          tile_step<D, kMaskUpper>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, 0, 0, kad,
+                                   vad);
         } else if (!any_a) {
-          tile_step<D, kMaskRange>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, lo_b, wb, kaddr,
-                                   vaddr);
+          tile_step<D, kMaskRange>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, lo_b, wb, kad,
+                                   vad);
         } else {
-          tile_step<D, kMaskBoth>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, lo_b, wb, kaddr,
-                                  vaddr);
+          tile_step<D, kMaskBoth>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, lo_b, wb, kad,
+                                  vad);
         }
       }
     }
 
-    __builtin_amdgcn_sched_barrier(0);
-    if (it + 1 < ntiles) store_tile(lds + (1 - STG) * C::STAGE);
+    // the next stage has landed (the barrier waits for this wave's direct
+    // loads) and every wave is done reading this one
     __syncthreads();
   };
 #ifndef MARS_TS_NOUNROLL
@@ -498,10 +505,6 @@ inline int heads_per_wg(int group) {
 template <int D>
 int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   using C = Cfg<D>;
-  if (hipFuncSetAttribute((const void*)two_stream_bf16_kernel<D>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)C::LDS_BYTES) != hipSuccess)
-    return MARS_ERR_LAUNCH;
   // d = 64: one head x 4 row tiles per workgroup, so that three 4-wave
   // workgroups share a CU (the kernel is bound by vector-ALU softmax work and
   // needs the extra waves to hide latency). d = 128: the GQA heads sharing a
@@ -514,7 +517,7 @@ int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   const double nblocks = (double)a.batch * a.Hkv * a.nhc * a.nqt;
   if (nblocks >= 2147483647.0) return MARS_ERR_SHAPE;
   hipLaunchKernelGGL(two_stream_bf16_kernel<D>, dim3((unsigned)nblocks), dim3(64 * a.nw),
-                     C::LDS_BYTES, st, a);
+                     0, st, a);
   return mars_launch_status();
 }
 

@@ -69,6 +69,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_block + 16 l (lds_block must be the same for the whole wave); reads
+// outside the buffer view land as zeros.
+__device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_block, uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block,
+                                           16, byte_off, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
