@@ -190,6 +190,13 @@ __device__ __forceinline__ float halves_sum(float x) {
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
 // O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
 // row. kad[c] / vad[i] are the lane's K and V^T read offsets inside a tile.
+//
+// The tile is worked as two 32-key halves in a software pipeline, so that a
+// wave always has matrix work next to its vector work: the scores of half 1
+// are multiplied while the probabilities of half 0 are formed, and half 0's
+// P V products run while half 1's probabilities are formed. Each half keeps
+// the lazy running maximum; when half 1 raises it, the output is rescaled
+// after half 0's products (which were formed with the old maximum).
 template <int D, int MASK>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
                                           const bf16_t* __restrict__ Vs,
@@ -197,75 +204,110 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
                                           float& m, float& l, float cs, int hi_a, int lo_b,
                                           int wb, const int (&kad)[D / 16],
                                           const int (&vad)[D / 32]) {
-  f32x16 s[2];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    s[n] = f32x16{};
+  auto qk = [&](int n) {
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       const bf16x8 ka = *(const bf16x8*)(Ks + kad[c] + 32 * n * D);
-      s[n] = mfma32(ka, qf[c], s[n]);
+      acc = mfma32(ka, qf[c], acc);
     }
-  }
-  if constexpr (MASK != kMaskNone) {
-    // tie the bounds to the scores so that the per-key tests are computed
-    // after the products, not hoisted above them with every result held live
-    asm volatile("" : "+v"(hi_a), "+v"(lo_b), "+v"(wb) : "v"(s[0]), "v"(s[1]));
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
+    return acc;
+  };
+  auto mask = [&](f32x16& sv, int n) {
+    if constexpr (MASK != kMaskNone) {
+      // tie the bounds to the scores so that the per-key tests are computed
+      // after the products, not hoisted above them with every result held live
+      int ha = hi_a, lb = lo_b, w = wb;
+      asm volatile("" : "+v"(ha), "+v"(lb), "+v"(w) : "v"(sv));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 32 * n + 8 * (r >> 2) + (r & 3);
         bool vis;
         if constexpr (MASK == kMaskUpper) {
-          vis = off < hi_a;
+          vis = off < ha;
         } else if constexpr (MASK == kMaskRange) {
-          vis = (uint32_t)(off - lo_b) < (uint32_t)wb;
+          vis = (uint32_t)(off - lb) < (uint32_t)w;
         } else {
-          vis = (off < hi_a) | ((uint32_t)(off - lo_b) < (uint32_t)wb);
+          vis = (off < ha) | ((uint32_t)(off - lb) < (uint32_t)w);
         }
-        s[n][r] = vis ? s[n][r] : -INFINITY;
+        sv[r] = vis ? sv[r] : -INFINITY;
       }
-  }
-  // row max of the raw scores (the scale is positive, so it commutes with max)
-  float mt = -INFINITY;
+    }
+  };
+  // row max of the raw scores, in log2 units (the scale is positive, so it
+  // commutes with max)
+  auto row_max = [&](const f32x16& sv) {
+    float mt = -INFINITY;
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[n][r]);
-  mt = halves_max(mt) * cs;
-  const bool grow = mt > m + kLazyRescale;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    const float mnew = grow ? mt : m;
-    // 1 when unchanged (also when still -inf), 0 when the first key arrives
-    const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-    m = mnew;
-  }
-  const float nm = m == -INFINITY ? 0.f : -m;
-  bf16x8 pb[4];
-  float ls = 0.f;
-#pragma unroll
-  for (int n = 0; n < 2; ++n)
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[r]);
+    return halves_max(mt) * cs;
+  };
+  // probabilities of 32 keys relative to the max -nm, as bf16 B fragments;
+  // returns their fp32 sum
+  auto probs = [&](const f32x16& sv, float nm, bf16x8& pa, bf16x8& pbk) {
+    float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = fast_exp2(fmaf(s[n][r], cs, nm));
+      const float e = fast_exp2(fmaf(sv[r], cs, nm));
       ls += e;
-      pb[2 * n + (r >> 3)][r & 7] = (bf16_t)e;
+      if (r < 8)
+        pa[r] = (bf16_t)e;
+      else
+        pbk[r - 8] = (bf16_t)e;
     }
-  l += ls;
+    return ls;
+  };
+  auto pv = [&](int kc, const bf16x8& pk) {
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int i = 0; i < D / 32; ++i) {
       const bf16x4 vlo = lds_read_tr(Vs + vad[i] + 16 * kc * D);
       const bf16x4 vhi = lds_read_tr(Vs + vad[i] + (16 * kc + 8) * D);
       const bf16x8 va = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-      o[i] = mfma32(va, pb[kc], o[i]);
+      o[i] = mfma32(va, pk, o[i]);
+    }
+  };
+
+  // ---- half 0: scores, max; a growth rescales the earlier tiles' output
+  f32x16 s0 = qk(0);
+  mask(s0, 0);
+  {
+    const float mt = row_max(s0);
+    const bool grow = mt > m + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? mt : m;
+      // 1 when unchanged (also when still -inf), 0 when the first key arrives
+      const float alpha = m == mnew ? 1.f : fast_exp2(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      m = mnew;
     }
   }
+  // ---- half 1 scores | half 0 probabilities
+  f32x16 s1 = qk(1);
+  bf16x8 p0, p1;
+  l += probs(s0, m == -INFINITY ? 0.f : -m, p0, p1);
+  mask(s1, 1);
+  const float mt1 = row_max(s1);
+  const bool grow1 = mt1 > m + kLazyRescale;
+  const bool any1 = __builtin_amdgcn_ballot_w64(grow1) != 0;
+  const float m1 = grow1 ? mt1 : m;
+  // ---- half 0 P V (old max) | half 1 probabilities (new max)
+  pv(0, p0);
+  pv(1, p1);
+  bf16x8 p2, p3;
+  const float l1 = probs(s1, m1 == -INFINITY ? 0.f : -m1, p2, p3);
+  if (any1) {
+    const float alpha = m == m1 ? 1.f : fast_exp2(m - m1);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+    m = m1;
+  }
+  l += l1;
+  // ---- half 1 P V
+  pv(2, p2);
+  pv(3, p3);
 }
 
 // Key ranges a block of query rows [a0, a_last] needs: r1 = [0, r1_hi) and
