@@ -512,14 +512,10 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     // loads) and every wave is done reading this one
     __syncthreads();
   };
-#ifndef MARS_TS_NOUNROLL
   for (int it = 0; it < ntiles; it += 2) {
     iteration(it, std::integral_constant<int, 0>{});
     if (it + 1 < ntiles) iteration(it + 1, std::integral_constant<int, 1>{});
   }
-#else
-  for (int it = 0; it < ntiles; ++it) iteration(it, std::integral_constant<int, 0>{});
-#endif
 
   const float lt = halves_sum(l);
   if (a >= p.twoL) return;
