@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MARS hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--profile-pass]
 
 A step is one pass of the whole hot path over synthetic, Qwen2.5-shaped inputs
 that are resident in HBM before timing starts:
@@ -20,6 +20,12 @@ kernels run on. Extras (skippable with --no-extras): the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), and the CPU oracle timed on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
+
+`roofline.traffic` is the HBM bytes one launch moves, from two rocprofv3
+counter runs of `--profile-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled
+by what the counter reads for a plain copy of known size; it is null when the
+kernel sources changed after the counters were taken. `--profile-pass` copies
+a 1 GiB buffer once and then launches every hot-path kernel once.
 """
 
 from __future__ import annotations
@@ -110,9 +116,13 @@ class Timer:
         return float(np.mean(self.samples[n]))
 
 
-def roofline(bound, achieved, peak, unit, traffic=None):
-    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic}
+def roofline(bound, achieved, peak, unit, traffic=None, algorithmic_bytes=None):
+    r = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4),
+         "traffic": None if traffic is None else int(round(traffic))}
+    if algorithmic_bytes is not None:
+        r["algorithmic_bytes"] = int(round(algorithmic_bytes))
+    return r
 
 
 def cpu_baseline(q, k, v, budget_s):
@@ -147,6 +157,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="copy 1 GiB once, launch each hot-path kernel once, exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -226,6 +238,20 @@ def main():
             timer.mark()
             timer.stop()
 
+    if args.profile_pass:
+        n = 1 << 28  # float32 elements: a 1 GiB calibration copy
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        step(0, False)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": n * 4,
+                          "status_flags": int(status.item())}), flush=True)
+        return
+
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i, False)
@@ -261,14 +287,21 @@ def main():
     lm_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + N * LM["V"] * 4
     commit_bytes = accepted / args.steps * DEC["Hkv"] * DEC["d"] * 2 * 2 * 2
 
+    from block_masked_causal_amd.profile_summary import load_traffic
+    traffic = load_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    b2, L2, Hq2, Hkv2, d2 = TS["batch"], TS["L"], TS["Hq"], TS["Hkv"], TS["d"]
+    ts_bytes = b2 * 2 * L2 * d2 * 2 * (2 * Hq2 + 2 * Hkv2)   # read Q, K, V; write O (bf16)
     kernels = {
-        "two_stream_attention": roofline("mfma", value, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "two_stream_attention": roofline("mfma", value, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                         traffic.get("two_stream_attention"), ts_bytes),
         "block_decode_attention": roofline("hbm", dbytes / (t_dec * 1e-3) / 1e9, PEAK_HBM_GBS,
-                                           "GB/s"),
+                                           "GB/s", traffic.get("block_decode_attention"),
+                                           dbytes),
         "lmhead_gemm_plus_confidence": roofline(
-            "hbm", (lm_bytes + N * LM["V"] * 4) / (t_lm * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+            "hbm", (lm_bytes + N * LM["V"] * 4) / (t_lm * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+            traffic.get("lmhead_gemm_plus_confidence"), lm_bytes + N * LM["V"] * 4),
         "accept_commit": roofline("hbm", commit_bytes / (t_acc * 1e-3) / 1e9, PEAK_HBM_GBS,
-                                  "GB/s"),
+                                  "GB/s", traffic.get("accept_commit"), commit_bytes),
     }
     kernels["block_decode_attention"]["useful_tflops"] = round(dflops / (t_dec * 1e-3) / 1e12, 3)
     kernels["lmhead_gemm_plus_confidence"]["useful_tflops"] = round(
