@@ -108,10 +108,11 @@ def mars_lmhead_workspace_bytes(N, V):
 
 
 def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None,
-                           workspace=None, status=None, stream=None, N=None, V=None):
+                           workspace=None, status=None, stream=None, fused=False):
     """LM head + confidence. With hidden [N,D] bf16 and w_lm [V,D] bf16, writes fp32
-    logits [N,V]; with hidden None, `logits` is the input. Returns
-    (logits, top_id int32 [N], p_max fp32 [N])."""
+    logits [N,V] (or, with fused=True, writes no logits and returns None for them);
+    with hidden None, `logits` is the input. Returns (logits, top_id int32 [N],
+    p_max fp32 [N])."""
     if hidden is not None:
         _need(hidden, "hidden", torch.bfloat16, 2)
         _need(w_lm, "w_lm", torch.bfloat16, 2)
@@ -119,15 +120,20 @@ def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None
         V = w_lm.shape[0]
         if w_lm.shape[1] != D:
             raise ValueError("w_lm must be [V, D]")
-        if logits is None:
+        if fused:
+            if logits is not None:
+                raise ValueError("fused=True writes no logits; pass logits=None")
+        elif logits is None:
             logits = torch.empty((N, V), dtype=torch.float32, device=hidden.device)
+        dev = hidden.device
     else:
-        if logits is None:
-            raise ValueError("logits are required when hidden is None")
+        if logits is None or fused:
+            raise ValueError("logits are required (and fused is off) when hidden is None")
         D = 0
-    _need(logits, "logits", torch.float32, 2)
-    N, V = logits.shape
-    dev = logits.device
+    if logits is not None:
+        _need(logits, "logits", torch.float32, 2)
+        N, V = logits.shape
+        dev = logits.device
     if top_id is None:
         top_id = torch.empty(N, dtype=torch.int32, device=dev)
     if p_max is None:

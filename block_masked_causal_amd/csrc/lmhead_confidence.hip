@@ -25,6 +25,27 @@ using namespace mars;
 
 namespace {
 
+// Per-row confidence partial over a slice of the vocabulary.
+struct ConfPart {
+  float m;
+  int32_t idx;
+  double s;  // sum of exp(l - m) over the chunk
+};
+
+
+// Combine (m1, i1, s1) with (m2, i2, s2); ties in m keep the lower index.
+__device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, float m2, int i2,
+                                             double s2) {
+  const float M = fmaxf(m1, m2);
+  const double w1 = m1 == -INFINITY ? 0.0 : (double)fast_exp2((m1 - M) * kLog2e);
+  const double w2 = m2 == -INFINITY ? 0.0 : (double)fast_exp2((m2 - M) * kLog2e);
+  const int idx = m1 > m2 ? i1 : (m2 > m1 ? i2 : min(i1, i2));
+  s1 = s1 * w1 + s2 * w2;
+  m1 = M;
+  i1 = idx;
+}
+
+
 // ------------------------------------------------------------------ GEMM ----
 // Workgroup tile: GM rows (all positions, up to 256) x GN vocabulary entries;
 // 8 waves as 4 (rows) x 2 (vocab), each wave 64 x 128 outputs, so each pair
@@ -51,11 +72,21 @@ struct GemmCfg {
 struct GemmArgs {
   const bf16_t* hidden;
   const bf16_t* w;
-  float* logits;
-  int N, D, V;
+  float* logits;     // unfused: [N, V] fp32
+  ConfPart* part;    // fused: [N][nvt] partials, one per vocabulary tile
+  int32_t* status;
+  int N, D, V, nvt;
 };
 
-template <int GK>
+// logits^T = W . hidden^T: the MFMA A operand is a 32-entry slice of the
+// vocabulary, B a 32-position slice, so lane (j, hf) of tile (va, pb) holds
+// position n0 + wn*64 + 32 pb + j and vocabulary entries
+// v0 + wv*128 + 32 va + 8 (r / 4) + 4 hf + r % 4, r = 0..15. A position's
+// 256 entries of the workgroup tile are thus 64 values in each of 4 lanes
+// (two halves of two waves): FUSED reduces them in registers to the
+// confidence partial (max, first argmax, sum exp(l - max)) and writes no
+// logits.
+template <int GK, bool FUSED>
 __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   using C = GemmCfg<GK>;
   constexpr int GST = C::GST, CPR = C::CPR, AL = C::AL, BL = C::BL;
@@ -106,28 +137,28 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
     }
   };
 
-  f32x16 acc[2][WNT];
+  f32x16 acc[WNT][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < WNT; ++a)
 #pragma unroll
-    for (int b = 0; b < WNT; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
   auto compute = [&](int buf) {
     const bf16_t* A = As(buf);
     const bf16_t* Bm = Bs(buf);
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 af[2], bfr[WNT];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        af[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
+      bf16x8 wf[WNT], hfr[2];
 #pragma unroll
       for (int t = 0; t < WNT; ++t)
-        bfr[t] = *(const bf16x8*)(Bm + (wv * (GN / 2) + 32 * t + j) * GST + 16 * ks + 8 * hf);
+        wf[t] = *(const bf16x8*)(Bm + (wv * (GN / 2) + 32 * t + j) * GST + 16 * ks + 8 * hf);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int t = 0; t < 2; ++t)
+        hfr[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
 #pragma unroll
-        for (int b = 0; b < WNT; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+      for (int a = 0; a < WNT; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(wf[a], hfr[b], acc[a][b]);
     }
   };
 
@@ -159,32 +190,113 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   for (int kt = 0; kt < nk; kt += kWRing) {
     step(kt, std::integral_constant<int, 0>{});
     if constexpr (kWRing > 1) if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % kWRing>{});
-    if constexpr (kWRing > 2) if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2 % kWRing>{});
-    if constexpr (kWRing > 3) if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % kWRing>{});
   }
 
-  // lane (j, hf) holds C[8*(r/4) + 4*hf + r%4][j]: rows = positions, j = vocab
+  const int vb = v0 + wv * (GN / 2) + 4 * hf;  // + 32 va + 8 (r / 4) + r % 4
+  if constexpr (!FUSED) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) {
+      const int n = n0 + wn * 64 + 32 * b + j;
+      if (n >= p.N) continue;
+      float* row = p.logits + (size_t)n * p.V;
 #pragma unroll
-    for (int b = 0; b < WNT; ++b) {
-      const int v = v0 + wv * (GN / 2) + 32 * b + j;
-      if (v >= p.V) continue;
+      for (int a = 0; a < WNT; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wn * 64 + 32 * a + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (n < p.N) p.logits[(size_t)n * p.V + v] = acc[a][b][r];
+        for (int g = 0; g < 4; ++g) {
+          const int v = vb + 32 * a + 8 * g;  // 4 consecutive entries; V % 4 == 0
+          if (v < p.V)
+            *(f32x4*)(row + v) = f32x4{acc[a][b][4 * g], acc[a][b][4 * g + 1],
+                                       acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]};
+        }
+    }
+  } else {
+    // exchange area for the two waves sharing a position (the K loop is done)
+    float* xm = (float*)gl;
+    int* xi = (int*)(xm + 4 * 64);
+    double* xs = (double*)(xi + 4 * 64);
+    bool bad = false;
+    float pm[2];
+    int pi[2];
+    double ps[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < WNT; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int v = vb + 32 * a + 8 * (r >> 2) + (r & 3);
+          if (v < p.V) m = fmaxf(m, acc[a][b][r]);
+        }
+      // the lowest entry equal to the max: walk the lane's entries downwards
+      int idx = 0x7FFFFFFF;
+      float sum = 0.f;
+#pragma unroll
+      for (int a = WNT - 1; a >= 0; --a)
+#pragma unroll
+        for (int r = 15; r >= 0; --r) {
+          const int v = vb + 32 * a + 8 * (r >> 2) + (r & 3);
+          const float x = acc[a][b][r];
+          if (v < p.V) {
+            idx = x == m ? v : idx;
+            sum += fast_exp2((x - m) * kLog2e);
+          }
+        }
+      if (m == -INFINITY) sum = 0.f;  // no entry of this lane lies below V
+      bad |= (m != -INFINITY) && !(isfinite(m) && isfinite(sum));
+      double sd = (double)sum;
+      // the other half of the wave holds the interleaved entries of the same position
+      const auto sm_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                        false, false);
+      const auto si_ = __builtin_amdgcn_permlane32_swap((uint32_t)idx, (uint32_t)idx, false,
+                                                        false);
+      const uint64_t sb = __builtin_bit_cast(uint64_t, sd);
+      const auto slo = __builtin_amdgcn_permlane32_swap((uint32_t)sb, (uint32_t)sb, false,
+                                                        false);
+      const auto shi = __builtin_amdgcn_permlane32_swap((uint32_t)(sb >> 32),
+                                                        (uint32_t)(sb >> 32), false, false);
+      // the swap leaves the lower half's values in one result and the upper
+      // half's in the other, in every lane; the combination is symmetric
+      // (commutative sum, ties to the lower index), so their order is immaterial
+      m = __uint_as_float(sm_[0]);
+      idx = (int)si_[0];
+      sd = __builtin_bit_cast(double, ((uint64_t)shi[0] << 32) | (uint64_t)slo[0]);
+      conf_combine(m, idx, sd, __uint_as_float(sm_[1]), (int)si_[1],
+                   __builtin_bit_cast(double, ((uint64_t)shi[1] << 32) | (uint64_t)slo[1]));
+      pm[b] = m;
+      pi[b] = idx;
+      ps[b] = sd;
+    }
+    if (bad) status_or(p.status, MARS_STATUS_NONFINITE);
+    if (wv == 1 && hf == 0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int slot = wn * 64 + 32 * b + j;
+        xm[slot] = pm[b];
+        xi[slot] = pi[b];
+        xs[slot] = ps[b];
       }
     }
+    __syncthreads();
+    if (wv == 0 && hf == 0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int slot = wn * 64 + 32 * b + j;
+        const int n = n0 + slot;
+        conf_combine(pm[b], pi[b], ps[b], xm[slot], xi[slot], xs[slot]);
+        if (n < p.N) {
+          ConfPart out;
+          out.m = pm[b];
+          out.idx = pi[b];
+          out.s = ps[b];
+          p.part[(size_t)n * p.nvt + blockIdx.x] = out;
+        }
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------ confidence ----
-struct ConfPart {
-  float m;
-  int32_t idx;
-  double s;  // sum of exp(l - m) over the chunk
-};
-
 struct ConfArgs {
   const float* logits;
   int32_t* top_id;
@@ -193,18 +305,6 @@ struct ConfArgs {
   int32_t* status;
   int N, V, nchunk, chunk;  // chunk: elements per chunk, multiple of 4
 };
-
-// Combine (m1, i1, s1) with (m2, i2, s2); ties in m keep the lower index.
-__device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, float m2, int i2,
-                                             double s2) {
-  const float M = fmaxf(m1, m2);
-  const double w1 = m1 == -INFINITY ? 0.0 : (double)fast_exp2((m1 - M) * kLog2e);
-  const double w2 = m2 == -INFINITY ? 0.0 : (double)fast_exp2((m2 - M) * kLog2e);
-  const int idx = m1 > m2 ? i1 : (m2 > m1 ? i2 : min(i1, i2));
-  s1 = s1 * w1 + s2 * w2;
-  m1 = M;
-  i1 = idx;
-}
 
 __global__ __launch_bounds__(256) void conf_partial_kernel(ConfArgs p) {
   const int c = blockIdx.x, row = blockIdx.y;
@@ -274,6 +374,41 @@ __global__ __launch_bounds__(256) void conf_merge_kernel(ConfArgs p) {
   p.p_max[row] = (float)(1.0 / S);
 }
 
+// Merge of many partials per row (the fused path: one per 256-entry vocabulary
+// tile): one workgroup per row, each thread folds a strided subset in order,
+// then a fixed butterfly over the wave and a fixed order over the 4 waves.
+__global__ __launch_bounds__(256) void conf_merge_wide_kernel(ConfArgs p) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const ConfPart* pr = p.part + (size_t)row * p.nchunk;
+  float m = -INFINITY;
+  int idx = 0x7FFFFFFF;
+  double s = 0.0;
+  for (int c = tid; c < p.nchunk; c += 256) conf_combine(m, idx, s, pr[c].m, pr[c].idx, pr[c].s);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(idx, o);
+    const double s2 = __shfl_xor(s, o);
+    conf_combine(m, idx, s, m2, i2, s2);
+  }
+  __shared__ float sm[4];
+  __shared__ int si[4];
+  __shared__ double ss[4];
+  const int wv = tid >> 6;
+  if ((tid & 63) == 0) {
+    sm[wv] = m;
+    si[wv] = idx;
+    ss[wv] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < 4; ++k) conf_combine(sm[0], si[0], ss[0], sm[k], si[k], ss[k]);
+    p.top_id[row] = si[0] == 0x7FFFFFFF ? 0 : si[0];
+    p.p_max[row] = (float)(1.0 / ss[0]);
+  }
+}
+
 void conf_layout(int N, int V, int* nchunk, int* chunk) {
   int c = std::max(1, std::min(32, (2048 + N - 1) / N));
   c = std::min(c, std::max(1, (V + 1023) / 1024));
@@ -287,14 +422,14 @@ void conf_layout(int N, int V, int* nchunk, int* chunk) {
 }  // namespace
 
 namespace {
-template <int GK>
+template <int GK, bool FUSED>
 int launch_gemm(dim3 grid, hipStream_t st, const GemmArgs& g) {
   // the workgroup tile needs more than the default 64 KiB of dynamic LDS
-  if (hipFuncSetAttribute((const void*)lmhead_gemm_kernel<GK>,
+  if (hipFuncSetAttribute((const void*)lmhead_gemm_kernel<GK, FUSED>,
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)GemmCfg<GK>::LDS) != hipSuccess)
     return MARS_ERR_LAUNCH;
-  hipLaunchKernelGGL(lmhead_gemm_kernel<GK>, grid, dim3(GT), GemmCfg<GK>::LDS, st, g);
+  hipLaunchKernelGGL((lmhead_gemm_kernel<GK, FUSED>), grid, dim3(GT), GemmCfg<GK>::LDS, st, g);
   return MARS_OK;
 }
 }  // namespace
@@ -303,15 +438,17 @@ extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
   if (N < 1 || V < 4 || V % 4) return 0;
   int nchunk, chunk;
   conf_layout(N, V, &nchunk, &chunk);
-  return (size_t)N * nchunk * sizeof(ConfPart);
+  const int nvt = (V + GN - 1) / GN;  // fused path: one partial per vocabulary tile
+  return (size_t)N * std::max(nchunk, nvt) * sizeof(ConfPart);
 }
 
 extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits,
                                       int32_t N, int32_t D, int32_t V, int32_t* top_id,
                                       float* p_max, void* workspace, size_t workspace_bytes,
                                       int32_t* status, void* stream) {
-  MARS_REQUIRE(logits && top_id && p_max, MARS_ERR_NULL);
+  MARS_REQUIRE(top_id && p_max, MARS_ERR_NULL);
   MARS_REQUIRE(!hidden || w_lm, MARS_ERR_NULL);
+  MARS_REQUIRE(hidden || logits, MARS_ERR_NULL);  // logits may be omitted only when fused
   MARS_REQUIRE(N >= 1 && V >= 4 && V % 4 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(N <= 65535, MARS_ERR_SHAPE);  // confidence grid: one row per gridDim.y
   MARS_REQUIRE((double)N * V < 9.0e18, MARS_ERR_SHAPE);
@@ -324,18 +461,6 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
   MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
   hipStream_t st = (hipStream_t)stream;
 
-  if (hidden) {
-    GemmArgs g;
-    g.hidden = (const bf16_t*)hidden;
-    g.w = (const bf16_t*)w_lm;
-    g.logits = logits;
-    g.N = N;
-    g.D = D;
-    g.V = V;
-    dim3 grid((V + GN - 1) / GN, (N + GM - 1) / GM);
-    const int rc = D % 64 == 0 ? launch_gemm<64>(grid, st, g) : launch_gemm<32>(grid, st, g);
-    if (rc != MARS_OK) return rc;
-  }
   ConfArgs c;
   c.logits = logits;
   c.top_id = top_id;
@@ -344,6 +469,31 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
   c.status = status;
   c.N = N;
   c.V = V;
+  if (hidden) {
+    GemmArgs g;
+    g.hidden = (const bf16_t*)hidden;
+    g.w = (const bf16_t*)w_lm;
+    g.logits = logits;
+    g.part = (ConfPart*)workspace;
+    g.status = status;
+    g.N = N;
+    g.D = D;
+    g.V = V;
+    g.nvt = (V + GN - 1) / GN;
+    dim3 grid(g.nvt, (N + GM - 1) / GM);
+    const bool fused = logits == nullptr;
+    const int rc = D % 64 == 0 ? (fused ? launch_gemm<64, true>(grid, st, g)
+                                        : launch_gemm<64, false>(grid, st, g))
+                               : (fused ? launch_gemm<32, true>(grid, st, g)
+                                        : launch_gemm<32, false>(grid, st, g));
+    if (rc != MARS_OK) return rc;
+    if (fused) {
+      c.nchunk = g.nvt;
+      c.chunk = GN;
+      hipLaunchKernelGGL(conf_merge_wide_kernel, dim3(N), dim3(256), 0, st, c);
+      return mars_launch_status();
+    }
+  }
   conf_layout(N, V, &c.nchunk, &c.chunk);
   hipLaunchKernelGGL(conf_partial_kernel, dim3(c.nchunk, N), dim3(256), 0, st, c);
   hipLaunchKernelGGL(conf_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, c);

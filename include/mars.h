@@ -150,11 +150,15 @@ size_t mars_decode_workspace_bytes(int32_t S, int32_t B, int32_t n_q_heads, int3
  *         confidence step runs.
  * w_lm    [V, D] bf16 (one row per vocabulary entry); ignored if hidden NULL.
  * logits  [N, V] float32: written (= hidden . w_lm^T, fp32 accumulation) when
- *         hidden != NULL, read otherwise.
+ *         hidden != NULL, read otherwise. May be NULL when hidden != NULL:
+ *         then the confidence is reduced inside the GEMM (per row and
+ *         256-entry vocabulary tile: max, lowest argmax, sum of exp) and no
+ *         logits are written. top_id is identical to the unfused call (same
+ *         fp32 values); p_max agrees to fp32 rounding of the sum order.
  * top_id  [N] int32, p_max [N] float32 (written).
- * workspace >= mars_lmhead_workspace_bytes(N, V) bytes.
+ * workspace >= mars_lmhead_workspace_bytes(N, V) bytes (covers both forms).
  * status  optional: MARS_STATUS_NONFINITE if a row held NaN/Inf (that row's
- *         p_max is then NaN or 0).
+ *         p_max is then NaN or 0). The fused form detects NaN and +Inf.
  * Limits: D % 32 == 0 when hidden != NULL; V % 4 == 0; N >= 1.
  */
 int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits, int32_t N,

@@ -97,7 +97,11 @@ def lm(hidden=FAKE, w=FAKE, logits=FAKE, N=16, D=64, V=1000, ws=FAKE, ws_bytes=1
 
 
 def test_lmhead_argument_checks():
-    assert lm(logits=None) == _lib.MARS_ERR_NULL
+    # logits may be omitted only with an LM head (fused form); every case below is
+    # rejected before any launch, so the fake addresses are never dereferenced
+    assert lm(hidden=None, w=None, logits=None) == _lib.MARS_ERR_NULL
+    assert mars.lib().mars_lmhead_confidence(FAKE, FAKE, None, 16, 64, 1000, None, FAKE, FAKE,
+                                             1 << 20, None, None) == _lib.MARS_ERR_NULL
     assert lm(w=None) == _lib.MARS_ERR_NULL
     assert lm(V=1002) == _lib.MARS_ERR_SHAPE      # V % 4 != 0
     assert lm(D=48) == _lib.MARS_ERR_SHAPE        # D % 32 != 0 with an LM head

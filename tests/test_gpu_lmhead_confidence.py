@@ -118,3 +118,50 @@ def test_full_size_qwen7b_lmhead_sampled_rows():
     assert np.max(np.abs(gp / rp - 1)) <= 1e-3
     # p_max of a random LM head is tiny, so tau in {1.0, 0.9, 0.7} accepts exactly one token
     assert gp.max() < 0.5
+
+
+@pytest.mark.parametrize("N,D,V", [(40, 256, 1000), (300, 96, 516), (256, 3584, 1024),
+                                   (7, 64, 260)])
+def test_fused_confidence_equals_unfused_and_oracle(N, D, V):
+    """GEMM epilogue reduction (no logits written) against the two-pass path on the same
+    device logits (ids bit-exact, p to 1e-6 relative) and against the fp64 oracle.
+    Shapes cover a partial last vocabulary tile, two row tiles, and a K step of 32."""
+    say(f"[lmhead fused] N={N} D={D} V={V}")
+    h, w = synth.lmhead_inputs(5200 + N, N, D, V)
+    H, W = to_dev(h), to_dev(w)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lg, ids_u, p_u = mars.mars_lmhead_confidence(H, W)
+    none, ids_f, p_f = mars.mars_lmhead_confidence(H, W, fused=True, status=status)
+    torch.cuda.synchronize()
+    assert none is None and int(status.item()) == 0
+    assert np.array_equal(ids_f.cpu().numpy(), ids_u.cpu().numpy())
+    pu = p_u.cpu().numpy().astype(np.float64)
+    pf = p_f.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(pf / pu - 1)) <= 1e-6
+    ref = oracle.lmhead(h.f32, w.f32)
+    rid, rp = oracle.confidence(ref)
+    gid = ids_f.cpu().numpy()
+    for i in range(N):
+        top2 = np.sort(ref[i])[-2:]
+        if top2[1] - top2[0] > 2e-4:
+            assert gid[i] == rid[i]
+    assert np.max(np.abs(pf / rp - 1)) <= 1e-3
+
+
+def test_full_size_qwen7b_fused_confidence():
+    """256 x 3584 x 152064 fused: every row against the unfused path, 8 against the oracle."""
+    N, D, V = 256, 3584, 152064
+    say("[lmhead fused] full size 256 x 3584 x 152064")
+    h, w = synth.lmhead_inputs(1004, N, D, V)
+    H, W = to_dev(h), to_dev(w)
+    _, ids_u, p_u = mars.mars_lmhead_confidence(H, W)
+    _, ids_f, p_f = mars.mars_lmhead_confidence(H, W, fused=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids_f.cpu().numpy(), ids_u.cpu().numpy())
+    pu = p_u.cpu().numpy().astype(np.float64)
+    pf = p_f.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(pf / pu - 1)) <= 1e-6
+    rows = [0, 31, 32, 100, 128, 200, 254, 255]
+    ref = oracle.lmhead(h.f32[rows], w.f32)
+    rid, rp = oracle.confidence(ref)
+    assert np.max(np.abs(pf[rows] / rp - 1)) <= 1e-3
