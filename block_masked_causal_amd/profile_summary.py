@@ -34,9 +34,11 @@ CALLS = {
                              ["two_stream_bf16_kernel"]),
     "block_decode_attention": (["attn_decode.hip", "mars_common.hpp"],
                                ["decode_split_kernel", "decode_merge_kernel"]),
+    "lmhead_confidence_fused": (["lmhead_confidence.hip", "mars_common.hpp"],
+                                [r"lmhead_gemm_kernel<\d+, true>", "conf_merge_wide_kernel"]),
     "lmhead_gemm_plus_confidence": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                    ["lmhead_gemm_kernel", "conf_partial_kernel",
-                                     "conf_merge_kernel"]),
+                                    [r"lmhead_gemm_kernel<\d+, false>", "conf_partial_kernel",
+                                     r"conf_merge_kernel\("]),
     "accept_commit": (["accept_commit.hip", "mars_common.hpp"], ["accept_commit_kernel"]),
 }
 COPY_KERNEL = "copyBuffer"
