@@ -14,9 +14,7 @@
 //   * S^T = K Q^T: lane (key i, half hf) reads 16 bytes of its key's row.
 //   * O^T = V^T P^T: the V pages are stored transposed ([d][slot]), so the A
 //     operand of lane (dim, hf) is two 8-byte reads of consecutive slots.
-// The cache of one sequence is cut into chunks (split-K): 256 keys, or 512
-// when there are already enough (sequence, KV head, query tile) items to fill
-// the GPU. Each workgroup handles one (chunk, KV head, sequence) and writes an
+// The cache of one sequence is cut into 512-key chunks (split-K). Each workgroup handles one (chunk, KV head, sequence) and writes an
 // unnormalised partial (O, running max, running sum); a merge kernel combines
 // the chunks. A sequence that fits in one chunk is written out directly.
 // Chunk 0 also handles the B new rows (causal among themselves).
@@ -26,10 +24,15 @@ using namespace mars;
 
 namespace {
 
-// Split-K chunk (cache keys per workgroup): small when sequences x heads alone
-// cannot fill the GPU, larger otherwise (fewer partials to write and merge).
+// Split-K chunk (cache keys per workgroup). 512 keys measured fastest both for
+// 64 sequences x 4 KV heads (where 256-key chunks give more workgroups but twice
+// the partials to write and merge) and for 256 x 4; a chunk's page ids must fit
+// one per lane (<= 64 pages of >= 16 keys).
 inline int decode_chunk(int S, int Hkv, int nqt) {
-  return (long long)S * Hkv * nqt >= 1024 ? 512 : 256;
+  (void)S;
+  (void)Hkv;
+  (void)nqt;
+  return 512;
 }
 constexpr int kMaxQT = 4;    // at most 4 query tiles of 32 packed rows
 

@@ -54,7 +54,7 @@ def test_decode_lengths_on_chunk_and_page_edges():
 
 
 def test_decode_large_batch_uses_512_key_chunks_on_edges():
-    """130 sequences x 8 KV heads fill the GPU without splitting: 512-key chunks;
+    """130 sequences x 8 KV heads, 512-key chunks;
     lengths sit on both sides of the chunk and single-chunk boundaries."""
     rng = np.random.default_rng(3150)
     lens = rng.integers(0, 1100, size=130)
