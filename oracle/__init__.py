@@ -11,6 +11,7 @@ from .mars_oracle import (  # noqa: F401
     causal_mask,
     ar_signal_ratio,
     attn_two_stream,
+    attn_two_stream_backward,
     attn_block_decode,
     gather_prefix,
     lmhead,

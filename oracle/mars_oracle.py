@@ -25,8 +25,8 @@ the lowest token id; "at least one token" means n = max(1, leading run);
 comparisons are p >= tau.
 
 Parity-pin status: every function below is pinned by tests other than itself
-(brute force, closed forms, library routines, printed values). None is
-"parity unpinned".
+(brute force, closed forms, library routines, printed values, central finite
+differences for the attention gradient). None is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -161,6 +161,60 @@ def attn_two_stream(q, k, v, L: int, B: int, scale: float | None = None,
             o[s0:s0 + r.size], l[s0:s0 + r.size] = _softmax_attend(Q, K, Vv, M[r], scale)
         outs[(bi, h)], lses[(bi, h)] = o, l
     return outs, lses
+
+
+def attn_two_stream_backward(q, k, v, do, L: int, B: int, scale: float | None = None,
+                             mask_mode: int = 0, groups=None, row_chunk: int = 1024):
+    """Gradients of `attn_two_stream` with respect to q, k and v, given do = dLoss/dO.
+
+    The pages train the model on L_mask + L_AR through this attention ([notes]
+    关键设计 2; [gist] 2B), so its gradient is that of the forward's definition,
+    by the chain rule. Per query head, with S = scale * Q K^T masked by M,
+    P = softmax over each row of S, O = P V:
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(dO * O))
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+    and a KV head collects dK, dV from every query head that reads it.
+
+    q, do [b, 2L, Hq, d]; k, v [b, 2L, Hkv, d]. `groups` restricts the work to
+    a list of (batch, kv_head): dq of that group's query heads and dk, dv of
+    that KV head are filled, everything else stays zero. Rows are processed in
+    chunks of `row_chunk` (the sums over rows are unchanged by that split).
+    Returns float64 arrays dq [b, 2L, Hq, d], dk, dv [b, 2L, Hkv, d].
+    """
+    q = np.asarray(q)
+    b, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert n == 2 * L and Hq % Hkv == 0
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    M = build_mask(L, B) if mask_mode == 0 else causal_mask(n)
+    if groups is None:
+        groups = [(bi, kv) for bi in range(b) for kv in range(Hkv)]
+    dq = np.zeros((b, n, Hq, d))
+    dk = np.zeros((b, n, Hkv, d))
+    dv = np.zeros((b, n, Hkv, d))
+    for (bi, kv) in groups:
+        K = np.asarray(k[bi, :, kv, :], dtype=np.float64)
+        Vv = np.asarray(v[bi, :, kv, :], dtype=np.float64)
+        for h in range(kv * g, (kv + 1) * g):
+            for r0 in range(0, n, row_chunk):
+                r = np.arange(r0, min(n, r0 + row_chunk))
+                Q = np.asarray(q[bi, r, h, :], dtype=np.float64)
+                dO = np.asarray(do[bi, r, h, :], dtype=np.float64)
+                s = np.where(M[r], (Q @ K.T) * scale, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                o = p @ Vv
+                dp = dO @ Vv.T
+                ds = p * (dp - (dO * o).sum(axis=1, keepdims=True))
+                dq[bi, r, h, :] = scale * (ds @ K)
+                dk[bi, :, kv, :] += scale * (ds.T @ Q)
+                dv[bi, :, kv, :] += p.T @ dO
+    return dq, dk, dv
 
 
 def gather_prefix(cache: np.ndarray, block_table: np.ndarray, s: int, length: int,

@@ -167,6 +167,82 @@ def check_gqa_head_map(attn, L=8, B=2, d=4):
 
 # ------------------------------------------------------------- decode ------
 
+# ------------------------------------------------------- attention backward -
+
+def _forward_full(attn, q, k, v, L, B, mask_mode):
+    """The forward oracle's output as one [b, 2L, Hq, d] array."""
+    outs, _ = attn(q, k, v, L, B, mask_mode=mask_mode)
+    o = np.zeros(q.shape)
+    for (bi, h), val in outs.items():
+        o[bi, :, h] = val
+    return o
+
+
+def check_backward_finite_differences(attn, bwd, L=6, B=2, Hq=4, Hkv=2, d=4, mask_mode=0,
+                                      seed=11):
+    """dLoss/dq, dk, dv of Loss = sum(do * O(q, k, v)) against central differences
+    of the (separately pinned) forward, entry by entry, in float64."""
+    q, k, v = rand_qkv(seed, 1, L, Hq, Hkv, d)
+    do = np.random.default_rng(seed + 1).standard_normal(q.shape)
+    dq, dk, dv = bwd(q, k, v, do, L, B, mask_mode=mask_mode)
+    h = 1e-5
+
+    def loss(qq, kk, vv):
+        return float(np.sum(do * _forward_full(attn, qq, kk, vv, L, B, mask_mode)))
+
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{"qq": args_p["q"], "kk": args_p["k"], "vv": args_p["v"]})
+                        - loss(**{"qq": args_m["q"], "kk": args_m["k"], "vv": args_m["v"]})) / (2 * h)
+        np.testing.assert_allclose(grad, num, atol=1e-7, rtol=0, err_msg=f"d{name}")
+
+
+def check_backward_vs_torch_autograd(bwd, L=10, B=3, Hq=6, Hkv=2, d=8, mask_mode=0, seed=12):
+    """Library reference: torch CPU autograd through dense softmax attention whose mask
+    is the independently written 0-based interval form (float64)."""
+    q, k, v = rand_qkv(seed, 2, L, Hq, Hkv, d)
+    do = np.random.default_rng(seed + 1).standard_normal(q.shape)
+    n = 2 * L
+    if mask_mode == 0:
+        vis = np.array([[zero_based_visible(a, c, L, B) for c in range(n)] for a in range(n)])
+    else:
+        vis = np.tril(np.ones((n, n), dtype=bool))
+    g = Hq // Hkv
+    Q = torch.tensor(q, requires_grad=True)
+    K = torch.tensor(k, requires_grad=True)
+    V = torch.tensor(v, requires_grad=True)
+    Kx = K.repeat_interleave(g, dim=2)
+    Vx = V.repeat_interleave(g, dim=2)
+    s = torch.einsum("bqhd,bkhd->bhqk", Q, Kx) / np.sqrt(d)
+    s = s.masked_fill(~torch.from_numpy(vis), float("-inf"))
+    o = torch.einsum("bhqk,bkhd->bqhd", torch.softmax(s, dim=-1), Vx)
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = bwd(q, k, v, do, L, B, mask_mode=mask_mode)
+    np.testing.assert_allclose(dq, Q.grad.numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dk, K.grad.numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dv, V.grad.numpy(), atol=1e-11, rtol=0)
+
+
+def check_backward_groups_and_chunks(bwd, L=9, B=2, Hq=4, Hkv=2, d=6, seed=13):
+    """Restricting to one (batch, KV head) group, or processing rows in small chunks,
+    gives the same numbers as the full call on the entries it fills."""
+    q, k, v = rand_qkv(seed, 2, L, Hq, Hkv, d)
+    do = np.random.default_rng(seed + 1).standard_normal(q.shape)
+    full = bwd(q, k, v, do, L, B)
+    part = bwd(q, k, v, do, L, B, groups=[(1, 0)], row_chunk=5)
+    np.testing.assert_allclose(part[0][1, :, 0:2], full[0][1, :, 0:2], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(part[1][1, :, 0], full[1][1, :, 0], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(part[2][1, :, 0], full[2][1, :, 0], atol=1e-12, rtol=0)
+    assert not part[0][0].any() and not part[1][:, :, 1].any()
+
+
 def paged_layout(kv_rows: np.ndarray, page_size: int, seed: int, total_pages: int | None = None):
     """Scatter logical rows [n, Hkv, d] into pages; returns (K pages, V^T pages, table)."""
     n, Hkv, d = kv_rows.shape

@@ -179,3 +179,47 @@ def test_commit_off_by_one_is_caught():
 
 def test_lmhead_transposed_is_caught():
     assert _fails(pc.check_lmhead_exact_integers, lambda h, w: (np.asarray(w, np.float64) @ np.asarray(h, np.float64).T))
+
+
+# -- attention backward mutants ------------------------------------------------
+
+def _bwd_mutant(kind):
+    """A copy of the backward oracle with one planted mistake."""
+    def bwd(q, k, v, do, L, B, scale=None, mask_mode=0, groups=None, row_chunk=1024):
+        q = np.asarray(q)
+        b, n, Hq, d = q.shape
+        Hkv = k.shape[2]
+        g = Hq // Hkv
+        sc = 1.0 / np.sqrt(d) if scale is None else scale
+        M = _build_mask(L, B) if mask_mode == 0 else om.causal_mask(n)
+        dq = np.zeros((b, n, Hq, d))
+        dk = np.zeros((b, n, Hkv, d))
+        dv = np.zeros((b, n, Hkv, d))
+        for bi in range(b):
+            for h in range(Hq):
+                kv = h // g
+                K, V = k[bi, :, kv], v[bi, :, kv]
+                Q, dO = q[bi, :, h], do[bi, :, h]
+                s = np.where(M, (Q @ K.T) * sc, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = dO @ V.T
+                if kind == "no_rowsum":
+                    ds = p * dp
+                else:
+                    ds = p * (dp - (dO * (p @ V)).sum(axis=1, keepdims=True))
+                dq[bi, :, h] = sc * (ds @ K)
+                if kind == "gqa_first_head" and h % g:
+                    continue
+                dk[bi, :, kv] += (ds.T @ Q) * (1.0 if kind == "dk_unscaled" else sc)
+                dv[bi, :, kv] += (ds.T @ dO) if kind == "dv_uses_ds" else (p.T @ dO)
+        return dq, dk, dv
+    return bwd
+
+
+@pytest.mark.parametrize("kind", ["no_rowsum", "dk_unscaled", "gqa_first_head", "dv_uses_ds"])
+def test_backward_mutants_are_caught(kind):
+    m = _bwd_mutant(kind)
+    assert _fails(pc.check_backward_finite_differences, oracle.attn_two_stream, m, L=4, B=2,
+                  Hq=2, Hkv=1, d=3)
+    assert _fails(pc.check_backward_vs_torch_autograd, m)

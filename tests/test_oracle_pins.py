@@ -187,3 +187,20 @@ def test_generators_are_seeded_and_bf16_exact():
     x = np.array([1.0, 1.00390625, 1.005859375, -2.5], dtype=np.float32)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: ties go to even (1.0)
     assert list(synth.bf16_bits_to_f32(synth.bf16_round(x))) == [1.0, 1.0, 1.0078125, -2.5]
+
+
+# ---- attention backward ([notes] 关键设计 2: the training loss runs through the forward)
+
+@pytest.mark.parametrize("L,B,mode", [(6, 2, 0), (5, 1, 0), (4, 4, 0), (5, 2, 1)])
+def test_backward_matches_central_differences(L, B, mode):
+    pc.check_backward_finite_differences(oracle.attn_two_stream, oracle.attn_two_stream_backward,
+                                         L=L, B=B, mask_mode=mode)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_backward_matches_torch_autograd(mode):
+    pc.check_backward_vs_torch_autograd(oracle.attn_two_stream_backward, mask_mode=mode)
+
+
+def test_backward_groups_and_row_chunks():
+    pc.check_backward_groups_and_chunks(oracle.attn_two_stream_backward)
