@@ -1,5 +1,6 @@
-"""MARS hot path on MI355X (gfx950): two-stream masked attention, block-decode
-attention, LM-head confidence and left-to-right acceptance with KV commit.
+"""MARS hot path on MI355X (gfx950): two-stream masked attention (forward and
+backward), block-decode attention, LM-head confidence and left-to-right
+acceptance with KV commit.
 
 The compute lives in libmars.so (hand-written HIP kernels behind a C ABI, see
 include/mars.h); this package is a thin ctypes binding with the same names.
@@ -20,6 +21,7 @@ from .api import (  # noqa: F401
     mars_accept_commit,
     mars_attn_block_decode,
     mars_attn_two_stream,
+    mars_attn_two_stream_bwd,
     mars_decode_workspace_bytes,
     mars_lmhead_confidence,
     mars_lmhead_workspace_bytes,

@@ -66,6 +66,37 @@ def mars_attn_two_stream(q, k, v, L: int, B: int, *, o=None, lse=None, return_ls
     return (o, lse) if lse is not None else o
 
 
+def mars_attn_two_stream_bwd(q, k, v, o, d_o, lse, L: int, B: int, *, dq=None, dk=None,
+                             dv=None, workspace=None, softmax_scale: float = 0.0,
+                             mask_mode: int = 0, stream=None):
+    """Backward of mars_attn_two_stream (bf16): returns (dq, dk, dv). o and lse are the
+    forward's outputs for the same inputs; d_o is dLoss/dO [b, 2L, Hq, d]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _need(t, n, torch.bfloat16, 4)
+    b, n2, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if (n2 != 2 * L or k.shape != (b, n2, Hkv, d) or v.shape != k.shape or o.shape != q.shape
+            or d_o.shape != q.shape):
+        raise ValueError("shapes must be q/o/d_o [b,2L,Hq,d], k/v [b,2L,Hkv,d]")
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (b, Hq, n2):
+        raise ValueError("lse must be [b, Hq, 2L]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, torch.bfloat16, 4)
+    need = int(_lib.lib().mars_attn_two_stream_bwd_workspace_bytes(b, L, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    code = _lib.lib().mars_attn_two_stream_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        b, L, B, Hq, Hkv, d, _DT[torch.bfloat16], float(softmax_scale), int(mask_mode),
+        _ptr(workspace), workspace.numel(), _stream(stream))
+    check("mars_attn_two_stream_bwd", code)
+    return dq, dk, dv
+
+
 def mars_decode_workspace_bytes(S, B, n_q_heads, n_kv_heads, head_dim, page_size, max_pages):
     return int(_lib.lib().mars_decode_workspace_bytes(S, B, n_q_heads, n_kv_heads, head_dim,
                                                       page_size, max_pages))

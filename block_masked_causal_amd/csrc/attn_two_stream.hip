@@ -12,7 +12,7 @@
 // skip the per-element test.
 #include <type_traits>
 
-#include "mars_common.hpp"
+#include "attn_common.hpp"
 
 using namespace mars;
 
@@ -31,21 +31,6 @@ struct TwoStreamArgs {
   int gh, nhc, rt, nw;  // bf16 path: heads per workgroup, head chunks per group,
                         // 32-row tiles per workgroup, waves per workgroup
 };
-
-// Visible keys of row a: c < hi1, or lo2 <= c < hi2.
-__device__ __forceinline__ void row_intervals(int a, int L, int B, int mode, int& hi1, int& lo2,
-                                              int& hi2) {
-  if (mode == 1 || a < L) {
-    hi1 = a + 1;
-    lo2 = 0;
-    hi2 = 0;
-    return;
-  }
-  const int bb = ((a - L) / B) * B;
-  hi1 = bb;
-  lo2 = L + bb;
-  hi2 = a + 1;
-}
 
 __device__ __forceinline__ bool in_rows(int c, int hi1, int lo2, int hi2) {
   return (c < hi1) | ((c >= lo2) & (c < hi2));
@@ -136,56 +121,10 @@ struct Cfg {
   static constexpr int BMAX = (NBLK + 3) / 4;  // blocks per wave, at >= 4 waves
 };
 
-// K and V tiles sit in LDS unpadded (a direct global->LDS load writes 1 KiB
-// contiguously per wave), with the 16-byte chunks of each row permuted by an
-// XOR of the row so that the reads below hit all 64 banks:
-//  * K rows are read 16 at a time at one chunk (ds_read_b128);
-//  * V is read through ds_read_b64_tr_b16, 4 rows x 4 chunks per 32 lanes.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return D == 64 ? (r >> 1) & 7 : r & 15;
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
-}
-
 // Rescaling of the running output is deferred until a row maximum grows by
 // more than 2^8: until then exp2(s - m) stays below 256, which neither fp32
 // nor bf16 minds, and the final O / l is unchanged by which m was used.
 constexpr float kLazyRescale = 8.0f;
-
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
-
-// How a tile's keys are tested against a lane's visible intervals (both given
-// relative to the lane's first key kb = c0 + 4 hf). The first interval always
-// starts at or before the tile, so only its upper end matters.
-enum : int {
-  kMaskNone = 0,   // every key visible to every row of the wave
-  kMaskUpper = 1,  // key < hi_a
-  kMaskRange = 2,  // lo_b <= key < lo_b + wb
-  kMaskBoth = 3,   // either
-};
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// 4 keys x 1 column of a row-major LDS tile (see the lane mapping above)
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
-}
-
-// max / sum of a value over the two halves of the wave (lanes l and l ^ 32)
-__device__ __forceinline__ float halves_max(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                   false);
-  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                   false);
-  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-}
 
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
 // O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
@@ -308,28 +247,6 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
   // ---- half 1 P V
   pv(2, p2);
   pv(3, p3);
-}
-
-// Key ranges a block of query rows [a0, a_last] needs: r1 = [0, r1_hi) and
-// r2 = [r2_lo, r2_hi); keys below full_below are visible to every row.
-__device__ __forceinline__ void rows_key_ranges(int a0, int a_last, int L, int B, int mode,
-                                                int& r1_hi, int& r2_lo, int& r2_hi,
-                                                int& full_below) {
-  r2_lo = 0;
-  r2_hi = 0;
-  if (mode == 1 || a_last < L) {
-    r1_hi = a_last + 1;
-    full_below = a0 + 1;          // causal: fully visible iff every key <= a0
-  } else if (a0 >= L) {
-    const int t0 = a0 - L, t1 = a_last - L;
-    r1_hi = (t1 / B) * B;         // clean keys of strictly earlier blocks
-    full_below = (t0 / B) * B;
-    r2_lo = L + full_below;       // mask keys of the blocks these rows sit in
-    r2_hi = a_last + 1;
-  } else {
-    r1_hi = a_last + 1;           // rows straddle the stream boundary: test every key
-    full_below = 0;
-  }
 }
 
 // Workgroup = nw waves, each owning one (query head, 32-row tile). The heads
@@ -531,13 +448,6 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     }
   }
   if (p.lse && hf == 0) p.lse[((size_t)b * p.Hq + h) * p.twoL + a] = (m + log2f(lt)) * kLn2;
-}
-
-// Heads per workgroup: the largest divisor of the GQA group size that is <= 8.
-inline int heads_per_wg(int group) {
-  for (int d = 8; d > 1; --d)
-    if (group % d == 0) return d;
-  return 1;
 }
 
 template <int D>

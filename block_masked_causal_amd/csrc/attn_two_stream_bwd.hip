@@ -1,0 +1,694 @@
+// Two-stream MARS attention backward (dQ, dK, dV) for gfx950.
+//
+// The pages train the unchanged model on L_mask + L_AR through the two-stream
+// attention (papernotes.org notes on "MARS: Enabling Autoregressive Models
+// Multi-Token Generation", key design 2 / 关键设计 2; gist.science explainer,
+// section 2B), so the training step needs the gradient of that attention.
+// With S = scale Q K^T under the mask M (key design 1, equation M_ij),
+// P = softmax_row(S), O = P V and the forward's log-sum-exp per row:
+//     P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,
+//     dS = P * (dP - D),  D = rowsum(dO * O),
+//     dQ = scale dS K,    dK = scale dS^T Q.
+// Three kernels:
+//  * bwd_dsum_kernel: D per (batch, head, row).
+//  * bwd_dq_kernel: the forward's structure (one wave per 32 query rows, the
+//    visible K/V tiles staged in LDS); P is recomputed from lse, dP^T = V dO^T
+//    and dQ^T += K^T dS^T with dS^T fed from registers.
+//  * bwd_dkv_kernel: one wave per 32 keys of a KV head; it walks only the
+//    query blocks that can see its keys (each key's visible rows are at most
+//    two intervals) and every query head of the GQA group, accumulating dK^T
+//    and dV^T in registers, so no atomics are needed.
+#include <type_traits>
+
+#include "attn_common.hpp"
+
+using namespace mars;
+
+namespace {
+
+struct BwdArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* o;
+  const bf16_t* dout;
+  const float* lse;  // [b, Hq, 2L], natural log
+  float* dsum;       // [b, Hq, 2L] workspace: rowsum(dO * O)
+  bf16_t* dq;
+  bf16_t* dk;
+  bf16_t* dv;
+  int batch, L, B, Hq, Hkv, twoL, group, mask_mode;
+  float scale, scale_log2;
+  int nqt, gh, nhc, rt, nw;  // dQ kernel split, as in the forward
+};
+
+// ------------------------------------------------------------------ D -------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs p) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;  // (b, a, h) in [b][2L][Hq] order
+  const size_t rows = (size_t)p.batch * p.twoL * p.Hq;
+  if (row >= rows) return;
+  const bf16_t* dor = p.dout + row * D;
+  const bf16_t* orr = p.o + row * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 x = *(const bf16x8*)(dor + 8 * c);
+    const bf16x8 y = *(const bf16x8*)(orr + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+  }
+  const int h = (int)(row % p.Hq);
+  const size_t ba = row / p.Hq;
+  const int a = (int)(ba % p.twoL);
+  const int b = (int)(ba / p.twoL);
+  p.dsum[((size_t)b * p.Hq + h) * p.twoL + a] = acc;
+}
+
+// ------------------------------------------------------------------ dQ ------
+template <int D>
+struct DqCfg {
+  static constexpr int BN = 64;
+  static constexpr int CPR = D / 8;
+  static constexpr int TSZ = BN * D;
+  static constexpr int NBLK = TSZ / 512;
+  static constexpr int BMAX = (NBLK + 3) / 4;
+};
+
+// One 64-key tile for one wave of 32 query rows: S^T = K Q^T and
+// dP^T = V dO^T (lane (j, hf) holds query row j and 16 keys per 32-key half),
+// P^T = exp2(cs S^T - lse2_j), dS^T = P^T (dP^T - D_j), dQ^T += K^T dS^T with
+// dS^T as the B operand (K slot (hf, e) of a 16-key chunk is key 4 hf + e or
+// 8 + 4 hf + e - 4, the keys the lane holds) and K^T from transposing reads.
+template <int D, int MASK>
+__device__ __forceinline__ void dq_tile(const bf16_t* __restrict__ Ks,
+                                        const bf16_t* __restrict__ Vs,
+                                        const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&dof)[D / 16], f32x16 (&dq)[D / 32],
+                                        float lse2, float dsum, float cs, int hi_a, int lo_b,
+                                        int wb, const int (&kad)[D / 16],
+                                        const int (&ktr)[2][D / 32]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 ka = *(const bf16x8*)(Ks + kad[c] + 32 * n * D);
+      s = mfma32(ka, qf[c], s);
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 va = *(const bf16x8*)(Vs + kad[c] + 32 * n * D);
+      dp = mfma32(va, dof[c], dp);
+    }
+    if constexpr (MASK != kMaskNone) {
+      int ha = hi_a, lb = lo_b, w = wb;
+      asm volatile("" : "+v"(ha), "+v"(lb), "+v"(w) : "v"(s));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * n + 8 * (r >> 2) + (r & 3);
+        bool vis;
+        if constexpr (MASK == kMaskUpper) {
+          vis = off < ha;
+        } else if constexpr (MASK == kMaskRange) {
+          vis = (uint32_t)(off - lb) < (uint32_t)w;
+        } else {
+          vis = (off < ha) | ((uint32_t)(off - lb) < (uint32_t)w);
+        }
+        s[r] = vis ? s[r] : -INFINITY;
+      }
+    }
+    bf16x8 ds[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(fmaf(s[r], cs, -lse2));
+      ds[r >> 3][r & 7] = (bf16_t)(pr * (dp[r] - dsum));
+    }
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int kc = 2 * n + kh;
+        const bf16x4 lo = lds_read_tr(Ks + ktr[0][i] + 16 * kc * D);
+        const bf16x4 hi = lds_read_tr(Ks + ktr[1][i] + 16 * kc * D);
+        const bf16x8 ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dq[i] = mfma32(ka, ds[kh], dq[i]);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16_t stage0[2 * C::TSZ];
+  __shared__ __attribute__((aligned(16))) bf16_t stage1[2 * C::TSZ];
+  const int NT = 64 * p.nw;
+  (void)NT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
+
+  // (batch, KV head, head chunk, query tile), heaviest tiles first
+  const int nkv = p.batch * p.Hkv;
+  const int hc = blockIdx.x % p.nhc;
+  const int kvg = (blockIdx.x / p.nhc) % nkv;
+  const int rank = blockIdx.x / (p.nhc * nkv);
+  const int b = kvg / p.Hkv;
+  const int kvh = kvg % p.Hkv;
+  const int h = kvh * p.group + hc * p.gh + w % p.gh;
+  const int bm = 32 * p.rt;
+  int qt;
+  if (p.mask_mode == 0 && (p.L % bm) == 0) {
+    const int nqs = p.L / bm;
+    qt = (rank & 1) * nqs + (nqs - 1 - (rank >> 1));
+  } else {
+    qt = p.nqt - 1 - rank;
+  }
+  const int a0 = qt * bm;
+  const int a_last = min(a0 + bm, p.twoL) - 1;
+
+  int r1_hi, r2_lo, r2_hi, full_below;
+  rows_key_ranges(a0, a_last, p.L, p.B, p.mask_mode, r1_hi, r2_lo, r2_hi, full_below);
+  const int n1 = (r1_hi + C::BN - 1) / C::BN;
+  const int n2 = r2_hi > r2_lo ? (r2_hi - r2_lo + C::BN - 1) / C::BN : 0;
+  const int ntiles = n1 + n2;
+  const int wa0 = a0 + 32 * (w / p.gh);
+  const bool wave_live = wa0 < p.twoL;
+  const int wa_last = wave_live ? min(wa0 + 31, p.twoL - 1) : wa0;
+  int w1_hi, w2_lo, w2_hi, w_full;
+  rows_key_ranges(wa0, wa_last, p.L, p.B, p.mask_mode, w1_hi, w2_lo, w2_hi, w_full);
+
+  const int a = wa0 + j;
+  int hi1, lo2, hi2;
+  row_intervals(a, p.L, p.B, p.mask_mode, hi1, lo2, hi2);
+  const bool row_ok = a < p.twoL;
+
+  const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
+  const rsrc_t rq = make_rsrc(p.q + (size_t)b * p.twoL * qs + (size_t)h * D,
+                              (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t)));
+  const rsrc_t rdo = make_rsrc(p.dout + (size_t)b * p.twoL * qs + (size_t)h * D,
+                               (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t)));
+  const uint32_t kv_bytes = (uint32_t)(((p.twoL - 1) * rs + D) * sizeof(bf16_t));
+  const rsrc_t rk = make_rsrc(p.k + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
+  const rsrc_t rv = make_rsrc(p.v + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
+
+  bf16x8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const uint32_t off = (uint32_t)((a * qs + 16 * c + 8 * hf) * sizeof(bf16_t));
+    qf[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    dof[c] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+  }
+  const size_t rowoff = ((size_t)b * p.Hq + h) * p.twoL;
+  const float lse2 = row_ok ? p.lse[rowoff + a] * kLog2e : 0.f;
+  const float dsum = row_ok ? p.dsum[rowoff + a] : 0.f;
+
+  auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
+
+  // K and V tiles: direct global -> LDS loads, rows XOR-permuted for row reads
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto issue_tile = [&](int it, bf16_t* st) {
+    const int c0 = tile_c0(it);
+#pragma unroll
+    for (int i = 0; i < C::BMAX; ++i) {
+      const int blk = wu + p.nw * i;
+      if (blk < C::NBLK) {
+        const int u = blk * 64 + lane;
+        const int row = u / C::CPR, slot = u % C::CPR;
+        const uint32_t off = (uint32_t)(((c0 + row) * rs) * sizeof(bf16_t)) +
+                             16 * (slot ^ swz_k<D>(row));
+        lds_load16(rk, st + blk * 512, off);
+        lds_load16(rv, st + C::TSZ + blk * 512, off);
+      }
+    }
+  };
+
+  // row reads (K for S^T, V for dP^T): row j (+ 32 n), chunk 2c + hf
+  int kad[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) kad[c] = j * D + 8 * ((2 * c + hf) ^ swz_k<D>(j));
+  // transposing K reads: 16-lane group g reads keys 4 (g / 2) + lane % 16 / 4
+  // (+ 8 e, + 16 kc) at columns 32 i + 16 (g % 2) + 4 (lane % 4)
+  int ktr[2][D / 32];
+  {
+    const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 4 * hf + ((lane & 15) >> 2) + 8 * e;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        ktr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_k<D>(row)) + 4 * (lane & 1);
+    }
+  }
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq[i] = f32x16{};
+
+  if (ntiles > 0) issue_tile(0, stage0);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]), "v"(dof[c]));
+  __syncthreads();
+
+  auto iteration = [&](int it, auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (it + 1 < ntiles) issue_tile(it + 1, STG == 0 ? stage1 : stage0);
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16_t* Ks = STG == 0 ? stage0 : stage1;
+    const bf16_t* Vs = Ks + C::TSZ;
+    const int c0 = tile_c0(it);
+    const bool in_r1 = it < n1;
+    const int lim_lo = in_r1 ? 0 : r2_lo;
+    const int lim_hi = in_r1 ? r1_hi : r2_hi;
+    const int t_lo = max(c0, lim_lo), t_hi = min(c0 + C::BN, lim_hi);
+    const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
+    if (need) {
+      if (in_r1 && c0 + C::BN - 1 < w_full) {
+        dq_tile<D, kMaskNone>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, 0, 0, 0, kad, ktr);
+      } else {
+        const int kb = c0 + 4 * hf;
+        const int hi_a = min(hi1, lim_hi) - kb;
+        const int lo_b = max(lo2, lim_lo) - kb;
+        const int wb = max(min(hi2, lim_hi) - kb - lo_b, 0);
+        const bool any_a = __builtin_amdgcn_ballot_w64(hi_a > 0) != 0;
+        const bool any_b = __builtin_amdgcn_ballot_w64(wb > 0) != 0;
+        if (!any_b) {
+          dq_tile<D, kMaskUpper>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, hi_a, 0, 0, kad,
+                                 ktr);
+        } else if (!any_a) {
+          dq_tile<D, kMaskRange>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, 0, lo_b, wb,
+                                 kad, ktr);
+        } else {
+          dq_tile<D, kMaskBoth>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, hi_a, lo_b, wb,
+                                kad, ktr);
+        }
+      }
+    }
+    __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    iteration(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) iteration(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!row_ok) return;
+  bf16_t* orow = p.dq + (((size_t)b * p.twoL + a) * p.Hq + h) * D;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk = {pack_bf16x2(dq[i][4 * g] * p.scale, dq[i][4 * g + 1] * p.scale),
+                  pack_bf16x2(dq[i][4 * g + 2] * p.scale, dq[i][4 * g + 3] * p.scale)};
+      *(u32x2*)(orow + 32 * i + 8 * g + 4 * hf) = pk;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV --
+// Workgroup: 4 waves, 128 consecutive keys of one (batch, KV head); wave w
+// owns keys k0 + 32 w + j. K rows sit in registers as B fragments, V rows in
+// LDS. The workgroup walks 32-row query blocks (for each query head of the
+// group) through double-buffered LDS stages holding Q, dO, lse and D.
+template <int D>
+struct DkvCfg {
+  static constexpr int QB = 32;                 // query rows per block
+  static constexpr int CPR = D / 8;
+  static constexpr int QSZ = QB * D;            // Q (or dO) block, elements
+  static constexpr int NBLK = QSZ / 512;        // 1 KiB blocks per Q (or dO) block
+  static constexpr int KB = 128;                // keys per workgroup
+  static constexpr int VSZ = KB * D;
+};
+
+template <int D, int MASK>
+__device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
+                                          const bf16_t* __restrict__ Ds,
+                                          const float* __restrict__ Ls,
+                                          const bf16_t* __restrict__ Vs,
+                                          const bf16x8 (&kf)[D / 16], f32x16 (&dk)[D / 32],
+                                          f32x16 (&dv)[D / 32], float cs, int lo1, int w1,
+                                          int lo2, int w2, const int (&qad)[D / 16],
+                                          const int (&qtr)[2][D / 32], const int (&vad)[D / 16],
+                                          int hf) {
+  // S = Q K^T and dP = dO V^T: lane (j, hf) holds key j and query rows
+  // 8 (r / 4) + 4 hf + r % 4 of the block
+  f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 qa = *(const bf16x8*)(Qs + qad[c]);
+    s = mfma32(qa, kf[c], s);
+  }
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 da = *(const bf16x8*)(Ds + qad[c]);
+    const bf16x8 vb = *(const bf16x8*)(Vs + vad[c]);
+    dp = mfma32(da, vb, dp);
+  }
+  if constexpr (MASK != kMaskNone) {
+    int l1 = lo1, x1 = w1, l2 = lo2, x2 = w2;
+    asm volatile("" : "+v"(l1), "+v"(x1), "+v"(l2), "+v"(x2) : "v"(s));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      bool vis;
+      if constexpr (MASK == kMaskRange) {
+        vis = (uint32_t)(off - l1) < (uint32_t)x1;
+      } else {
+        vis = ((uint32_t)(off - l1) < (uint32_t)x1) | ((uint32_t)(off - l2) < (uint32_t)x2);
+      }
+      s[r] = vis ? s[r] : -INFINITY;
+    }
+  }
+  // lse2 and D of the lane's 16 rows: 4 runs of 4 consecutive rows
+  bf16x8 pp[2], ps[2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 l4 = *(const f32x4*)(Ls + 8 * g + 4 * hf);
+    const f32x4 d4 = *(const f32x4*)(Ls + 32 + 8 * g + 4 * hf);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      const float pr = fast_exp2(fmaf(s[r], cs, -l4[e]));
+      pp[r >> 3][r & 7] = (bf16_t)pr;
+      ps[r >> 3][r & 7] = (bf16_t)(pr * (dp[r] - d4[e]));
+    }
+  }
+  // dV^T += dO^T P and dK^T += Q^T dS: A from transposing reads of the dO / Q
+  // block (rows = query slots of the 16-row chunk kc), B from registers
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x4 dlo = lds_read_tr(Ds + qtr[0][i] + 16 * kc * D);
+      const bf16x4 dhi = lds_read_tr(Ds + qtr[1][i] + 16 * kc * D);
+      const bf16x8 da = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
+      dv[i] = mfma32(da, pp[kc], dv[i]);
+      const bf16x4 qlo = lds_read_tr(Qs + qtr[0][i] + 16 * kc * D);
+      const bf16x4 qhi = lds_read_tr(Qs + qtr[1][i] + 16 * kc * D);
+      const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+      dk[i] = mfma32(qa, ps[kc], dk[i]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
+  using C = DkvCfg<D>;
+  // per stage: Q block, dO block, then lse2[32] and D[32]
+  constexpr int STG_EL = 2 * C::QSZ + 128;  // elements (bf16 units); the floats take 128
+  __shared__ __attribute__((aligned(16))) bf16_t stage0[STG_EL];
+  __shared__ __attribute__((aligned(16))) bf16_t stage1[STG_EL];
+  __shared__ __attribute__((aligned(16))) bf16_t vtile[C::VSZ];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
+
+  const int nkb = (p.twoL + C::KB - 1) / C::KB;
+  const int kbi = blockIdx.x % nkb;  // key blocks in increasing order: clean keys first
+  const int kvg = blockIdx.x / nkb;
+  const int b = kvg / p.Hkv;
+  const int kvh = kvg % p.Hkv;
+  const int k0 = kbi * C::KB;
+  const int kw0 = k0 + 32 * w;
+  const int key = kw0 + j;
+  const bool key_ok = key < p.twoL;
+
+  // the lane's key and the query rows that see it
+  int lo1, hi1, lo2, hi2;
+  key_rows(min(key, p.twoL - 1), p.L, p.B, p.mask_mode, lo1, hi1, lo2, hi2);
+  if (!key_ok) {
+    hi1 = lo1;
+    hi2 = lo2;
+  }
+  // the workgroup's query rows: the union over its keys, as up to two ranges
+  const int klast = min(k0 + C::KB, p.twoL) - 1;
+  int qa1, qb1, qa2 = 0, qb2 = 0;
+  if (p.mask_mode == 1 || (k0 < p.L && klast >= p.L)) {
+    qa1 = k0;
+    qb1 = p.twoL;
+  } else if (klast < p.L) {
+    int x1, x2, y1, y2;
+    key_rows(k0, p.L, p.B, 0, qa1, x1, qa2, x2);
+    key_rows(klast, p.L, p.B, 0, y1, qb1, y2, qb2);
+    qb1 = p.L;
+    qb2 = p.twoL;
+  } else {
+    int x1, x2, y1, y2;
+    key_rows(k0, p.L, p.B, 0, qa1, x1, y1, y2);
+    key_rows(klast, p.L, p.B, 0, x2, qb1, y1, y2);
+  }
+  const int fb1 = qa1 / C::QB, lb1 = qb1 > qa1 ? (qb1 - 1) / C::QB : fb1 - 1;
+  int fb2 = qb2 > qa2 ? qa2 / C::QB : 0, lb2 = qb2 > qa2 ? (qb2 - 1) / C::QB : -1;
+  if (fb2 <= lb1) fb2 = lb1 + 1;  // never the same query block twice
+  const int nb1 = lb1 - fb1 + 1;
+  const int nb2 = lb2 >= fb2 ? lb2 - fb2 + 1 : 0;
+  const int nblocks = nb1 + nb2;
+  const int g = p.group;
+  const int niter = nblocks * g;
+
+  const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
+  const uint32_t q_bytes = (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t));
+  const bf16_t* qbase = p.q + (size_t)b * p.twoL * qs;
+  const bf16_t* dobase = p.dout + (size_t)b * p.twoL * qs;
+  const uint32_t kv_bytes = (uint32_t)(((p.twoL - 1) * rs + D) * sizeof(bf16_t));
+  const rsrc_t rk = make_rsrc(p.k + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
+  const rsrc_t rv = make_rsrc(p.v + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
+
+  // K rows of the lane's key as B fragments; V rows of the workgroup's keys into LDS
+  bf16x8 kf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    kf[c] = __builtin_bit_cast(
+        bf16x8, buf_load16(rk, (uint32_t)((key * rs + 16 * c + 8 * hf) * sizeof(bf16_t))));
+  {
+    constexpr int VB = C::VSZ / 512;  // 1 KiB blocks of the V tile
+#pragma unroll
+    for (int i = 0; i < (VB + 3) / 4; ++i) {
+      const int blk = w + 4 * i;
+      if (blk < VB) {
+        const int u = blk * 64 + lane;
+        const int row = u / C::CPR, slot = u % C::CPR;
+        lds_load16(rv, vtile + blk * 512,
+                   (uint32_t)(((k0 + row) * rs) * sizeof(bf16_t)) + 16 * (slot ^ swz_k<D>(row)));
+      }
+    }
+  }
+
+  // iteration it: query block it / g of the two ranges, query head kvh*g + it % g
+  auto block_q0 = [&](int it) {
+    const int bi = it / g;
+    return (bi < nb1 ? fb1 + bi : fb2 + (bi - nb1)) * C::QB;
+  };
+  const size_t lrow = (size_t)b * p.Hq;
+  auto issue_block = [&](int it, bf16_t* st) {
+    const int q0 = block_q0(it);
+    const int h = kvh * g + it % g;
+    const rsrc_t rq = make_rsrc(qbase + (size_t)h * D, q_bytes);
+    const rsrc_t rdo = make_rsrc(dobase + (size_t)h * D, q_bytes);
+#pragma unroll
+    for (int i = 0; i < (C::NBLK + 3) / 4; ++i) {
+      const int blk = w + 4 * i;
+      if (blk < C::NBLK) {
+        const int u = blk * 64 + lane;
+        const int row = u / C::CPR, slot = u % C::CPR;
+        const uint32_t off = (uint32_t)(((q0 + row) * qs) * sizeof(bf16_t)) +
+                             16 * (slot ^ swz_k<D>(row));
+        lds_load16(rq, st + blk * 512, off);
+        lds_load16(rdo, st + C::QSZ + blk * 512, off);
+      }
+    }
+  };
+  // lse2 and D of a block: loaded into registers by wave 0, stored after compute
+  float lval = 0.f, dval = 0.f;
+  auto load_ld = [&](int it) {
+    if (w == 0 && lane < C::QB) {
+      const int q0 = block_q0(it);
+      const int h = kvh * g + it % g;
+      const int a = q0 + lane;
+      const size_t ro = (lrow + h) * p.twoL;
+      lval = a < p.twoL ? p.lse[ro + a] * kLog2e : 0.f;
+      dval = a < p.twoL ? p.dsum[ro + a] : 0.f;
+    }
+  };
+  auto store_ld = [&](bf16_t* st) {
+    if (w == 0 && lane < C::QB) {
+      float* L2 = (float*)(st + 2 * C::QSZ);
+      L2[lane] = lval;
+      L2[32 + lane] = dval;
+    }
+  };
+
+  // read offsets. Row reads of the Q / dO block: row i = lane % 32, chunk 2c + hf.
+  // V row reads: key row 32 w + j. Transposing reads of Q / dO: 16-lane group
+  // g reads rows 4 (g / 2) + lane % 16 / 4 (+ 8 e, + 16 kc) at columns
+  // 32 i + 16 (g % 2) + 4 (lane % 4).
+  int qad[D / 16], vad[D / 16], qtr[2][D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    qad[c] = j * D + 8 * ((2 * c + hf) ^ swz_k<D>(j));
+    vad[c] = (32 * w + j) * D + 8 * ((2 * c + hf) ^ swz_k<D>(32 * w + j));
+  }
+  {
+    const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 4 * hf + ((lane & 15) >> 2) + 8 * e;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        qtr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_k<D>(row)) + 4 * (lane & 1);
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+
+  if (niter > 0) {
+    issue_block(0, stage0);
+    load_ld(0);
+    store_ld(stage0);
+  }
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(kf[c]));
+  __syncthreads();
+
+  auto iteration = [&](int it, auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
+    bf16_t* nxt = STG == 0 ? stage1 : stage0;
+    if (it + 1 < niter) {
+      issue_block(it + 1, nxt);
+      load_ld(it + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16_t* Qs = STG == 0 ? stage0 : stage1;
+    const bf16_t* Ds = Qs + C::QSZ;
+    const float* Ls = (const float*)(Qs + 2 * C::QSZ);
+    const int q0 = block_q0(it);
+    // the lane's visible rows relative to its first row q0 + 4 hf
+    const int rb = q0 + 4 * hf;
+    const int l1 = max(lo1, q0) - rb, x1 = max(min(hi1, q0 + C::QB) - max(lo1, q0), 0);
+    const int l2 = max(lo2, q0) - rb, x2 = max(min(hi2, q0 + C::QB) - max(lo2, q0), 0);
+    const bool any = __builtin_amdgcn_ballot_w64((x1 > 0) | (x2 > 0)) != 0;
+    if (any) {
+      // every row of the block visible to every key of the wave?
+      const bool all1 = (lo1 <= q0) & (hi1 >= q0 + C::QB);
+      const bool all2 = (lo2 <= q0) & (hi2 >= q0 + C::QB);
+      const bool full = __builtin_amdgcn_ballot_w64(!(all1 | all2)) == 0;
+      const bool two = __builtin_amdgcn_ballot_w64((x1 > 0) & (x2 > 0)) != 0;
+      if (full) {
+        dkv_block<D, kMaskNone>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, 0, 0, 0, 0, qad,
+                                qtr, vad, hf);
+      } else if (!two) {
+        const bool in1 = x1 > 0;
+        dkv_block<D, kMaskRange>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, in1 ? l1 : l2,
+                                 in1 ? x1 : x2, 0, 0, qad, qtr, vad, hf);
+      } else {
+        dkv_block<D, kMaskBoth>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, l1, x1, l2, x2,
+                                qad, qtr, vad, hf);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < niter) store_ld(nxt);
+    __syncthreads();
+  };
+  for (int it = 0; it < niter; it += 2) {
+    iteration(it, std::integral_constant<int, 0>{});
+    if (it + 1 < niter) iteration(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!key_ok) return;
+  // lane (j, hf) holds dK^T / dV^T rows d = 32 i + 8 (r / 4) + 4 hf + r % 4 of its key
+  bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
+  bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const u32x2 pk = {pack_bf16x2(dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale),
+                        pack_bf16x2(dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale)};
+      *(u32x2*)(dkr + 32 * i + 8 * gg + 4 * hf) = pk;
+      const u32x2 pv = {pack_bf16x2(dv[i][4 * gg], dv[i][4 * gg + 1]),
+                        pack_bf16x2(dv[i][4 * gg + 2], dv[i][4 * gg + 3])};
+      *(u32x2*)(dvr + 32 * i + 8 * gg + 4 * hf) = pv;
+    }
+  }
+}
+
+template <int D>
+int launch_bwd(BwdArgs a, hipStream_t st) {
+  const size_t rows = (size_t)a.batch * a.twoL * a.Hq;
+  hipLaunchKernelGGL(bwd_dsum_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                     a);
+  a.gh = D == 64 ? 1 : heads_per_wg(a.group);
+  a.nhc = a.group / a.gh;
+  a.rt = D == 64 ? 4 : 8 / a.gh;
+  a.nw = a.gh * a.rt;
+  a.nqt = (a.twoL + 32 * a.rt - 1) / (32 * a.rt);
+  const double nq = (double)a.batch * a.Hkv * a.nhc * a.nqt;
+  const int nkb = (a.twoL + DkvCfg<D>::KB - 1) / DkvCfg<D>::KB;
+  const double nk = (double)a.batch * a.Hkv * nkb;
+  if (nq >= 2147483647.0 || nk >= 2147483647.0) return MARS_ERR_SHAPE;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(64 * a.nw), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)nk), dim3(256), 0, st, a);
+  return mars_launch_status();
+}
+
+}  // namespace
+
+extern "C" size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L,
+                                                           int32_t n_q_heads) {
+  if (batch < 1 || L < 1 || n_q_heads < 1) return 0;
+  return (size_t)batch * n_q_heads * 2 * (size_t)L * sizeof(float);
+}
+
+extern "C" int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v,
+                                        const void* o, const void* d_o, const float* lse,
+                                        void* dq, void* dk, void* dv, int32_t batch, int32_t L,
+                                        int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, int32_t dtype, float softmax_scale,
+                                        int32_t mask_mode, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  MARS_REQUIRE(q && k && v && o && d_o && lse && dq && dk && dv, MARS_ERR_NULL);
+  MARS_REQUIRE(dtype == MARS_BF16, MARS_ERR_DTYPE);
+  MARS_REQUIRE(head_dim == 64 || head_dim == 128, MARS_ERR_UNSUPPORTED);
+  MARS_REQUIRE(batch >= 1 && L >= 1 && B >= 1 && B <= L && L <= (1 << 29), MARS_ERR_SHAPE);
+  MARS_REQUIRE(n_q_heads >= 1 && n_kv_heads >= 1 && n_q_heads % n_kv_heads == 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(mask_mode == 0 || mask_mode == 1, MARS_ERR_SHAPE);
+  MARS_REQUIRE(mars_aligned16(q) && mars_aligned16(k) && mars_aligned16(v) && mars_aligned16(o) &&
+                   mars_aligned16(d_o) && mars_aligned16(lse) && mars_aligned16(dq) &&
+                   mars_aligned16(dk) && mars_aligned16(dv) && mars_aligned16(workspace),
+               MARS_ERR_ALIGN);
+  const int twoL = 2 * L;
+  MARS_REQUIRE(((double)twoL + 64) * n_q_heads * head_dim * 4 < 2147483647.0, MARS_ERR_SHAPE);
+  const size_t need = mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads);
+  MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
+
+  BwdArgs a;
+  a.q = (const bf16_t*)q;
+  a.k = (const bf16_t*)k;
+  a.v = (const bf16_t*)v;
+  a.o = (const bf16_t*)o;
+  a.dout = (const bf16_t*)d_o;
+  a.lse = lse;
+  a.dsum = (float*)workspace;
+  a.dq = (bf16_t*)dq;
+  a.dk = (bf16_t*)dk;
+  a.dv = (bf16_t*)dv;
+  a.batch = batch;
+  a.L = L;
+  a.B = B;
+  a.Hq = n_q_heads;
+  a.Hkv = n_kv_heads;
+  a.twoL = twoL;
+  a.group = n_q_heads / n_kv_heads;
+  a.mask_mode = mask_mode;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+  a.scale_log2 = a.scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  return head_dim == 64 ? launch_bwd<64>(a, st) : launch_bwd<128>(a, st);
+}

@@ -97,6 +97,37 @@ int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o, f
                          float softmax_scale, int32_t mask_mode, void* stream);
 
 /*
+ * Two-stream MARS attention backward: dq, dk, dv of mars_attn_two_stream.
+ *
+ * Defines: the pages train the unchanged model on L_mask + L_AR through the
+ * two-stream attention (papernotes.org notes, key design 2 (关键设计 2);
+ * gist.science explainer, section 2B), so a training step needs the gradient
+ * of that attention. With S = scale Q K^T under the mask of key design 1,
+ * P = softmax(S), O = P V: dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)),
+ * dQ = scale dS K, dK = scale dS^T Q; a KV head sums over its query heads.
+ *
+ * q, d_o, o, dq [batch, 2L, n_q_heads, head_dim]; k, v, dk, dv
+ * [batch, 2L, n_kv_heads, head_dim]; all bf16 (dtype MARS_BF16), head_dim 64
+ * or 128. o and lse [batch, n_q_heads, 2L] (float32, natural log) are the
+ * forward's outputs for the same q, k, v, B, scale and mask_mode. dq, dk, dv
+ * are written (every element); the inputs are not modified.
+ * workspace >= mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads)
+ * bytes of device memory (per-row rowsum(dO * O)).
+ * Errors: as mars_attn_two_stream; MARS_ERR_DTYPE for fp32; MARS_ERR_UNSUPPORTED
+ * for other head sizes; MARS_ERR_WORKSPACE if the workspace is missing or
+ * small. Deterministic: no atomics.
+ */
+int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const void* d_o, const float* lse, void* dq, void* dk, void* dv,
+                             int32_t batch, int32_t L, int32_t B, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                             float softmax_scale, int32_t mask_mode, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mars_attn_two_stream_bwd needs (0 on bad sizes). */
+size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L, int32_t n_q_heads);
+
+/*
  * Block-decode attention (inference form).
  *
  * Defines: each sequence appends B [MASK] queries; a single forward scores all

@@ -67,6 +67,26 @@ def dec(S=2, B=4, Hq=4, Hkv=2, d=128, page=16, max_pages=4, num_pages=8, dtype=1
                                              ws, ws_bytes, None, None)
 
 
+def bwd(dtype=1, d=64, ws=FAKE, ws_bytes=1 << 20, q=FAKE, B=4, L=16, mode=0):
+    return mars.lib().mars_attn_two_stream_bwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                               1, L, B, 4, 2, d, dtype, 0.0, mode, ws, ws_bytes,
+                                               None)
+
+
+def test_two_stream_bwd_argument_checks():
+    # every case is rejected before any launch: the fake addresses are never used
+    assert bwd(q=None) == _lib.MARS_ERR_NULL
+    assert bwd(dtype=0) == _lib.MARS_ERR_DTYPE            # fp32 has no backward
+    assert bwd(d=32) == _lib.MARS_ERR_UNSUPPORTED
+    assert bwd(B=17) == _lib.MARS_ERR_SHAPE               # B > L
+    assert bwd(mode=2) == _lib.MARS_ERR_SHAPE
+    assert bwd(q=MIS) == _lib.MARS_ERR_ALIGN
+    need = mars.lib().mars_attn_two_stream_bwd_workspace_bytes(1, 16, 4)
+    assert need == 1 * 4 * 32 * 4
+    assert bwd(ws_bytes=need - 1) == _lib.MARS_ERR_WORKSPACE
+    assert bwd(ws=None) == _lib.MARS_ERR_WORKSPACE
+
+
 def test_decode_argument_checks():
     assert dec(q=None) == _lib.MARS_ERR_NULL
     assert dec(dtype=5) == _lib.MARS_ERR_DTYPE
