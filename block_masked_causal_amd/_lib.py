@@ -38,7 +38,7 @@ SIGNATURES = {
     "mars_attn_two_stream_bwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz,
                                                 _p]),
-    "mars_attn_two_stream_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "mars_attn_two_stream_bwd_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "mars_attn_block_decode": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _f, _p, _sz,
                                               _p, _p]),

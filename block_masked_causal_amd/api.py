@@ -86,7 +86,7 @@ def mars_attn_two_stream_bwd(q, k, v, o, d_o, lse, L: int, B: int, *, dq=None, d
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, n, torch.bfloat16, 4)
-    need = int(_lib.lib().mars_attn_two_stream_bwd_workspace_bytes(b, L, Hq))
+    need = int(_lib.lib().mars_attn_two_stream_bwd_workspace_bytes(b, L, Hq, Hkv, d))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     code = _lib.lib().mars_attn_two_stream_bwd(

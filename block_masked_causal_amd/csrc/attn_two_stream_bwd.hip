@@ -14,10 +14,12 @@
 //  * bwd_dq_kernel: the forward's structure (one wave per 32 query rows, the
 //    visible K/V tiles staged in LDS); P is recomputed from lse, dP^T = V dO^T
 //    and dQ^T += K^T dS^T with dS^T fed from registers.
-//  * bwd_dkv_kernel: one wave per 32 keys of a KV head; it walks only the
-//    query blocks that can see its keys (each key's visible rows are at most
-//    two intervals) and every query head of the GQA group, accumulating dK^T
-//    and dV^T in registers, so no atomics are needed.
+//  * bwd_dkv_kernel: one wave per 32 keys and one query head; it walks only
+//    the query blocks that can see its keys (each key's visible rows are at
+//    most two intervals), accumulating dK^T and dV^T in registers. With a GQA
+//    group of one head it writes dK, dV directly; otherwise it writes fp32
+//    partials per query head and bwd_dkv_reduce_kernel sums the group's heads
+//    in a fixed order (no atomics: the result is deterministic).
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -34,6 +36,8 @@ struct BwdArgs {
   const bf16_t* dout;
   const float* lse;  // [b, Hq, 2L], natural log
   float* dsum;       // [b, Hq, 2L] workspace: rowsum(dO * O)
+  float* dkp;        // [b, 2L, Hq, d] workspace: per-query-head dK (group > 1)
+  float* dvp;        // [b, 2L, Hq, d] workspace: per-query-head dV (group > 1)
   bf16_t* dq;
   bf16_t* dk;
   bf16_t* dv;
@@ -307,10 +311,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ dK, dV --
-// Workgroup: 4 waves, 128 consecutive keys of one (batch, KV head); wave w
+// Workgroup: 4 waves, 128 consecutive keys of one (batch, query head); wave w
 // owns keys k0 + 32 w + j. K rows sit in registers as B fragments, V rows in
-// LDS. The workgroup walks 32-row query blocks (for each query head of the
-// group) through double-buffered LDS stages holding Q, dO, lse and D.
+// LDS. The workgroup walks 32-row query blocks through double-buffered LDS
+// stages holding Q, dO, lse and D.
 template <int D>
 struct DkvCfg {
   static constexpr int QB = 32;                 // query rows per block
@@ -405,11 +409,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
 
-  const int nkb = (p.twoL + C::KB - 1) / C::KB;
-  const int kbi = blockIdx.x % nkb;  // key blocks in increasing order: clean keys first
-  const int kvg = blockIdx.x / nkb;
-  const int b = kvg / p.Hkv;
-  const int kvh = kvg % p.Hkv;
+  // key blocks in increasing order (the clean keys near the start see the
+  // most rows), the (batch, query head) pairs of one key block side by side
+  const int nbh = p.batch * p.Hq;
+  const int kbi = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / p.Hq;
+  const int hq = bh % p.Hq;
+  const int kvh = hq / p.group;
   const int k0 = kbi * C::KB;
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + j;
@@ -445,8 +452,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
   const int nb1 = lb1 - fb1 + 1;
   const int nb2 = lb2 >= fb2 ? lb2 - fb2 + 1 : 0;
   const int nblocks = nb1 + nb2;
-  const int g = p.group;
-  const int niter = nblocks * g;
+  const int niter = nblocks;
 
   const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
   const uint32_t q_bytes = (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t));
@@ -476,17 +482,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
     }
   }
 
-  // iteration it: query block it / g of the two ranges, query head kvh*g + it % g
-  auto block_q0 = [&](int it) {
-    const int bi = it / g;
-    return (bi < nb1 ? fb1 + bi : fb2 + (bi - nb1)) * C::QB;
-  };
-  const size_t lrow = (size_t)b * p.Hq;
+  // iteration it: query block it of the two ranges
+  auto block_q0 = [&](int it) { return (it < nb1 ? fb1 + it : fb2 + (it - nb1)) * C::QB; };
+  const size_t lrow = ((size_t)b * p.Hq + hq) * p.twoL;
+  const rsrc_t rq = make_rsrc(qbase + (size_t)hq * D, q_bytes);
+  const rsrc_t rdo = make_rsrc(dobase + (size_t)hq * D, q_bytes);
   auto issue_block = [&](int it, bf16_t* st) {
     const int q0 = block_q0(it);
-    const int h = kvh * g + it % g;
-    const rsrc_t rq = make_rsrc(qbase + (size_t)h * D, q_bytes);
-    const rsrc_t rdo = make_rsrc(dobase + (size_t)h * D, q_bytes);
 #pragma unroll
     for (int i = 0; i < (C::NBLK + 3) / 4; ++i) {
       const int blk = w + 4 * i;
@@ -504,12 +506,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
   float lval = 0.f, dval = 0.f;
   auto load_ld = [&](int it) {
     if (w == 0 && lane < C::QB) {
-      const int q0 = block_q0(it);
-      const int h = kvh * g + it % g;
-      const int a = q0 + lane;
-      const size_t ro = (lrow + h) * p.twoL;
-      lval = a < p.twoL ? p.lse[ro + a] * kLog2e : 0.f;
-      dval = a < p.twoL ? p.dsum[ro + a] : 0.f;
+      const int a = block_q0(it) + lane;
+      lval = a < p.twoL ? p.lse[lrow + a] * kLog2e : 0.f;
+      dval = a < p.twoL ? p.dsum[lrow + a] : 0.f;
     }
   };
   auto store_ld = [&](bf16_t* st) {
@@ -603,6 +602,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
 
   if (!key_ok) return;
   // lane (j, hf) holds dK^T / dV^T rows d = 32 i + 8 (r / 4) + 4 hf + r % 4 of its key
+  if (p.group > 1) {
+    float* dkr = p.dkp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
+    float* dvr = p.dvp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        *(f32x4*)(dkr + 32 * i + 8 * gg + 4 * hf) =
+            f32x4{dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale,
+                  dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale};
+        *(f32x4*)(dvr + 32 * i + 8 * gg + 4 * hf) =
+            f32x4{dv[i][4 * gg], dv[i][4 * gg + 1], dv[i][4 * gg + 2], dv[i][4 * gg + 3]};
+      }
+    return;
+  }
   bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
   bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
 #pragma unroll
@@ -619,6 +633,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
   }
 }
 
+// dK, dV of a KV head = the sum of its query heads' partials, in head order.
+// One thread per (batch, key, KV head, 8 consecutive columns).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t total = (size_t)p.batch * p.twoL * p.Hkv * (D / 8);
+  if (t >= total) return;
+  const int c8 = (int)(t % (D / 8));
+  const size_t bkh = t / (D / 8);  // (b, key, kvh) in [b][2L][Hkv] order
+  const int kvh = (int)(bkh % p.Hkv);
+  const size_t bk = bkh / p.Hkv;
+  const float* kp = p.dkp + (bk * p.Hq + (size_t)kvh * p.group) * D + 8 * c8;
+  const float* vp = p.dvp + (bk * p.Hq + (size_t)kvh * p.group) * D + 8 * c8;
+  float sk[8], sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+  for (int h = 0; h < p.group; ++h) {
+    const f32x4 k0 = *(const f32x4*)(kp + (size_t)h * D), k1 = *(const f32x4*)(kp + (size_t)h * D + 4);
+    const f32x4 v0 = *(const f32x4*)(vp + (size_t)h * D), v1 = *(const f32x4*)(vp + (size_t)h * D + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk[e] += k0[e];
+      sk[4 + e] += k1[e];
+      sv[e] += v0[e];
+      sv[4 + e] += v1[e];
+    }
+  }
+  const size_t o = bkh * D + 8 * c8;
+  *(u32x4*)(p.dk + o) = u32x4{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3]),
+                              pack_bf16x2(sk[4], sk[5]), pack_bf16x2(sk[6], sk[7])};
+  *(u32x4*)(p.dv + o) = u32x4{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
+                              pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])};
+}
+
 template <int D>
 int launch_bwd(BwdArgs a, hipStream_t st) {
   const size_t rows = (size_t)a.batch * a.twoL * a.Hq;
@@ -631,19 +679,36 @@ int launch_bwd(BwdArgs a, hipStream_t st) {
   a.nqt = (a.twoL + 32 * a.rt - 1) / (32 * a.rt);
   const double nq = (double)a.batch * a.Hkv * a.nhc * a.nqt;
   const int nkb = (a.twoL + DkvCfg<D>::KB - 1) / DkvCfg<D>::KB;
-  const double nk = (double)a.batch * a.Hkv * nkb;
+  const double nk = (double)a.batch * a.Hq * nkb;
   if (nq >= 2147483647.0 || nk >= 2147483647.0) return MARS_ERR_SHAPE;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(64 * a.nw), 0, st, a);
   hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)nk), dim3(256), 0, st, a);
+  if (a.group > 1) {
+    const size_t tot = (size_t)a.batch * a.twoL * a.Hkv * (D / 8);
+    hipLaunchKernelGGL(bwd_dkv_reduce_kernel<D>, dim3((unsigned)((tot + 255) / 256)), dim3(256),
+                       0, st, a);
+  }
   return mars_launch_status();
 }
 
 }  // namespace
 
+// Layout: dsum [b, Hq, 2L] fp32, then (when Hq > Hkv) the per-query-head dK
+// and dV partials [b, 2L, Hq, d] fp32 each, every part 256-byte aligned.
+namespace {
+size_t bwd_ws_part(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+}  // namespace
+
 extern "C" size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L,
-                                                           int32_t n_q_heads) {
-  if (batch < 1 || L < 1 || n_q_heads < 1) return 0;
-  return (size_t)batch * n_q_heads * 2 * (size_t)L * sizeof(float);
+                                                           int32_t n_q_heads, int32_t n_kv_heads,
+                                                           int32_t head_dim) {
+  if (batch < 1 || L < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 ||
+      n_q_heads % n_kv_heads)
+    return 0;
+  const size_t rows = (size_t)batch * 2 * (size_t)L * n_q_heads;
+  size_t n = bwd_ws_part(rows * sizeof(float));
+  if (n_q_heads > n_kv_heads) n += 2 * bwd_ws_part(rows * head_dim * sizeof(float));
+  return n;
 }
 
 extern "C" int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v,
@@ -665,7 +730,8 @@ extern "C" int mars_attn_two_stream_bwd(const void* q, const void* k, const void
                MARS_ERR_ALIGN);
   const int twoL = 2 * L;
   MARS_REQUIRE(((double)twoL + 64) * n_q_heads * head_dim * 4 < 2147483647.0, MARS_ERR_SHAPE);
-  const size_t need = mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads);
+  const size_t need =
+      mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads, n_kv_heads, head_dim);
   MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
 
   BwdArgs a;
@@ -675,7 +741,10 @@ extern "C" int mars_attn_two_stream_bwd(const void* q, const void* k, const void
   a.o = (const bf16_t*)o;
   a.dout = (const bf16_t*)d_o;
   a.lse = lse;
+  const size_t rows = (size_t)batch * twoL * n_q_heads;
   a.dsum = (float*)workspace;
+  a.dkp = (float*)((char*)workspace + bwd_ws_part(rows * sizeof(float)));
+  a.dvp = (float*)((char*)a.dkp + bwd_ws_part(rows * head_dim * sizeof(float)));
   a.dq = (bf16_t*)dq;
   a.dk = (bf16_t*)dk;
   a.dv = (bf16_t*)dv;

@@ -111,8 +111,8 @@ int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o, f
  * or 128. o and lse [batch, n_q_heads, 2L] (float32, natural log) are the
  * forward's outputs for the same q, k, v, B, scale and mask_mode. dq, dk, dv
  * are written (every element); the inputs are not modified.
- * workspace >= mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads)
- * bytes of device memory (per-row rowsum(dO * O)).
+ * workspace >= mars_attn_two_stream_bwd_workspace_bytes(batch, L, n_q_heads,
+ * n_kv_heads, head_dim) bytes of device memory.
  * Errors: as mars_attn_two_stream; MARS_ERR_DTYPE for fp32; MARS_ERR_UNSUPPORTED
  * for other head sizes; MARS_ERR_WORKSPACE if the workspace is missing or
  * small. Deterministic: no atomics.
@@ -124,8 +124,11 @@ int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v, const 
                              float softmax_scale, int32_t mask_mode, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mars_attn_two_stream_bwd needs (0 on bad sizes). */
-size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L, int32_t n_q_heads);
+/* Workspace bytes mars_attn_two_stream_bwd needs (0 on bad sizes): the rowsum
+ * per (batch, query head, row), plus fp32 dK/dV partials per query head when
+ * n_q_heads > n_kv_heads (they are summed per KV head in head order). */
+size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L, int32_t n_q_heads,
+                                                int32_t n_kv_heads, int32_t head_dim);
 
 /*
  * Block-decode attention (inference form).

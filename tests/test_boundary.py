@@ -81,8 +81,11 @@ def test_two_stream_bwd_argument_checks():
     assert bwd(B=17) == _lib.MARS_ERR_SHAPE               # B > L
     assert bwd(mode=2) == _lib.MARS_ERR_SHAPE
     assert bwd(q=MIS) == _lib.MARS_ERR_ALIGN
-    need = mars.lib().mars_attn_two_stream_bwd_workspace_bytes(1, 16, 4)
-    assert need == 1 * 4 * 32 * 4
+    need = mars.lib().mars_attn_two_stream_bwd_workspace_bytes(1, 16, 4, 2, 64)
+    rows = 1 * 32 * 4
+    assert need == rows * 4 + 2 * rows * 64 * 4               # rowsum, dK and dV partials
+    assert mars.lib().mars_attn_two_stream_bwd_workspace_bytes(1, 16, 2, 2, 64) == 256
+    assert mars.lib().mars_attn_two_stream_bwd_workspace_bytes(1, 16, 3, 2, 64) == 0
     assert bwd(ws_bytes=need - 1) == _lib.MARS_ERR_WORKSPACE
     assert bwd(ws=None) == _lib.MARS_ERR_WORKSPACE
 
