@@ -396,8 +396,10 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
   }
 }
 
+// d = 128 runs one wave per SIMD: the dK^T / dV^T accumulators (128 registers)
+// then live in accumulation registers instead of spilling (2x faster measured).
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p) {
   using C = DkvCfg<D>;
   // per stage: Q block, dO block, then lse2[32] and D[32]
   constexpr int STG_EL = 2 * C::QSZ + 128;  // elements (bf16 units); the floats take 128
