@@ -252,6 +252,10 @@ def main():
         # the two-pass LM head as well (its own traffic line)
         mars.mars_lmhead_confidence(H, W, logits, top_id=top, p_max=pm, workspace=lws,
                                     status=status)
+        # and the two-stream backward at the 0.5B shape
+        lse = torch.empty((TS["batch"], TS["Hq"], 2 * TS["L"]), dtype=torch.float32, device=dev)
+        mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O, lse=lse)
+        mars.mars_attn_two_stream_bwd(Q, K, V, O, Q, lse, TS["L"], TS["B"])
         torch.cuda.synchronize()
         print(json.dumps({"profile_pass": True, "copy_bytes": n * 4,
                           "status_flags": int(status.item())}), flush=True)
@@ -421,9 +425,49 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
     del Q, K, V, O
     torch.cuda.empty_cache()
 
+    # two-stream attention backward (dq, dk, dv) at both training shapes
+    out["two_stream_bwd"] = two_stream_bwd(mars, synth, torch, dev, traffic)
+
     # batched decode loop with a live tau switch
     out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
     return out
+
+
+def two_stream_bwd(mars, synth, torch, dev, traffic):
+    """Backward of the two-stream attention; useful FLOPs = 10 d per visible pair per query
+    head (QK^T recomputed, dO V^T, and the dV, dK, dQ products: 2d each)."""
+    res = {}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for name, c in (("0.5b", TS), ("7b", TS7)):
+        log(f"two-stream backward, {name} shape")
+        q, k, v = synth.two_stream_qkv(1006, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
+        do, _, _ = synth.two_stream_qkv(1007, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
+        Q, K, V, DO = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), to_dev(do, dev)
+        del q, k, v, do
+        o, lse = mars.mars_attn_two_stream(Q, K, V, c["L"], c["B"], return_lse=True)
+        dq, dk, dv = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        ws = torch.empty(mars.lib().mars_attn_two_stream_bwd_workspace_bytes(
+            c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"]), dtype=torch.uint8, device=dev)
+        call = lambda: mars.mars_attn_two_stream_bwd(Q, K, V, o, DO, lse, c["L"], c["B"], dq=dq,
+                                                     dk=dk, dv=dv, workspace=ws)
+        for _ in range(2):
+            call()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(5):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 5
+        fl = 2.5 * useful_two_stream_flops(c["batch"], c["L"], c["B"], c["Hq"], c["d"])
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"shape": c, "ms": round(ms, 4), "useful_tflops": round(tf, 2),
+                     "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                          traffic.get("two_stream_backward") if name == "0.5b"
+                                          else None)}
+        del Q, K, V, DO, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def decode_loop(mars, synth, torch, dev, status):

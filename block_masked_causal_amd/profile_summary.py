@@ -30,7 +30,7 @@ CSRC = os.path.join(HERE, "csrc")
 
 # hot-path call -> (source files that build it, kernel-name substrings of its dispatches)
 CALLS = {
-    "two_stream_attention": (["attn_two_stream.hip", "mars_common.hpp"],
+    "two_stream_attention": (["attn_two_stream.hip", "attn_common.hpp", "mars_common.hpp"],
                              ["two_stream_bf16_kernel"]),
     "block_decode_attention": (["attn_decode.hip", "mars_common.hpp"],
                                ["decode_split_kernel", "decode_merge_kernel"]),
@@ -40,6 +40,9 @@ CALLS = {
                                     [r"lmhead_gemm_kernel<\d+, false>", "conf_partial_kernel",
                                      r"conf_merge_kernel\("]),
     "accept_commit": (["accept_commit.hip", "mars_common.hpp"], ["accept_commit_kernel"]),
+    "two_stream_backward": (["attn_two_stream_bwd.hip", "attn_common.hpp", "mars_common.hpp"],
+                            ["bwd_dsum_kernel", "bwd_dq_kernel", r"bwd_dkv_kernel<",
+                             "bwd_dkv_reduce_kernel"]),
 }
 COPY_KERNEL = "copyBuffer"
 
