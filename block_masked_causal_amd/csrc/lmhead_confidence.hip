@@ -49,25 +49,29 @@ __device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, flo
 // ------------------------------------------------------------------ GEMM ----
 // Workgroup tile: GM rows (all positions, up to 256) x GN vocabulary entries;
 // 8 waves as 4 (rows) x 2 (vocab), each wave 64 x 128 outputs, so each pair
-// of fragments read from LDS feeds eight MFMAs. K advances GK per stage
-// through two LDS buffers (GK = 64 when D allows it, else 32); weight rows
-// are requested kWRing = 2 stages ahead of their use.
+// of fragments read from LDS feeds eight MFMAs and each weight row is read
+// from HBM once. K advances GK = 32 per stage through a ring of GSTAGES = 4
+// LDS stages filled by direct global->LDS loads: three stages are always in
+// flight while one is multiplied (one 64-wide stage in flight, as a register
+// staged pipeline allows, left each workgroup waiting on memory latency).
 constexpr int GM = 256;
 constexpr int GN = 256;
-constexpr int GT = 512;            // threads per workgroup
-constexpr int WNT = GN / 64;       // 32-wide vocab MFMA tiles per wave
-constexpr int kWRing = 2;
+constexpr int GT = 512;                 // threads per workgroup
+constexpr int WNT = GN / 64;            // 32-wide vocab MFMA tiles per wave
+constexpr int GK = 32;                  // K per stage
+constexpr int GSTAGES = 4;
+constexpr int GCPR = GK / 8;            // 16-byte chunks per tile row
+constexpr int GROWS_BLK = 64 / GCPR;    // rows per 1 KiB direct-load block
+constexpr int GABLK = GM / GROWS_BLK;   // blocks per hidden tile
+constexpr int GWBLK = GN / GROWS_BLK;   // blocks per weight tile
+constexpr int GBPW = (GABLK + GWBLK) / (GT / 64);  // blocks per wave per stage
+constexpr int GSTAGE_EL = (GM + GN) * GK;          // elements per stage
+static_assert((GABLK + GWBLK) % (GT / 64) == 0 && GBPW < 8, "stage split");
 
-template <int GK>
-struct GemmCfg {
-  static constexpr int GST = GK + 8;        // LDS row stride (elements): 4 dwords mod 32 banks
-  static constexpr int CPR = GK / 8;        // 16-byte chunks per tile row
-  static constexpr int AL = GM * CPR / GT;  // hidden chunks per thread per stage
-  static constexpr int BL = GN * CPR / GT;  // weight chunks per thread per stage
-  static constexpr size_t LDS = 2 * (size_t)(GM + GN) * GST * sizeof(bf16_t);
-  static_assert(GK % 16 == 0 && (GM * CPR) % GT == 0 && (GN * CPR) % GT == 0, "tile shape");
-  static_assert(LDS <= 160 * 1024, "LDS");
-};
+// Rows sit in LDS unpadded; chunk c of row r is stored at chunk c ^ gswz(r),
+// which keeps 16 consecutive rows read at one chunk on 16 distinct groups of
+// 4 banks (64 banks).
+__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 struct GemmArgs {
   const bf16_t* hidden;
@@ -86,54 +90,37 @@ struct GemmArgs {
 // (two halves of two waves): FUSED reduces them in registers to the
 // confidence partial (max, first argmax, sum exp(l - max)) and writes no
 // logits.
-template <int GK, bool FUSED>
+template <bool FUSED>
 __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
-  using C = GemmCfg<GK>;
-  constexpr int GST = C::GST, CPR = C::CPR, AL = C::AL, BL = C::BL;
-  extern __shared__ __attribute__((aligned(16))) bf16_t gl[];
-  auto As = [&](int buf) { return gl + buf * GM * GST; };
-  auto Bs = [&](int buf) { return gl + 2 * GM * GST + buf * GN * GST; };
+  __shared__ __attribute__((aligned(16))) bf16_t st0[GSTAGE_EL];
+  __shared__ __attribute__((aligned(16))) bf16_t st1[GSTAGE_EL];
+  __shared__ __attribute__((aligned(16))) bf16_t st2[GSTAGE_EL];
+  __shared__ __attribute__((aligned(16))) bf16_t st3[GSTAGE_EL];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
   const int wn = w >> 1, wv = w & 1;
   const int v0 = blockIdx.x * GN;
   const int n0 = blockIdx.y * GM;
   const int nk = p.D / GK;
 
-  u32x4 areg[AL];
-  u32x4 wring[kWRing][BL];
-  auto load_a = [&](int kt) {
+  // buffer views of this tile's rows: rows past N (or V) read as zeros
+  const u32x4 rh = rsrc_words(p.hidden + (size_t)n0 * p.D,
+                              (uint32_t)((size_t)min(GM, p.N - n0) * p.D * sizeof(bf16_t)));
+  const u32x4 rw = rsrc_words(p.w + (size_t)v0 * p.D,
+                              (uint32_t)((size_t)min(GN, p.V - v0) * p.D * sizeof(bf16_t)));
+  // stage kt: wave w fills blocks w, w + 8, ... (hidden tile first, then weights)
+  auto issue = [&](int kt, bf16_t* st) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-      const int idx = tid + GT * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int n = n0 + row;
-      areg[i] = n < p.N ? *(const u32x4*)(p.hidden + (size_t)n * p.D + kt * GK + ch * 8)
-                        : u32x4{};
-    }
-  };
-  auto load_w = [&](int kt, u32x4 (&dst)[BL]) {
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const int idx = tid + GT * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int v = v0 + row;
-      dst[i] = v < p.V ? *(const u32x4*)(p.w + (size_t)v * p.D + kt * GK + ch * 8) : u32x4{};
-    }
-  };
-  auto store = [&](int buf, const u32x4 (&wreg)[BL]) {
-    bf16_t* A = As(buf);
-    bf16_t* Bm = Bs(buf);
-#pragma unroll
-    for (int i = 0; i < AL; ++i) {
-      const int idx = tid + GT * i;
-      *(u32x4*)(A + (idx / CPR) * GST + (idx % CPR) * 8) = areg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const int idx = tid + GT * i;
-      *(u32x4*)(Bm + (idx / CPR) * GST + (idx % CPR) * 8) = wreg[i];
+    for (int i = 0; i < GBPW; ++i) {
+      const int blk = w + (GT / 64) * i;
+      const bool is_a = blk < GABLK;
+      const int rb = (is_a ? blk : blk - GABLK) * GROWS_BLK;
+      const int row = rb + lane / GCPR, slot = lane % GCPR;
+      const uint32_t off = (uint32_t)((size_t)row * p.D * sizeof(bf16_t)) +
+                           (uint32_t)(kt * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row));
+      lds_dma16(is_a ? rh : rw, st + (is_a ? 0 : GM * GK) + rb * GK, off);
     }
   };
 
@@ -143,18 +130,23 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  auto compute = [&](int buf) {
-    const bf16_t* A = As(buf);
-    const bf16_t* Bm = Bs(buf);
+  // fragment offsets: row base + 32 t + j has the swizzle of j; chunk 2 ks + hf
+  const int sw = gswz(j);
+  int koff[GK / 16];
+#pragma unroll
+  for (int ks = 0; ks < GK / 16; ++ks) koff[ks] = 8 * ((2 * ks + hf) ^ sw);
+  auto compute = [&](const bf16_t* st) {
+    const bf16_t* A = st;
+    const bf16_t* Wt = st + GM * GK;
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
       bf16x8 wf[WNT], hfr[2];
 #pragma unroll
       for (int t = 0; t < WNT; ++t)
-        wf[t] = *(const bf16x8*)(Bm + (wv * (GN / 2) + 32 * t + j) * GST + 16 * ks + 8 * hf);
+        wf[t] = *(const bf16x8*)(Wt + (wv * (GN / 2) + 32 * t + j) * GK + koff[ks]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        hfr[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GST + 16 * ks + 8 * hf);
+        hfr[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GK + koff[ks]);
 #pragma unroll
       for (int a = 0; a < WNT; ++a)
 #pragma unroll
@@ -162,35 +154,41 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
     }
   };
 
-  // prologue: weight stages 0 .. kWRing-1 in flight, stage 0 staged
-#pragma unroll
-  for (int u = 0; u < kWRing; ++u)
-    if (u < nk) load_w(u, wring[u]);
-  load_a(0);
-  store(0, wring[0]);
-  if (kWRing > 1 && kWRing < nk) load_w(kWRing, wring[0]);
-  __syncthreads();
+  // prologue: stages 0..2 in flight, wait for stage 0
+  issue(0, st0);
+  if (nk > 1) issue(1, st1);
+  if (nk > 2) issue(2, st2);
+  if (nk > 2)
+    wait_vm_upto<2 * GBPW>();
+  else if (nk > 1)
+    wait_vm_upto<GBPW>();
+  else
+    wait_vm_upto<0>();
+  __builtin_amdgcn_s_barrier();
 
-  // one K stage; the ring slot of stage kt + 1 is a compile-time constant
-  auto step = [&](int kt, auto u_tag) {
-    constexpr int un = (decltype(u_tag)::value + 1) % kWRing;
-    if (kt + 1 < nk) {
-      load_a(kt + 1);
-      if (kWRing == 1) load_w(kt + 1, wring[0]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kt & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      store((kt + 1) & 1, wring[un]);
-      if (kWRing > 1 && kt + 1 + kWRing < nk) load_w(kt + 1 + kWRing, wring[un]);
-    }
-    __syncthreads();
+  // step kt reads stage kt % 4 and refills the stage step kt - 1 read
+  auto step = [&](int kt, auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
+    bf16_t* const cur = S == 0 ? st0 : S == 1 ? st1 : S == 2 ? st2 : st3;
+    bf16_t* const ref = S == 0 ? st3 : S == 1 ? st0 : S == 2 ? st1 : st2;
+    if (kt + 3 < nk) issue(kt + 3, ref);
+    compute(cur);
+    // stage kt + 1 has landed once at most the stages issued after it are in flight
+    if (kt + 3 < nk)
+      wait_vm_upto<2 * GBPW>();
+    else if (kt + 2 < nk)
+      wait_vm_upto<GBPW>();
+    else
+      wait_vm_upto<0>();
+    __builtin_amdgcn_s_barrier();
   };
-  for (int kt = 0; kt < nk; kt += kWRing) {
+  for (int kt = 0; kt < nk; kt += GSTAGES) {
     step(kt, std::integral_constant<int, 0>{});
-    if constexpr (kWRing > 1) if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % kWRing>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3>{});
   }
+  bf16_t* const gl = st0;  // free after the K loop: the epilogue's exchange area
 
   const int vb = v0 + wv * (GN / 2) + 4 * hf;  // + 32 va + 8 (r / 4) + r % 4
   if constexpr (!FUSED) {
@@ -422,14 +420,9 @@ void conf_layout(int N, int V, int* nchunk, int* chunk) {
 }  // namespace
 
 namespace {
-template <int GK, bool FUSED>
+template <bool FUSED>
 int launch_gemm(dim3 grid, hipStream_t st, const GemmArgs& g) {
-  // the workgroup tile needs more than the default 64 KiB of dynamic LDS
-  if (hipFuncSetAttribute((const void*)lmhead_gemm_kernel<GK, FUSED>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)GemmCfg<GK>::LDS) != hipSuccess)
-    return MARS_ERR_LAUNCH;
-  hipLaunchKernelGGL((lmhead_gemm_kernel<GK, FUSED>), grid, dim3(GT), GemmCfg<GK>::LDS, st, g);
+  hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED>), grid, dim3(GT), 0, st, g);
   return MARS_OK;
 }
 }  // namespace
@@ -452,7 +445,11 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
   MARS_REQUIRE(N >= 1 && V >= 4 && V % 4 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(N <= 65535, MARS_ERR_SHAPE);  // confidence grid: one row per gridDim.y
   MARS_REQUIRE((double)N * V < 9.0e18, MARS_ERR_SHAPE);
-  if (hidden) MARS_REQUIRE(D >= 32 && D % 32 == 0, MARS_ERR_SHAPE);
+  if (hidden) {
+    MARS_REQUIRE(D >= 32 && D % 32 == 0, MARS_ERR_SHAPE);
+    // buffer views address one 256-row tile with 32-bit byte offsets
+    MARS_REQUIRE((double)GN * D * 2 < 4294967295.0, MARS_ERR_SHAPE);
+  }
   MARS_REQUIRE(mars_aligned16(hidden) && mars_aligned16(w_lm) && mars_aligned16(logits) &&
                    mars_aligned16(top_id) && mars_aligned16(p_max) &&
                    mars_aligned16(workspace),
@@ -482,10 +479,7 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
     g.nvt = (V + GN - 1) / GN;
     dim3 grid(g.nvt, (N + GM - 1) / GM);
     const bool fused = logits == nullptr;
-    const int rc = D % 64 == 0 ? (fused ? launch_gemm<64, true>(grid, st, g)
-                                        : launch_gemm<64, false>(grid, st, g))
-                               : (fused ? launch_gemm<32, true>(grid, st, g)
-                                        : launch_gemm<32, false>(grid, st, g));
+    const int rc = fused ? launch_gemm<true>(grid, st, g) : launch_gemm<false>(grid, st, g);
     if (rc != MARS_OK) return rc;
     if (fused) {
       c.nchunk = g.nvt;

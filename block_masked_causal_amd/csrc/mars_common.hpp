@@ -77,6 +77,32 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, void* lds_block, uint32_t b
                                            16, byte_off, 0, 0, 0);
 }
 
+// Buffer descriptor as four words (for inline assembly): base address, no
+// stride, `bytes` records; reads outside [0, bytes) return zeros.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// As lds_load16, but issued as inline assembly so that the compiler inserts
+// no waits of its own for it: the caller waits with wait_vm_upto before the
+// barrier that publishes the data. Kernels using it set M0 nowhere else.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, void* lds_block, uint32_t byte_off) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_block;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(la), "v"(byte_off), "s"(rsrc)
+               : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight (loads
+// complete in order, so everything older than the newest N has landed).
+template <int N>
+__device__ __forceinline__ void wait_vm_upto() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt = N, expcnt and lgkmcnt unconstrained
+}
+
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
