@@ -317,7 +317,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 // stages holding Q, dO, lse and D.
 template <int D>
 struct DkvCfg {
-  static constexpr int QB = 32;                 // query rows per block
+  static constexpr int QB = 64;                 // query rows per staged block (2 x 32)
   static constexpr int CPR = D / 8;
   static constexpr int QSZ = QB * D;            // Q (or dO) block, elements
   static constexpr int NBLK = QSZ / 512;        // 1 KiB blocks per Q (or dO) block
@@ -329,6 +329,7 @@ template <int D, int MASK>
 __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
                                           const bf16_t* __restrict__ Ds,
                                           const float* __restrict__ Ls,
+                                          const float* __restrict__ Dl,
                                           const bf16_t* __restrict__ Vs,
                                           const bf16x8 (&kf)[D / 16], f32x16 (&dk)[D / 32],
                                           f32x16 (&dv)[D / 32], float cs, int lo1, int w1,
@@ -369,7 +370,7 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const f32x4 l4 = *(const f32x4*)(Ls + 8 * g + 4 * hf);
-    const f32x4 d4 = *(const f32x4*)(Ls + 32 + 8 * g + 4 * hf);
+    const f32x4 d4 = *(const f32x4*)(Dl + 8 * g + 4 * hf);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * g + e;
@@ -402,7 +403,7 @@ template <int D>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p) {
   using C = DkvCfg<D>;
   // per stage: Q block, dO block, then lse2[32] and D[32]
-  constexpr int STG_EL = 2 * C::QSZ + 128;  // elements (bf16 units); the floats take 128
+  constexpr int STG_EL = 2 * C::QSZ + 4 * C::QB;  // elements (bf16 units); 2 QB floats
   __shared__ __attribute__((aligned(16))) bf16_t stage0[STG_EL];
   __shared__ __attribute__((aligned(16))) bf16_t stage1[STG_EL];
   __shared__ __attribute__((aligned(16))) bf16_t vtile[C::VSZ];
@@ -506,18 +507,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   };
   // lse2 and D of a block: loaded into registers by wave 0, stored after compute
   float lval = 0.f, dval = 0.f;
+  static_assert(C::QB == 64, "one lse / D value per lane of wave 0");
   auto load_ld = [&](int it) {
-    if (w == 0 && lane < C::QB) {
+    if (w == 0) {
       const int a = block_q0(it) + lane;
       lval = a < p.twoL ? p.lse[lrow + a] * kLog2e : 0.f;
       dval = a < p.twoL ? p.dsum[lrow + a] : 0.f;
     }
   };
   auto store_ld = [&](bf16_t* st) {
-    if (w == 0 && lane < C::QB) {
+    if (w == 0) {
       float* L2 = (float*)(st + 2 * C::QSZ);
       L2[lane] = lval;
-      L2[32 + lane] = dval;
+      L2[C::QB + lane] = dval;
     }
   };
 
@@ -569,28 +571,36 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
     const bf16_t* Qs = STG == 0 ? stage0 : stage1;
     const bf16_t* Ds = Qs + C::QSZ;
     const float* Ls = (const float*)(Qs + 2 * C::QSZ);
-    const int q0 = block_q0(it);
-    // the lane's visible rows relative to its first row q0 + 4 hf
-    const int rb = q0 + 4 * hf;
-    const int l1 = max(lo1, q0) - rb, x1 = max(min(hi1, q0 + C::QB) - max(lo1, q0), 0);
-    const int l2 = max(lo2, q0) - rb, x2 = max(min(hi2, q0 + C::QB) - max(lo2, q0), 0);
-    const bool any = __builtin_amdgcn_ballot_w64((x1 > 0) | (x2 > 0)) != 0;
-    if (any) {
-      // every row of the block visible to every key of the wave?
-      const bool all1 = (lo1 <= q0) & (hi1 >= q0 + C::QB);
-      const bool all2 = (lo2 <= q0) & (hi2 >= q0 + C::QB);
-      const bool full = __builtin_amdgcn_ballot_w64(!(all1 | all2)) == 0;
-      const bool two = __builtin_amdgcn_ballot_w64((x1 > 0) & (x2 > 0)) != 0;
-      if (full) {
-        dkv_block<D, kMaskNone>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, 0, 0, 0, 0, qad,
-                                qtr, vad, hf);
-      } else if (!two) {
-        const bool in1 = x1 > 0;
-        dkv_block<D, kMaskRange>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, in1 ? l1 : l2,
-                                 in1 ? x1 : x2, 0, 0, qad, qtr, vad, hf);
-      } else {
-        dkv_block<D, kMaskBoth>(Qs, Ds, Ls, vtile, kf, dk, dv, p.scale_log2, l1, x1, l2, x2,
-                                qad, qtr, vad, hf);
+    // two 32-row sub-blocks of the staged 64 rows
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int q0 = block_q0(it) + 32 * sb;
+      // the lane's visible rows relative to its first row q0 + 4 hf
+      const int rb = q0 + 4 * hf;
+      const int l1 = max(lo1, q0) - rb, x1 = max(min(hi1, q0 + 32) - max(lo1, q0), 0);
+      const int l2 = max(lo2, q0) - rb, x2 = max(min(hi2, q0 + 32) - max(lo2, q0), 0);
+      const bool any = __builtin_amdgcn_ballot_w64((x1 > 0) | (x2 > 0)) != 0;
+      if (any) {
+        const bf16_t* Qb = Qs + 32 * sb * D;
+        const bf16_t* Db = Ds + 32 * sb * D;
+        const float* Lb = Ls + 32 * sb;
+        const float* Dlb = Ls + C::QB + 32 * sb;
+        // every row of the sub-block visible to every key of the wave?
+        const bool all1 = (lo1 <= q0) & (hi1 >= q0 + 32);
+        const bool all2 = (lo2 <= q0) & (hi2 >= q0 + 32);
+        const bool full = __builtin_amdgcn_ballot_w64(!(all1 | all2)) == 0;
+        const bool two = __builtin_amdgcn_ballot_w64((x1 > 0) & (x2 > 0)) != 0;
+        if (full) {
+          dkv_block<D, kMaskNone>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, 0, 0, 0, 0,
+                                  qad, qtr, vad, hf);
+        } else if (!two) {
+          const bool in1 = x1 > 0;
+          dkv_block<D, kMaskRange>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2,
+                                   in1 ? l1 : l2, in1 ? x1 : x2, 0, 0, qad, qtr, vad, hf);
+        } else {
+          dkv_block<D, kMaskBoth>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, l1, x1, l2,
+                                  x2, qad, qtr, vad, hf);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
