@@ -10,6 +10,7 @@ from .mars_oracle import (  # noqa: F401
     build_mask_loops,
     causal_mask,
     ar_signal_ratio,
+    attn_causal,
     attn_two_stream,
     attn_two_stream_backward,
     attn_block_decode,

@@ -163,6 +163,32 @@ def attn_two_stream(q, k, v, L: int, B: int, scale: float | None = None,
     return outs, lses
 
 
+def attn_causal(q, k, v, scale: float | None = None, pairs=None):
+    """Plain causal attention over T positions (the no-cache prefill path: every step
+    recomputes the whole sequence, prompt plus the B [MASK] rows, causally; [gist] 4
+    and the notes' wall-clock table for the no-cache setting).
+
+    q [b, T, Hq, d], k/v [b, T, Hkv, d]. Returns (out, lse) dicts keyed by
+    (batch, q_head), as attn_two_stream.
+    """
+    q = np.asarray(q)
+    b, n, Hq, d = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    M = causal_mask(n)
+    if pairs is None:
+        pairs = [(bi, h) for bi in range(b) for h in range(Hq)]
+    outs, lses = {}, {}
+    for (bi, h) in pairs:
+        K = np.asarray(k[bi, :, h // g, :], dtype=np.float64)
+        Vv = np.asarray(v[bi, :, h // g, :], dtype=np.float64)
+        Q = np.asarray(q[bi, :, h, :], dtype=np.float64)
+        outs[(bi, h)], lses[(bi, h)] = _softmax_attend(Q, K, Vv, M, scale)
+    return outs, lses
+
+
 def attn_two_stream_backward(q, k, v, do, L: int, B: int, scale: float | None = None,
                              mask_mode: int = 0, groups=None, row_chunk: int = 1024):
     """Gradients of `attn_two_stream` with respect to q, k and v, given do = dLoss/dO.

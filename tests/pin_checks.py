@@ -167,6 +167,36 @@ def check_gqa_head_map(attn, L=8, B=2, d=4):
 
 # ------------------------------------------------------------- decode ------
 
+# ---------------------------------------------------------- causal prefill -
+
+def check_causal_vs_sdpa(causal, T=23, Hq=4, Hkv=2, d=8, seed=21):
+    """Library reference: torch CPU causal scaled_dot_product_attention, any length."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, T, Hq, d))
+    k = rng.standard_normal((2, T, Hkv, d))
+    v = rng.standard_normal((2, T, Hkv, d))
+    outs, lses = causal(q, k, v)
+    g = Hq // Hkv
+    for (bi, h), o in outs.items():
+        np.testing.assert_allclose(o, sdpa_causal(q[bi, :, h], k[bi, :, h // g],
+                                                  v[bi, :, h // g], 1 / np.sqrt(d)),
+                                   atol=1e-12, rtol=0)
+        # lse: natural log of the sum of exp of the scaled causal scores, row by row
+        s = (q[bi, :, h] @ k[bi, :, h // g].T) / np.sqrt(d)
+        ref = np.array([np.log(np.exp(s[i, :i + 1]).sum()) for i in range(T)])
+        np.testing.assert_allclose(lses[(bi, h)], ref, atol=1e-12, rtol=0)
+
+
+def check_causal_equals_mode1(causal, attn, L=9, Hq=2, Hkv=1, d=4, seed=22):
+    """For an even length 2L the prefill equals the two-stream kernel's causal mode."""
+    q, k, v = rand_qkv(seed, 1, L, Hq, Hkv, d)
+    a, la = causal(q, k, v)
+    b, lb = attn(q, k, v, L, 3, mask_mode=1)
+    for key in a:
+        np.testing.assert_allclose(a[key], b[key], atol=1e-12, rtol=0)
+        np.testing.assert_allclose(la[key], lb[key], atol=1e-12, rtol=0)
+
+
 # ------------------------------------------------------- attention backward -
 
 def _forward_full(attn, q, k, v, L, B, mask_mode):

@@ -223,3 +223,26 @@ def test_backward_mutants_are_caught(kind):
     assert _fails(pc.check_backward_finite_differences, oracle.attn_two_stream, m, L=4, B=2,
                   Hq=2, Hkv=1, d=3)
     assert _fails(pc.check_backward_vs_torch_autograd, m)
+
+
+def test_causal_prefill_mutants_are_caught():
+    def causal_strict(q, k, v, scale=None, pairs=None):
+        # a row may not see itself (the diagonal dropped); row 0 then sees key 0 only
+        q = np.asarray(q)
+        b, n, Hq, d = q.shape
+        g = Hq // k.shape[2]
+        sc = 1.0 / np.sqrt(d) if scale is None else scale
+        M = np.tril(np.ones((n, n), dtype=bool), -1)
+        M[0, 0] = True
+        outs, lses = {}, {}
+        for bi in range(b):
+            for h in range(Hq):
+                outs[(bi, h)], lses[(bi, h)] = om._softmax_attend(
+                    q[bi, :, h], k[bi, :, h // g], v[bi, :, h // g], M, sc)
+        return outs, lses
+
+    def causal_unscaled(q, k, v, scale=None, pairs=None):
+        return oracle.attn_causal(q, k, v, scale=1.0, pairs=pairs)
+
+    assert _fails(pc.check_causal_vs_sdpa, causal_strict)
+    assert _fails(pc.check_causal_vs_sdpa, causal_unscaled)

@@ -204,3 +204,13 @@ def test_backward_matches_torch_autograd(mode):
 
 def test_backward_groups_and_row_chunks():
     pc.check_backward_groups_and_chunks(oracle.attn_two_stream_backward)
+
+
+# ---- no-cache prefill: plain causal attention over any length ([gist] 4)
+
+def test_causal_prefill_matches_sdpa():
+    pc.check_causal_vs_sdpa(oracle.attn_causal)
+
+
+def test_causal_prefill_equals_two_stream_mode1():
+    pc.check_causal_equals_mode1(oracle.attn_causal, oracle.attn_two_stream)
