@@ -20,9 +20,11 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     mars_accept_commit,
     mars_attn_block_decode,
+    mars_attn_causal,
     mars_attn_two_stream,
     mars_attn_two_stream_bwd,
     mars_decode_workspace_bytes,
+    mars_kv_append,
     mars_lmhead_confidence,
     mars_lmhead_workspace_bytes,
 )

@@ -35,6 +35,10 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "mars_attn_two_stream": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f, _i32, _p]),
+    "mars_attn_causal": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        _f, _p]),
+    "mars_kv_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _p, _p]),
     "mars_attn_two_stream_bwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _i32, _f, _i32, _p, _sz,
                                                 _p]),

@@ -66,6 +66,52 @@ def mars_attn_two_stream(q, k, v, L: int, B: int, *, o=None, lse=None, return_ls
     return (o, lse) if lse is not None else o
 
 
+def mars_attn_causal(q, k, v, *, o=None, lse=None, return_lse=False,
+                     softmax_scale: float = 0.0, stream=None):
+    """Causal attention over T positions (no-cache prefill). q [b, T, Hq, d],
+    k/v [b, T, Hkv, d]; returns o (and lse [b, Hq, T] when asked)."""
+    dt = q.dtype
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, 4)
+    b, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (b, T, Hkv, d) or v.shape != k.shape:
+        raise ValueError("shapes must be q [b,T,Hq,d], k/v [b,T,Hkv,d]")
+    if o is None:
+        o = torch.empty_like(q)
+    _need(o, "o", dt)
+    if lse is None and return_lse:
+        lse = torch.empty((b, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    code = _lib.lib().mars_attn_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, T, Hq,
+                                       Hkv, d, _DT.get(dt, -1), float(softmax_scale),
+                                       _stream(stream))
+    check("mars_attn_causal", code)
+    return (o, lse) if lse is not None else o
+
+
+def mars_kv_append(k_rows, v_rows, k_cache, v_cache, block_table, cache_len, *, status=None,
+                   stream=None):
+    """Append k_rows/v_rows [S, T, Hkv, d] to the paged cache at cache_len; cache_len
+    is advanced in place. Cache layouts as for mars_attn_block_decode."""
+    dt = k_rows.dtype
+    for t, n in ((k_rows, "k_rows"), (v_rows, "v_rows"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, n, dt, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    S, T, Hkv, d = k_rows.shape
+    num_pages, _, page, _ = k_cache.shape
+    if v_rows.shape != k_rows.shape or tuple(v_cache.shape) != (num_pages, Hkv, d, page):
+        raise ValueError("v_rows as k_rows; k_cache [pages,Hkv,page,d], v_cache [pages,Hkv,d,page]")
+    code = _lib.lib().mars_kv_append(_ptr(k_rows), _ptr(v_rows), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_table), _ptr(cache_len), S, T, Hkv, d, page,
+                                     block_table.shape[1], num_pages, _DT.get(dt, -1),
+                                     _ptr(status), _stream(stream))
+    check("mars_kv_append", code)
+
+
 def mars_attn_two_stream_bwd(q, k, v, o, d_o, lse, L: int, B: int, *, dq=None, dk=None,
                              dv=None, workspace=None, softmax_scale: float = 0.0,
                              mask_mode: int = 0, stream=None):

@@ -110,6 +110,85 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
   if (tid == 0) p.cache_len[s] = len + nc;
 }
 
+// ---------------------------------------------------------------- append ----
+// Append T rows per sequence to the paged cache (the prefill's K/V): row r of
+// sequence s goes to position cache_len[s] + r. Grid (ceil(T / 64), S): each
+// workgroup resolves the pages of its 64 rows in parallel, then copies them
+// with the same layouts as the commit above.
+struct AppendArgs {
+  const char* k_rows;
+  const char* v_rows;
+  char* k_cache;
+  char* v_cache;
+  const int32_t* block_table;
+  int32_t* cache_len;
+  int32_t* status;
+  int S, T, Hkv, D, page_size, max_pages, num_pages;
+};
+
+template <int ES>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
+  __shared__ int sh_page[64];
+  const int s = blockIdx.y, r0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int len = p.cache_len[s];
+  const int nr = min(64, p.T - r0);
+  if (tid < nr) {
+    const long long pos = (long long)len + r0 + tid;
+    const long long cap = (long long)p.max_pages * p.page_size;
+    int pg = -1;
+    if (len < 0 || pos >= cap) {
+      status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+    } else {
+      pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
+      if (pg < 0 || pg >= p.num_pages) {
+        status_or(p.status, MARS_STATUS_BAD_PAGE);
+        pg = -1;
+      }
+    }
+    sh_page[tid] = pg;
+  }
+  __syncthreads();
+  const int rowbytes = p.D * ES;
+  const int chunks = rowbytes / 16;
+  for (int idx = tid; idx < nr * p.Hkv * chunks; idx += 256) {
+    const int ch = idx % chunks;
+    const int kvh = (idx / chunks) % p.Hkv;
+    const int r = idx / (chunks * p.Hkv);
+    const int pg = sh_page[r];
+    if (pg < 0) continue;
+    const int pos = len + r0 + r;
+    const size_t src = (((size_t)s * p.T + r0 + r) * p.Hkv + kvh) * rowbytes + ch * 16;
+    const size_t dst =
+        (((size_t)pg * p.Hkv + kvh) * p.page_size + pos % p.page_size) * rowbytes + ch * 16;
+    *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_rows + src);
+  }
+  for (int idx = tid; idx < nr * p.Hkv * p.D; idx += 256) {
+    const int r = idx % nr;
+    const int d = (idx / nr) % p.D;
+    const int kvh = idx / (nr * p.D);
+    const int pg = sh_page[r];
+    if (pg < 0) continue;
+    const int pos = len + r0 + r;
+    const size_t src = ((((size_t)s * p.T + r0 + r) * p.Hkv + kvh) * p.D + d) * ES;
+    const size_t dst =
+        ((((size_t)pg * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
+    if (ES == 2)
+      *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_rows + src);
+    else
+      *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_rows + src);
+  }
+}
+
+// After the copy (same stream): cache_len[s] advances by the rows that fit.
+__global__ __launch_bounds__(256) void kv_append_len_kernel(AppendArgs p) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= p.S) return;
+  const int len = p.cache_len[s];
+  if (len < 0) return;
+  const long long cap = (long long)p.max_pages * p.page_size;
+  p.cache_len[s] = (int)min((long long)len + p.T, max((long long)len, cap));
+}
+
 }  // namespace
 
 extern "C" int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* tau,
@@ -178,3 +257,44 @@ extern "C" const char* mars_strerror(int code) {
 }
 
 extern "C" int mars_version(void) { return 100; }
+
+extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_cache,
+                              void* v_cache, const int32_t* block_table, int32_t* cache_len,
+                              int32_t S, int32_t T, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t max_pages, int32_t num_pages,
+                              int32_t dtype, int32_t* status, void* stream) {
+  MARS_REQUIRE(k_rows && v_rows && k_cache && v_cache && block_table && cache_len,
+               MARS_ERR_NULL);
+  MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
+  MARS_REQUIRE(S >= 1 && S <= 65535 && T >= 1 && T <= (1 << 30), MARS_ERR_SHAPE);
+  MARS_REQUIRE(n_kv_heads >= 1 && head_dim >= 8 && head_dim % 8 == 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(page_size >= 1 && max_pages >= 1 && num_pages >= 1, MARS_ERR_SHAPE);
+  MARS_REQUIRE((long long)max_pages * page_size <= (1LL << 30), MARS_ERR_SHAPE);
+  MARS_REQUIRE(mars_aligned16(k_rows) && mars_aligned16(v_rows) && mars_aligned16(k_cache) &&
+                   mars_aligned16(v_cache) && mars_aligned16(block_table) &&
+                   mars_aligned16(cache_len),
+               MARS_ERR_ALIGN);
+  AppendArgs a;
+  a.k_rows = (const char*)k_rows;
+  a.v_rows = (const char*)v_rows;
+  a.k_cache = (char*)k_cache;
+  a.v_cache = (char*)v_cache;
+  a.block_table = block_table;
+  a.cache_len = cache_len;
+  a.status = status;
+  a.S = S;
+  a.T = T;
+  a.Hkv = n_kv_heads;
+  a.D = head_dim;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((T + 63) / 64, S);
+  if (dtype == MARS_BF16)
+    hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(kv_append_len_kernel, dim3((S + 255) / 256), dim3(256), 0, st, a);
+  return mars_launch_status();
+}

@@ -478,21 +478,21 @@ int launch_f32(const TwoStreamArgs& a, hipStream_t st) {
 
 }  // namespace
 
-extern "C" int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o,
-                                    float* lse, int32_t batch, int32_t L, int32_t B,
-                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                                    int32_t dtype, float softmax_scale, int32_t mask_mode,
-                                    void* stream) {
+namespace {
+// Common path of both entry points: the attention over n = twoL positions under
+// mask_mode (0: MARS two-stream mask with stream length L and block size B,
+// 1: causal over all n positions).
+int run_attention(const void* q, const void* k, const void* v, void* o, float* lse, int32_t batch,
+                  int32_t L, int32_t twoL, int32_t B, int32_t n_q_heads, int32_t n_kv_heads,
+                  int32_t head_dim, int32_t dtype, float softmax_scale, int32_t mask_mode,
+                  void* stream) {
   MARS_REQUIRE(q && k && v && o, MARS_ERR_NULL);
   MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
-  MARS_REQUIRE(batch >= 1 && L >= 1 && B >= 1 && B <= L && L <= (1 << 29), MARS_ERR_SHAPE);
   MARS_REQUIRE(n_q_heads >= 1 && n_kv_heads >= 1 && n_q_heads % n_kv_heads == 0, MARS_ERR_SHAPE);
-  MARS_REQUIRE(mask_mode == 0 || mask_mode == 1, MARS_ERR_SHAPE);
   MARS_REQUIRE(head_dim >= 1, MARS_ERR_SHAPE);
   MARS_REQUIRE(mars_aligned16(q) && mars_aligned16(k) && mars_aligned16(v) &&
                    mars_aligned16(o) && mars_aligned16(lse),
                MARS_ERR_ALIGN);
-  const int twoL = 2 * L;
   // Element offsets must fit the kernels' index arithmetic.
   MARS_REQUIRE((double)batch * twoL * n_q_heads * head_dim < 9.0e18, MARS_ERR_SHAPE);
   // Buffer loads address one (batch, head) slice with 32-bit byte offsets.
@@ -527,4 +527,30 @@ extern "C" int mars_attn_two_stream(const void* q, const void* k, const void* v,
   if (head_dim == 64) return launch_f32<64>(a, st);
   if (head_dim == 128) return launch_f32<128>(a, st);
   return MARS_ERR_UNSUPPORTED;
+}
+}  // namespace
+
+extern "C" int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int32_t batch, int32_t L, int32_t B,
+                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t dtype, float softmax_scale, int32_t mask_mode,
+                                    void* stream) {
+  MARS_REQUIRE(q && k && v && o, MARS_ERR_NULL);
+  MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
+  MARS_REQUIRE(batch >= 1 && L >= 1 && B >= 1 && B <= L && L <= (1 << 29), MARS_ERR_SHAPE);
+  MARS_REQUIRE(mask_mode == 0 || mask_mode == 1, MARS_ERR_SHAPE);
+  return run_attention(q, k, v, o, lse, batch, L, 2 * L, B, n_q_heads, n_kv_heads, head_dim,
+                       dtype, softmax_scale, mask_mode, stream);
+}
+
+extern "C" int mars_attn_causal(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t batch, int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t dtype, float softmax_scale,
+                                void* stream) {
+  MARS_REQUIRE(q && k && v && o, MARS_ERR_NULL);
+  MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
+  MARS_REQUIRE(batch >= 1 && T >= 1 && T <= (1 << 30), MARS_ERR_SHAPE);
+  // causal mode: the stream split (L, B) plays no part
+  return run_attention(q, k, v, o, lse, batch, (T + 1) / 2, T, 1, n_q_heads, n_kv_heads,
+                       head_dim, dtype, softmax_scale, 1, stream);
 }

@@ -97,6 +97,40 @@ int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o, f
                          float softmax_scale, int32_t mask_mode, void* stream);
 
 /*
+ * Causal attention over T positions: the no-cache prefill, in which every step
+ * recomputes the whole sequence (prompt plus the B [MASK] rows) causally
+ * (gist.science explainer, section 4; papernotes.org notes, wall-clock table,
+ * no-cache row).
+ *
+ * q [batch, T, n_q_heads, head_dim], k/v [batch, T, n_kv_heads, head_dim],
+ * o as q; lse optional [batch, n_q_heads, T]. T may be odd. Same dtypes, head
+ * sizes, scale default, errors and determinism as mars_attn_two_stream in its
+ * causal mode (which this is, with the two-stream split removed).
+ */
+int mars_attn_causal(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int32_t batch, int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t dtype, float softmax_scale, void* stream);
+
+/*
+ * Append T rows per sequence to the paged KV cache (fills the block-level
+ * cache from a prefill; notes, key design 4 (关键设计 4)). Row r of sequence s
+ * goes to position cache_len[s] + r, in the layouts of mars_attn_block_decode
+ * (K [pages, Hkv, page, d], V [pages, Hkv, d, page]); then cache_len[s]
+ * advances by the rows that fit in the sequence's max_pages * page_size
+ * capacity.
+ *
+ * k_rows, v_rows [S, T, n_kv_heads, head_dim] (dtype MARS_BF16 or MARS_F32);
+ * block_table [S, max_pages] int32; cache_len [S] int32 (updated in place).
+ * Rows past the capacity or on a page id outside [0, num_pages) are skipped
+ * and raise MARS_STATUS_CACHE_OVERFLOW / MARS_STATUS_BAD_PAGE in `status`
+ * (optional). Two launches on `stream`: the copy, then the length update.
+ */
+int mars_kv_append(const void* k_rows, const void* v_rows, void* k_cache, void* v_cache,
+                   const int32_t* block_table, int32_t* cache_len, int32_t S, int32_t T,
+                   int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t max_pages,
+                   int32_t num_pages, int32_t dtype, int32_t* status, void* stream);
+
+/*
  * Two-stream MARS attention backward: dq, dk, dv of mars_attn_two_stream.
  *
  * Defines: the pages train the unchanged model on L_mask + L_AR through the

@@ -16,6 +16,7 @@ from .generators import (  # noqa: F401
     bf16_round,
     bf16_bits_to_f32,
     two_stream_qkv,
+    sequence_qkv,
     decode_inputs,
     lmhead_inputs,
     normal_logits,

@@ -83,6 +83,16 @@ def two_stream_qkv(seed: int, batch: int, L: int, n_q_heads: int, n_kv_heads: in
     return q, k, v
 
 
+def sequence_qkv(seed: int, batch: int, T: int, n_q_heads: int, n_kv_heads: int,
+                 head_dim: int, dtype: str = "bf16"):
+    """Q/K/V over one sequence of T positions (any T), entries N(0, 1)."""
+    rng = np.random.default_rng([seed, 104729])
+    q = _make(_normal(rng, (batch, T, n_q_heads, head_dim)), dtype)
+    k = _make(_normal(rng, (batch, T, n_kv_heads, head_dim)), dtype)
+    v = _make(_normal(rng, (batch, T, n_kv_heads, head_dim)), dtype)
+    return q, k, v
+
+
 @dataclass
 class DecodeInputs:
     q: Tensor

@@ -90,6 +90,29 @@ def test_two_stream_bwd_argument_checks():
     assert bwd(ws=None) == _lib.MARS_ERR_WORKSPACE
 
 
+def test_causal_and_append_argument_checks():
+    L_ = mars.lib()
+    # rejected before any launch
+    assert L_.mars_attn_causal(None, FAKE, FAKE, FAKE, None, 1, 9, 2, 1, 64, 1, 0.0,
+                               None) == _lib.MARS_ERR_NULL
+    assert L_.mars_attn_causal(FAKE, FAKE, FAKE, FAKE, None, 1, 0, 2, 1, 64, 1, 0.0,
+                               None) == _lib.MARS_ERR_SHAPE
+    assert L_.mars_attn_causal(FAKE, FAKE, FAKE, FAKE, None, 1, 9, 3, 2, 64, 1, 0.0,
+                               None) == _lib.MARS_ERR_SHAPE
+    assert L_.mars_attn_causal(FAKE, FAKE, FAKE, FAKE, None, 1, 9, 2, 1, 64, 7, 0.0,
+                               None) == _lib.MARS_ERR_DTYPE
+    assert L_.mars_attn_causal(MIS, FAKE, FAKE, FAKE, None, 1, 9, 2, 1, 64, 1, 0.0,
+                               None) == _lib.MARS_ERR_ALIGN
+    ap = lambda **kw: L_.mars_kv_append(kw.get("k", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        kw.get("S", 2), kw.get("T", 5), 2, kw.get("d", 64),
+                                        16, 4, 8, kw.get("dt", 1), None, None)
+    assert ap(k=None) == _lib.MARS_ERR_NULL
+    assert ap(T=0) == _lib.MARS_ERR_SHAPE
+    assert ap(d=12) == _lib.MARS_ERR_SHAPE
+    assert ap(dt=5) == _lib.MARS_ERR_DTYPE
+    assert ap(k=MIS) == _lib.MARS_ERR_ALIGN
+
+
 def test_decode_argument_checks():
     assert dec(q=None) == _lib.MARS_ERR_NULL
     assert dec(dtype=5) == _lib.MARS_ERR_DTYPE
