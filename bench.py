@@ -20,7 +20,8 @@ second. Per-kernel times come from HIP events recorded on the stream the
 kernels run on. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
-switch (accepted tokens/s), and the CPU oracle timed on a bounded sample.
+switch (accepted tokens/s), the no-cache causal prefill and the paged KV
+append, and the CPU oracle timed on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
 
 `roofline.traffic` is the HBM bytes one launch moves, from two rocprofv3
@@ -52,6 +53,8 @@ TS = dict(batch=8, L=2048, B=4, Hq=14, Hkv=2, d=64)           # two-stream, 0.5B
 TS7 = dict(batch=4, L=4096, B=16, Hq=28, Hkv=4, d=128)        # two-stream, 7B shape
 DEC = dict(S=64, B=4, Hq=28, Hkv=4, d=128, lo=512, hi=4096, page=16)
 LM = dict(D=3584, V=152064)
+PRE = dict(batch=8, T=4096 + 4, Hq=14, Hkv=2, d=64)              # no-cache prefill, 0.5B
+APP = dict(S=64, T=2048, Hkv=4, d=128, page=16)                  # prompt KV append, 7B
 LOOP = dict(S=256, B=8, Hq=28, Hkv=4, d=128, lo=128, hi=2048, page=16, steps=64, switch=32)
 
 
@@ -256,6 +259,9 @@ def main():
         lse = torch.empty((TS["batch"], TS["Hq"], 2 * TS["L"]), dtype=torch.float32, device=dev)
         mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O, lse=lse)
         mars.mars_attn_two_stream_bwd(Q, K, V, O, Q, lse, TS["L"], TS["B"])
+        # and one KV append at the prompt-append shape
+        app = append_inputs(synth, torch, dev)
+        mars.mars_kv_append(*app)
         torch.cuda.synchronize()
         print(json.dumps({"profile_pass": True, "copy_bytes": n * 4,
                           "status_flags": int(status.item())}), flush=True)
@@ -428,6 +434,10 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
     # two-stream attention backward (dq, dk, dv) at both training shapes
     out["two_stream_bwd"] = two_stream_bwd(mars, synth, torch, dev, traffic)
 
+    # no-cache causal prefill over prompt + one block of masks, and the KV append
+    # that fills the paged cache from a prompt
+    out["causal_prefill"] = causal_prefill(mars, synth, torch, dev, traffic)
+
     # batched decode loop with a live tau switch
     out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
     return out
@@ -467,6 +477,70 @@ def two_stream_bwd(mars, synth, torch, dev, traffic):
                                           else None)}
         del Q, K, V, DO, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+    return res
+
+
+def append_inputs(synth, torch, dev):
+    """Rows to append and an empty paged cache with room for them (APP shape)."""
+    a_ = APP
+    di = synth.decode_inputs(1009, a_["S"], 1, a_["Hkv"], a_["Hkv"], a_["d"], 0, 0, a_["page"],
+                             extra_capacity=a_["T"])
+    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+    bt = to_dev(di.block_table, dev)
+    del di
+    _, kr, vr = synth.decode_step_tensors(1009, 0, a_["S"], a_["T"], a_["Hkv"], a_["Hkv"],
+                                          a_["d"])
+    KR, VR = to_dev(kr, dev), to_dev(vr, dev)
+    cl = torch.zeros(a_["S"], dtype=torch.int32, device=dev)
+    return KR, VR, kc, vc, bt, cl
+
+
+def causal_prefill(mars, synth, torch, dev, traffic):
+    """Causal attention over T = prompt + B positions (useful FLOPs: 4 d per visible
+    pair per query head, T (T + 1) / 2 pairs), and the paged KV append of a prompt
+    (bytes: K and V rows read once and written once)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    c = PRE
+    log(f"causal prefill b={c['batch']} T={c['T']} heads {c['Hq']}/{c['Hkv']} d={c['d']}")
+    q, k, v = synth.sequence_qkv(1008, c["batch"], c["T"], c["Hq"], c["Hkv"], c["d"])
+    Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+    del q, k, v
+    O = torch.empty_like(Q)
+    for _ in range(2):
+        mars.mars_attn_causal(Q, K, V, o=O)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(5):
+        mars.mars_attn_causal(Q, K, V, o=O)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    fl = 4.0 * c["d"] * c["Hq"] * c["batch"] * c["T"] * (c["T"] + 1) / 2
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"prefill": {"shape": c, "ms": round(ms, 4), "useful_tflops": round(tf, 2),
+                       "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s")}}
+    del Q, K, V, O
+
+    a_ = APP
+    log(f"KV append S={a_['S']} T={a_['T']} heads {a_['Hkv']} d={a_['d']} page {a_['page']}")
+    KR, VR, kc, vc, bt, cl = append_inputs(synth, torch, dev)
+    times = []
+    for i in range(7):
+        cl.zero_()
+        a, b = ev(), ev()
+        a.record()
+        mars.mars_kv_append(KR, VR, kc, vc, bt, cl)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(a.elapsed_time(b))
+    ms = sum(times) / len(times)
+    nbytes = 2 * 2 * a_["S"] * a_["T"] * a_["Hkv"] * a_["d"] * 2
+    res["kv_append"] = {"shape": a_, "ms": round(ms, 4),
+                        "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS,
+                                             "GB/s", traffic.get("kv_append"), nbytes)}
+    del KR, VR, kc, vc, bt, cl
+    torch.cuda.empty_cache()
     return res
 
 

@@ -112,9 +112,15 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
 
 // ---------------------------------------------------------------- append ----
 // Append T rows per sequence to the paged cache (the prefill's K/V): row r of
-// sequence s goes to position cache_len[s] + r. Grid (ceil(T / 64), S): each
-// workgroup resolves the pages of its 64 rows in parallel, then copies them
-// with the same layouts as the commit above.
+// sequence s goes to position cache_len[s] + r. Grid (ceil((T + 7) / 64), S):
+// workgroup x of sequence s owns the 64 cache positions starting at
+// (cache_len[s] rounded down to a multiple of 8) + 64 x, so that every group of
+// 8 positions it writes is 8-aligned. It resolves the page of each position in
+// parallel, copies K rows straight through ([page][head][slot][d] keeps a row
+// contiguous), and stages V one head at a time in LDS so that it can write
+// the transposed V layout ([page][head][d][slot]) as runs of 8 slots, one
+// 16-byte store per run of 8 bf16 values, where the page size is a multiple
+// of 8; other page sizes take element stores.
 struct AppendArgs {
   const char* k_rows;
   const char* v_rows;
@@ -126,23 +132,36 @@ struct AppendArgs {
   int S, T, Hkv, D, page_size, max_pages, num_pages;
 };
 
+constexpr int kAppendMaxRowBytes = 512;  // head_dim * element size staged per V row
+
 template <int ES>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
-  __shared__ int sh_page[64];
-  const int s = blockIdx.y, r0 = blockIdx.x * 64, tid = threadIdx.x;
+  // V rows of one head, row stride rowbytes + 4 so that column reads of rows
+  // 8 apart fall in different banks
+  // (dynamic LDS of 64 * (head_dim * ES + 4) bytes)
+  extern __shared__ __attribute__((aligned(16))) char sv[];
+  __shared__ int sh_page[64];  // page of each window position; -1 skip (flagged), -2 not ours
+  const int s = blockIdx.y, tid = threadIdx.x;
   const int len = p.cache_len[s];
-  const int nr = min(64, p.T - r0);
-  if (tid < nr) {
-    const long long pos = (long long)len + r0 + tid;
-    const long long cap = (long long)p.max_pages * p.page_size;
-    int pg = -1;
-    if (len < 0 || pos >= cap) {
-      status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
-    } else {
-      pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
-      if (pg < 0 || pg >= p.num_pages) {
-        status_or(p.status, MARS_STATUS_BAD_PAGE);
+  if (len < 0) {
+    if (blockIdx.x == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+    return;
+  }
+  const long long wbase = (long long)(len & ~7) + 64LL * blockIdx.x;
+  const long long cap = (long long)p.max_pages * p.page_size;
+  if (tid < 64) {
+    const long long pos = wbase + tid;
+    int pg = -2;
+    if (pos >= len && pos < (long long)len + p.T) {
+      if (pos >= cap) {
+        status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
         pg = -1;
+      } else {
+        pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
+        if (pg < 0 || pg >= p.num_pages) {
+          status_or(p.status, MARS_STATUS_BAD_PAGE);
+          pg = -1;
+        }
       }
     }
     sh_page[tid] = pg;
@@ -150,32 +169,81 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   __syncthreads();
   const int rowbytes = p.D * ES;
   const int chunks = rowbytes / 16;
-  for (int idx = tid; idx < nr * p.Hkv * chunks; idx += 256) {
+  // a position with a page (pg >= 0) lies in [len, min(len + T, cap)): its row
+  // index and slot fit in int
+  const size_t row0 = (size_t)s * p.T;  // first row of this sequence
+  for (int idx = tid; idx < 64 * p.Hkv * chunks; idx += 256) {
     const int ch = idx % chunks;
     const int kvh = (idx / chunks) % p.Hkv;
-    const int r = idx / (chunks * p.Hkv);
-    const int pg = sh_page[r];
+    const int t = idx / (chunks * p.Hkv);
+    const int pg = sh_page[t];
     if (pg < 0) continue;
-    const int pos = len + r0 + r;
-    const size_t src = (((size_t)s * p.T + r0 + r) * p.Hkv + kvh) * rowbytes + ch * 16;
+    const int pos = (int)(wbase + t);
+    const size_t src = ((row0 + (pos - len)) * p.Hkv + kvh) * rowbytes + ch * 16;
     const size_t dst =
         (((size_t)pg * p.Hkv + kvh) * p.page_size + pos % p.page_size) * rowbytes + ch * 16;
     *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_rows + src);
   }
-  for (int idx = tid; idx < nr * p.Hkv * p.D; idx += 256) {
-    const int r = idx % nr;
-    const int d = (idx / nr) % p.D;
-    const int kvh = idx / (nr * p.D);
-    const int pg = sh_page[r];
-    if (pg < 0) continue;
-    const int pos = len + r0 + r;
-    const size_t src = ((((size_t)s * p.T + r0 + r) * p.Hkv + kvh) * p.D + d) * ES;
-    const size_t dst =
-        ((((size_t)pg * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
-    if (ES == 2)
-      *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_rows + src);
-    else
-      *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_rows + src);
+  const int rs = rowbytes + 4;
+  const bool runs = (p.page_size % 8) == 0;
+  for (int kvh = 0; kvh < p.Hkv; ++kvh) {
+    __syncthreads();  // the previous head's column reads are done
+    for (int idx = tid; idx < 64 * chunks; idx += 256) {
+      const int ch = idx % chunks;
+      const int t = idx / chunks;
+      if (sh_page[t] < 0) continue;
+      const int pos = (int)(wbase + t);
+      const u32x4 x = *(const u32x4*)(p.v_rows + ((row0 + (pos - len)) * p.Hkv + kvh) *
+                                                     rowbytes + ch * 16);
+      uint32_t* d4 = (uint32_t*)(sv + t * rs + ch * 16);
+      d4[0] = x[0];
+      d4[1] = x[1];
+      d4[2] = x[2];
+      d4[3] = x[3];
+    }
+    __syncthreads();
+    // (d, group of 8 positions), groups fastest: lanes next to each other
+    // write neighbouring slot runs of the same V column
+    for (int idx = tid; idx < 8 * p.D; idx += 256) {
+      const int g = idx & 7;
+      const int d = idx >> 3;
+      const int t0 = 8 * g;
+      const int pg0 = sh_page[t0];
+      bool whole = runs && pg0 >= 0;
+#pragma unroll
+      for (int i = 1; i < 8; ++i) whole = whole && sh_page[t0 + i] >= 0;
+      if (whole) {  // 8 aligned positions of one page: one contiguous run
+        const int pos0 = (int)(wbase + t0);
+        char* dst = p.v_cache + ((((size_t)pg0 * p.Hkv + kvh) * p.D + d) * p.page_size +
+                                 pos0 % p.page_size) * ES;
+        if (ES == 2) {
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)*(const uint16_t*)(sv + (t0 + 2 * i) * rs + d * 2) |
+                   ((uint32_t)*(const uint16_t*)(sv + (t0 + 2 * i + 1) * rs + d * 2) << 16);
+          *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+          uint32_t w[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = *(const uint32_t*)(sv + (t0 + i) * rs + d * 4);
+          *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+          *(u32x4*)(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
+        }
+      } else {
+        for (int i = 0; i < 8; ++i) {
+          const int pg = sh_page[t0 + i];
+          if (pg < 0) continue;
+          const int pos = (int)(wbase + t0 + i);
+          char* dst = p.v_cache + ((((size_t)pg * p.Hkv + kvh) * p.D + d) * p.page_size +
+                                   pos % p.page_size) * ES;
+          if (ES == 2)
+            *(uint16_t*)dst = *(const uint16_t*)(sv + (t0 + i) * rs + d * 2);
+          else
+            *(uint32_t*)dst = *(const uint32_t*)(sv + (t0 + i) * rs + d * 4);
+        }
+      }
+    }
   }
 }
 
@@ -270,6 +338,9 @@ extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_ca
   MARS_REQUIRE(n_kv_heads >= 1 && head_dim >= 8 && head_dim % 8 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(page_size >= 1 && max_pages >= 1 && num_pages >= 1, MARS_ERR_SHAPE);
   MARS_REQUIRE((long long)max_pages * page_size <= (1LL << 30), MARS_ERR_SHAPE);
+  MARS_REQUIRE(n_kv_heads <= 65535, MARS_ERR_SHAPE);
+  MARS_REQUIRE(head_dim * (dtype == MARS_BF16 ? 2 : 4) <= kAppendMaxRowBytes,
+               MARS_ERR_UNSUPPORTED);
   MARS_REQUIRE(mars_aligned16(k_rows) && mars_aligned16(v_rows) && mars_aligned16(k_cache) &&
                    mars_aligned16(v_cache) && mars_aligned16(block_table) &&
                    mars_aligned16(cache_len),
@@ -290,11 +361,12 @@ extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_ca
   a.max_pages = max_pages;
   a.num_pages = num_pages;
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((T + 63) / 64, S);
+  const dim3 grid((T + 7 + 63) / 64, S);
+  const size_t lds = 64 * ((size_t)head_dim * (dtype == MARS_BF16 ? 2 : 4) + 4);
   if (dtype == MARS_BF16)
-    hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), lds, st, a);
   else
-    hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), lds, st, a);
   hipLaunchKernelGGL(kv_append_len_kernel, dim3((S + 255) / 256), dim3(256), 0, st, a);
   return mars_launch_status();
 }

@@ -35,11 +35,13 @@ CALLS = {
     "block_decode_attention": (["attn_decode.hip", "mars_common.hpp"],
                                ["decode_split_kernel", "decode_merge_kernel"]),
     "lmhead_confidence_fused": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                [r"lmhead_gemm_kernel<\d+, true>", "conf_merge_wide_kernel"]),
+                                ["lmhead_gemm_kernel<true>", "conf_merge_wide_kernel"]),
     "lmhead_gemm_plus_confidence": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                    [r"lmhead_gemm_kernel<\d+, false>", "conf_partial_kernel",
+                                    ["lmhead_gemm_kernel<false>", "conf_partial_kernel",
                                      r"conf_merge_kernel\("]),
     "accept_commit": (["accept_commit.hip", "mars_common.hpp"], ["accept_commit_kernel"]),
+    "kv_append": (["accept_commit.hip", "mars_common.hpp"],
+                  ["kv_append_kernel", "kv_append_len_kernel"]),
     "two_stream_backward": (["attn_two_stream_bwd.hip", "attn_common.hpp", "mars_common.hpp"],
                             ["bwd_dsum_kernel", "bwd_dq_kernel", r"bwd_dkv_kernel<",
                              "bwd_dkv_reduce_kernel"]),

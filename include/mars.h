@@ -119,7 +119,9 @@ int mars_attn_causal(const void* q, const void* k, const void* v, void* o, float
  * advances by the rows that fit in the sequence's max_pages * page_size
  * capacity.
  *
- * k_rows, v_rows [S, T, n_kv_heads, head_dim] (dtype MARS_BF16 or MARS_F32);
+ * k_rows, v_rows [S, T, n_kv_heads, head_dim] (dtype MARS_BF16 or MARS_F32;
+ * head_dim a multiple of 8 with head_dim * element size <= 512 bytes, else
+ * MARS_ERR_UNSUPPORTED; S <= 65535, n_kv_heads <= 65535);
  * block_table [S, max_pages] int32; cache_len [S] int32 (updated in place).
  * Rows past the capacity or on a page id outside [0, num_pages) are skipped
  * and raise MARS_STATUS_CACHE_OVERFLOW / MARS_STATUS_BAD_PAGE in `status`

@@ -111,6 +111,7 @@ def test_causal_and_append_argument_checks():
     assert ap(d=12) == _lib.MARS_ERR_SHAPE
     assert ap(dt=5) == _lib.MARS_ERR_DTYPE
     assert ap(k=MIS) == _lib.MARS_ERR_ALIGN
+    assert ap(d=512) == _lib.MARS_ERR_UNSUPPORTED          # 1 KiB V rows exceed the staging
 
 
 def test_decode_argument_checks():

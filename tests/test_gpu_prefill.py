@@ -97,6 +97,9 @@ def ref_bits(x, dtype):
     (4, 70, 2, 64, 16, 0, 40, "bf16"),    # more than one 64-row chunk, ragged
     (2, 130, 1, 128, 64, 3, 3, "bf16"),
     (5, 1, 3, 64, 1, 0, 9, "bf16"),       # one-slot pages
+    (3, 45, 2, 64, 12, 0, 30, "bf16"),    # page size not a multiple of 8: element stores
+    (2, 200, 4, 128, 16, 5, 77, "f32"),   # 32-byte V runs, unaligned start
+    (64, 2048, 4, 128, 16, 0, 0, "bf16"), # the benchmarked prompt append
 ])
 def test_append_matches_commit_of_all_rows(S, T, Hkv, D, page, lo, hi, dtype):
     say(f"[append] S={S} T={T} Hkv={Hkv} D={D} page={page} {dtype}")
