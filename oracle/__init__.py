@@ -14,6 +14,10 @@ from .mars_oracle import (  # noqa: F401
     attn_two_stream,
     attn_two_stream_backward,
     attn_block_decode,
+    attn_block_decode_rows,
+    block_sync_advance,
+    block_sync_step,
+    block_freeze,
     gather_prefix,
     lmhead,
     confidence,

@@ -387,6 +387,116 @@ def commit(k_cache, v_cache, block_table, cache_len, k_new, v_new, n_accepted,
     return k_cache, v_cache, cache_len, commit_pos
 
 
+# ---------------------------------------------------------------------------
+# Batch-synchronous block cache                     [notes] 关键设计 4; [gist] 2D
+# ---------------------------------------------------------------------------
+#
+# Reading taken (the pages describe the policy in two sentences that are read
+# here as one rule): the persistent prefix cache grows only by whole blocks of
+# B_cache tokens, and only once every sequence of the batch has filled the
+# block; until then the tokens accepted since the last frozen block are
+# re-fed to every forward (their K/V are recomputed), ahead of the B [MASK]
+# rows. Policy "min" (the default): each step the whole batch advances by the
+# smallest accepted count of the step, capped at the block boundary. Policy
+# "wait": each sequence advances by its own count, capped at the boundary,
+# where a faster sequence waits (advances by 0) until the batch has filled the
+# block. The forward after the block fills has the B_cache block tokens as its
+# first rows; that forward freezes them into the cache.
+
+
+def attn_block_decode_rows(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_rows,
+                           page_size: int, scale: float | None = None, seqs=None):
+    """Block-decode attention with a per-sequence count of new rows.
+
+    Under the block cache a step's forward takes, for sequence s, the u_s
+    tokens not yet frozen followed by the B [MASK] rows: n_rows[s] = u_s + B
+    rows out of the R rows that q/k_new/v_new [S, R, ...] hold. Row r <
+    n_rows[s] attends to the frozen prefix (cache_len[s] rows) and to new rows
+    0..r. Returns {s: out [n_rows[s], Hq, d]} (float64).
+    """
+    S = q.shape[0]
+    if seqs is None:
+        seqs = range(S)
+    out = {}
+    for s in seqs:
+        R = int(n_rows[s])
+        if R == 0:
+            out[s] = np.zeros((0, q.shape[2], q.shape[3]))
+            continue
+        out[s] = attn_block_decode(q[s:s + 1, :R], k_new[s:s + 1, :R], v_new[s:s + 1, :R],
+                                   k_cache, v_cache, block_table[s:s + 1], cache_len[s:s + 1],
+                                   page_size, scale)[0]
+    return out
+
+
+def block_sync_advance(n_accepted, unfrozen, B_cache: int, policy: str = "min"):
+    """Tokens each sequence keeps this step under the batch-synchronous block cache.
+
+    n_accepted [S]: the step's accepted counts (accept_count); unfrozen [S]:
+    tokens accepted since the last frozen block (0..B_cache). "min": every
+    sequence keeps min over the batch of n_accepted, but no more than the room
+    left in its block; "wait": each keeps its own count, but no more than the
+    room left in its block.
+    """
+    n = np.asarray(n_accepted, dtype=np.int64)
+    room = B_cache - np.asarray(unfrozen, dtype=np.int64)
+    if policy == "min":
+        keep = np.minimum(n.min(), room)
+    elif policy == "wait":
+        keep = np.minimum(n, room)
+    else:
+        raise ValueError(f"policy must be 'min' or 'wait', got {policy!r}")
+    return keep.astype(np.int32)
+
+
+def block_sync_step(p_max, top_id, tau, unfrozen, block_tokens, B_cache: int,
+                    policy: str = "min"):
+    """Acceptance under the batch-synchronous block cache, for one step.
+
+    1. If every sequence's block was full when this step's forward ran, that
+       forward froze the block: the unfrozen count restarts at 0.
+    2. Each sequence's accepted count n_s follows the threshold rule
+       (accept_count); the batch policy turns it into the kept count a_s.
+    3. The a_s kept tokens (the first a_s top ids) join the unfrozen block.
+
+    Returns (kept [S], unfrozen [S], block_tokens [S, B_cache] padded with -1,
+    froze: bool, n_rows_next [S] = unfrozen + B).
+    """
+    S, B = np.asarray(p_max).shape
+    u = np.array(unfrozen, dtype=np.int32, copy=True)
+    toks = np.array(block_tokens, dtype=np.int32, copy=True)
+    froze = bool(np.all(u == B_cache))
+    if froze:
+        u[:] = 0
+        toks[:] = -1
+    n, _ = accept(p_max, top_id, tau)
+    keep = block_sync_advance(n, u, B_cache, policy)
+    for s in range(S):
+        for i in range(int(keep[s])):
+            toks[s, u[s] + i] = top_id[s][i]
+        u[s] += keep[s]
+    return keep, u, toks, froze, u + B
+
+
+def block_freeze(k_cache, v_cache, block_table, cache_len, k_rows, v_rows, unfrozen,
+                 B_cache: int, page_size: int):
+    """Freeze the block into the persistent cache when every sequence has filled it.
+
+    k_rows/v_rows [S, R, Hkv, d] are the K/V of a forward whose first B_cache
+    rows per sequence are the block's tokens. If every unfrozen count equals
+    B_cache, those rows are appended to the paged cache (commit of B_cache rows
+    per sequence); otherwise nothing changes. Returns (k_cache, v_cache,
+    cache_len, froze).
+    """
+    if not np.all(np.asarray(unfrozen) == B_cache):
+        return (np.array(k_cache, copy=True), np.array(v_cache, copy=True),
+                np.array(cache_len, copy=True), False)
+    S = k_rows.shape[0]
+    kc, vc, ln, _ = commit(k_cache, v_cache, block_table, cache_len, k_rows[:, :B_cache],
+                           v_rows[:, :B_cache], np.full(S, B_cache), page_size)
+    return kc, vc, ln, True
+
+
 def useful_pairs_two_stream(L: int, B: int, mask_mode: int = 0) -> int:
     """Number of visible (query, key) pairs per head under the explicit mask."""
     M = build_mask(L, B) if mask_mode == 0 else causal_mask(2 * L)

@@ -430,3 +430,152 @@ def check_lmhead_exact_integers(lmhead):
     for n in range(N):
         for vv in range(V):
             assert got[n, vv] == sum(int(h[n, k]) * int(w[vv, k]) for k in range(D))
+
+
+# ------------------------------------------------ batch-synchronous block cache ----
+
+def check_block_sync_example(step):
+    """The hand-worked four-step example, both policies."""
+    with open(os.path.join(GOLDEN, "block_sync_example.json")) as f:
+        ex = json.load(f)
+    S, B, Bc = ex["S"], ex["B"], ex["B_cache"]
+    tau = np.full(S, ex["tau"], dtype=np.float32)
+    for policy in ("min", "wait"):
+        want = ex[policy]
+        u = np.zeros(S, dtype=np.int32)
+        toks = np.full((S, Bc), -1, dtype=np.int32)
+        for t, p in enumerate(ex["p_max"]):
+            ids = np.array([[100 * t + 10 * s + i for i in range(B)] for s in range(S)],
+                           dtype=np.int32)
+            keep, u, toks, froze, nrows = step(np.array(p, dtype=np.float32), ids, tau, u, toks,
+                                               Bc, policy)
+            assert froze == want["froze"][t], (policy, t)
+            assert list(keep) == want["kept"][t], (policy, t, list(keep))
+            assert list(u) == want["unfrozen"][t], (policy, t, list(u))
+            assert toks.tolist() == want["block_tokens"][t], (policy, t)
+            assert list(nrows) == [x + B for x in want["unfrozen"][t]]
+
+
+def check_block_sync_advance_closed_forms(advance):
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        S = int(rng.integers(1, 7))
+        Bc = int(rng.integers(1, 33))
+        n = rng.integers(1, 9, size=S)
+        u = rng.integers(0, Bc + 1, size=S)
+        room = Bc - u
+        w = advance(n, u, Bc, "wait")
+        m = advance(n, u, Bc, "min")
+        # never past the block boundary, never more than accepted, never negative
+        for a in (w, m):
+            assert np.all(a >= 0) and np.all(a <= room) and np.all(a <= n)
+        # with room for every accepted token, "wait" is plain per-sequence acceptance
+        ok = room >= n
+        assert np.array_equal(w[ok], n[ok])
+        # "min" keeps the batch minimum wherever the block has room for it
+        fit = room >= n.min()
+        assert np.all(m[fit] == n.min())
+        assert np.array_equal(m[~fit], room[~fit])
+        # one sequence: the two policies coincide
+        if S == 1:
+            assert np.array_equal(w, m)
+        # equal progress stays equal under "min"
+        ue = np.full(S, u[0])
+        me = advance(n, ue, Bc, "min")
+        assert np.all(me == me[0])
+
+
+def check_block_sync_token_stream(step):
+    """Random runs: each sequence's token stream (frozen blocks, then the open
+    block) is the concatenation of its kept ids; under "min" the batch stays
+    in step; a block freezes exactly when every sequence has filled it."""
+    rng = np.random.default_rng(12)
+    for policy in ("min", "wait"):
+        for _ in range(20):
+            S = int(rng.integers(1, 6))
+            B = int(rng.integers(1, 6))
+            Bc = int(rng.integers(1, 9))
+            u = np.zeros(S, dtype=np.int32)
+            toks = np.full((S, Bc), -1, dtype=np.int32)
+            frozen = [[] for _ in range(S)]
+            kept_all = [[] for _ in range(S)]
+            for t in range(30):
+                p = rng.uniform(0, 1, size=(S, B)).astype(np.float32)
+                ids = rng.integers(0, 1000, size=(S, B)).astype(np.int32)
+                tau = np.full(S, 0.3, dtype=np.float32)
+                full_before = bool(np.all(u == Bc))
+                before = toks.copy()
+                keep, u, toks, froze, _ = step(p, ids, tau, u, toks, Bc, policy)
+                assert froze == full_before
+                if froze:
+                    for s in range(S):
+                        frozen[s] += before[s].tolist()
+                for s in range(S):
+                    kept_all[s] += ids[s, :keep[s]].tolist()
+                assert np.all(u <= Bc)
+                if policy == "min":
+                    assert np.all(u == u[0]) and np.all(keep == keep[0])
+                for s in range(S):
+                    assert frozen[s] + toks[s, :u[s]].tolist() == kept_all[s]
+                    assert np.all(toks[s, u[s]:] == -1)
+
+
+def check_block_freeze(freeze):
+    """All blocks full: rows 0..B_cache-1 land at positions cache_len + r, by a
+    plain loop over rows here; any block not full: nothing changes."""
+    rng = np.random.default_rng(13)
+    S, R, Hkv, d, ps, Bc, P = 3, 7, 2, 3, 4, 5, 12
+    kc = rng.standard_normal((P, Hkv, ps, d))
+    vc = rng.standard_normal((P, Hkv, d, ps))
+    table = rng.permutation(P).astype(np.int32).reshape(S, 4)
+    lens = np.array([0, 3, 8], dtype=np.int32)
+    kr = rng.standard_normal((S, R, Hkv, d))
+    vr = rng.standard_normal((S, R, Hkv, d))
+    k2, v2, l2, froze = freeze(kc, vc, table, lens, kr, vr, np.array([Bc, Bc, Bc]), Bc, ps)
+    assert froze and list(l2) == [Bc, 3 + Bc, 8 + Bc]
+    kw, vw = kc.copy(), vc.copy()
+    for s in range(S):
+        for r in range(Bc):
+            pos = lens[s] + r
+            kw[table[s, pos // ps], :, pos % ps, :] = kr[s, r]
+            vw[table[s, pos // ps], :, :, pos % ps] = vr[s, r]
+    np.testing.assert_array_equal(k2, kw)
+    np.testing.assert_array_equal(v2, vw)
+    k3, v3, l3, froze = freeze(kc, vc, table, lens, kr, vr, np.array([Bc, Bc - 1, Bc]), Bc, ps)
+    assert not froze and np.array_equal(l3, lens)
+    np.testing.assert_array_equal(k3, kc)
+    np.testing.assert_array_equal(v3, vc)
+
+
+def check_block_decode_rows_vs_causal(fn, attn_causal):
+    """Row r of a sequence with n frozen prefix rows is position n + r of plain
+    causal attention over prefix + new rows (the prefix written into pages by
+    a plain loop here); rows past n_rows[s] play no part."""
+    rng = np.random.default_rng(14)
+    S, R, Hq, Hkv, d, ps = 3, 6, 4, 2, 8, 4
+    lens = np.array([0, 5, 9], dtype=np.int32)
+    n_rows = np.array([6, 2, 4], dtype=np.int32)
+    max_pages = 4
+    table = rng.permutation(S * max_pages).astype(np.int32).reshape(S, max_pages)
+    kc = rng.standard_normal((S * max_pages, Hkv, ps, d))
+    vc = rng.standard_normal((S * max_pages, Hkv, d, ps))
+    q = rng.standard_normal((S, R, Hq, d))
+    kn = rng.standard_normal((S, R, Hkv, d))
+    vn = rng.standard_normal((S, R, Hkv, d))
+    kfull = [rng.standard_normal((int(lens[s]), Hkv, d)) for s in range(S)]
+    vfull = [rng.standard_normal((int(lens[s]), Hkv, d)) for s in range(S)]
+    for s in range(S):
+        for pos in range(int(lens[s])):
+            kc[table[s, pos // ps], :, pos % ps, :] = kfull[s][pos]
+            vc[table[s, pos // ps], :, :, pos % ps] = vfull[s][pos]
+    out = fn(q, kn, vn, kc, vc, table, lens, n_rows, ps)
+    for s in range(S):
+        n, Rs = int(lens[s]), int(n_rows[s])
+        assert out[s].shape == (Rs, Hq, d)
+        K = np.concatenate([kfull[s], kn[s, :Rs]])[None]
+        V = np.concatenate([vfull[s], vn[s, :Rs]])[None]
+        Q = np.concatenate([rng.standard_normal((n, Hq, d)), q[s, :Rs]])[None]
+        ref, _ = attn_causal(Q, K, V)
+        for h in range(Hq):
+            np.testing.assert_allclose(out[s][:, h], ref[(0, h)][n:], rtol=1e-12, atol=1e-12)
+

@@ -246,3 +246,86 @@ def test_causal_prefill_mutants_are_caught():
 
     assert _fails(pc.check_causal_vs_sdpa, causal_strict)
     assert _fails(pc.check_causal_vs_sdpa, causal_unscaled)
+
+
+# -- batch-synchronous block cache mutants ------------------------------------
+
+def _advance_mutant(kind):
+    def adv(n_accepted, unfrozen, B_cache, policy="min"):
+        n = np.asarray(n_accepted, dtype=np.int64)
+        room = B_cache - np.asarray(unfrozen, dtype=np.int64)
+        if kind == "room_plus_one":
+            room = room + 1
+        if policy == "min":
+            pick = n.max() if kind == "max_not_min" else n.min()
+            keep = pick if kind == "no_cap" else np.minimum(pick, room)
+            keep = np.broadcast_to(keep, n.shape)
+        else:
+            keep = n if kind == "no_cap" else np.minimum(n, room)
+        return np.asarray(keep, dtype=np.int32)
+    return adv
+
+
+@pytest.mark.parametrize("kind", ["max_not_min", "no_cap", "room_plus_one"])
+def test_block_sync_advance_mutants_are_caught(kind, monkeypatch):
+    adv = _advance_mutant(kind)
+    assert _fails(pc.check_block_sync_advance_closed_forms, adv)
+    monkeypatch.setattr(om, "block_sync_advance", adv)
+    assert _fails(pc.check_block_sync_example, om.block_sync_step)
+
+
+def _step_mutant(kind):
+    def step(p_max, top_id, tau, unfrozen, block_tokens, B_cache, policy="min"):
+        S, B = np.asarray(p_max).shape
+        u = np.array(unfrozen, dtype=np.int32, copy=True)
+        toks = np.array(block_tokens, dtype=np.int32, copy=True)
+        full = np.any(u == B_cache) if kind == "freeze_on_any" else np.all(u == B_cache)
+        froze = bool(full)
+        if froze and kind != "no_reset":
+            u[:] = 0
+            toks[:] = -1
+        n, _ = oracle.accept(p_max, top_id, tau)
+        keep = oracle.block_sync_advance(n, u, B_cache, policy)
+        for s in range(S):
+            for i in range(int(keep[s])):
+                at = i if kind == "write_at_zero" else u[s] + i
+                if at < B_cache:
+                    toks[s, at] = top_id[s][i]
+            u[s] += keep[s]
+        return keep, u, toks, froze, u + B
+    return step
+
+
+@pytest.mark.parametrize("kind", ["freeze_on_any", "no_reset", "write_at_zero"])
+def test_block_sync_step_mutants_are_caught(kind):
+    step = _step_mutant(kind)
+    assert _fails(pc.check_block_sync_example, step)
+    assert _fails(pc.check_block_sync_token_stream, step)
+
+
+def test_block_freeze_on_any_full_is_caught():
+    def freeze(k_cache, v_cache, block_table, cache_len, k_rows, v_rows, unfrozen, B_cache,
+               page_size):
+        if not np.any(np.asarray(unfrozen) == B_cache):
+            return k_cache.copy(), v_cache.copy(), cache_len.copy(), False
+        S = k_rows.shape[0]
+        kc, vc, ln, _ = oracle.commit(k_cache, v_cache, block_table, cache_len,
+                                      k_rows[:, :B_cache], v_rows[:, :B_cache],
+                                      np.full(S, B_cache), page_size)
+        return kc, vc, ln, True
+    assert _fails(pc.check_block_freeze, freeze)
+
+
+def test_block_decode_rows_mutants_are_caught():
+    def all_rows(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_rows, page_size):
+        full = oracle.attn_block_decode(q, k_new, v_new, k_cache, v_cache, block_table,
+                                        cache_len, page_size)
+        return {s: full[s] for s in range(q.shape[0])}
+
+    def short_prefix(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_rows,
+                     page_size):
+        return oracle.attn_block_decode_rows(q, k_new, v_new, k_cache, v_cache, block_table,
+                                             np.maximum(np.asarray(cache_len) - 1, 0), n_rows,
+                                             page_size)
+    assert _fails(pc.check_block_decode_rows_vs_causal, all_rows, oracle.attn_causal)
+    assert _fails(pc.check_block_decode_rows_vs_causal, short_prefix, oracle.attn_causal)

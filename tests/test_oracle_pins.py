@@ -214,3 +214,24 @@ def test_causal_prefill_matches_sdpa():
 
 def test_causal_prefill_equals_two_stream_mode1():
     pc.check_causal_equals_mode1(oracle.attn_causal, oracle.attn_two_stream)
+
+
+def test_block_sync_hand_worked_example():
+    pc.check_block_sync_example(oracle.block_sync_step)
+
+
+def test_block_sync_advance_closed_forms():
+    pc.check_block_sync_advance_closed_forms(oracle.block_sync_advance)
+
+
+def test_block_sync_token_stream():
+    pc.check_block_sync_token_stream(oracle.block_sync_step)
+
+
+def test_block_freeze():
+    pc.check_block_freeze(oracle.block_freeze)
+
+
+def test_block_decode_rows_vs_causal():
+    pc.check_block_decode_rows_vs_causal(oracle.attn_block_decode_rows, oracle.attn_causal)
+
