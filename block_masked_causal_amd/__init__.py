@@ -25,6 +25,8 @@ from .api import (  # noqa: F401
     mars_attn_two_stream_bwd,
     mars_decode_workspace_bytes,
     mars_kv_append,
+    mars_block_sync_accept,
+    mars_block_freeze,
     mars_lmhead_confidence,
     mars_lmhead_workspace_bytes,
 )

@@ -37,6 +37,13 @@ SIGNATURES = {
                                             _i32, _i32, _f, _i32, _p]),
     "mars_attn_causal": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                         _f, _p]),
+    "mars_attn_block_decode_rows": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
+                                                   _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, _f, _p, _sz, _p, _p]),
+    "mars_block_sync_accept": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
+                                              _i32, _p, _p]),
+    "mars_block_freeze": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "mars_kv_append": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _p, _p]),
     "mars_attn_two_stream_bwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,

@@ -149,11 +149,13 @@ def mars_decode_workspace_bytes(S, B, n_q_heads, n_kv_heads, head_dim, page_size
 
 
 def mars_attn_block_decode(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, *,
-                           o=None, workspace=None, status=None, softmax_scale: float = 0.0,
-                           stream=None):
+                           n_rows=None, o=None, workspace=None, status=None,
+                           softmax_scale: float = 0.0, stream=None):
     """Block-decode attention. q [S,B,Hq,d]; k_new/v_new [S,B,Hkv,d]; K cache
     [pages,Hkv,page,d]; V cache [pages,Hkv,d,page]; block_table [S,max_pages];
-    cache_len [S] (all on the GPU). Returns o [S,B,Hq,d]."""
+    cache_len [S] (all on the GPU). Returns o [S,B,Hq,d]. With n_rows (int32 [S],
+    on the GPU), sequence s uses only its first n_rows[s] rows (the block-cache
+    form); output rows past them are left as they were."""
     dt = q.dtype
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
                  (v_cache, "v_cache")):
@@ -171,13 +173,68 @@ def mars_attn_block_decode(q, k_new, v_new, k_cache, v_cache, block_table, cache
     need = mars_decode_workspace_bytes(S, B, Hq, Hkv, d, page, max_pages)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    code = _lib.lib().mars_attn_block_decode(
+    if n_rows is None:
+        code = _lib.lib().mars_attn_block_decode(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(cache_len), _ptr(o), S, B, Hq, Hkv, d, page, max_pages, num_pages,
+            _DT.get(dt, -1), float(softmax_scale), _ptr(workspace), workspace.numel(),
+            _ptr(status), _stream(stream))
+        check("mars_attn_block_decode", code)
+        return o
+    _need(n_rows, "n_rows", torch.int32, 1)
+    code = _lib.lib().mars_attn_block_decode_rows(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(cache_len), _ptr(o), S, B, Hq, Hkv, d, page, max_pages, num_pages,
+        _ptr(cache_len), _ptr(n_rows), _ptr(o), S, B, Hq, Hkv, d, page, max_pages, num_pages,
         _DT.get(dt, -1), float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(status),
         _stream(stream))
-    check("mars_attn_block_decode", code)
+    check("mars_attn_block_decode_rows", code)
     return o
+
+
+_POLICY = {"min": 0, "wait": 1}
+
+
+def mars_block_sync_accept(p_max, top_id, tau, unfrozen, block_tokens, *, policy="min",
+                           n_kept=None, n_rows=None, status=None, stream=None):
+    """Acceptance under the batch-synchronous block cache. p_max/top_id [S,B], tau [S];
+    unfrozen [S] and block_tokens [S,B_cache] (int32) are updated in place.
+    Returns (n_kept [S], n_rows [S]) (int32)."""
+    _need(p_max, "p_max", torch.float32, 2)
+    _need(top_id, "top_id", torch.int32, 2)
+    _need(tau, "tau", torch.float32, 1)
+    _need(unfrozen, "unfrozen", torch.int32, 1)
+    _need(block_tokens, "block_tokens", torch.int32, 2)
+    S, B = p_max.shape
+    Bc = block_tokens.shape[1]
+    if n_kept is None:
+        n_kept = torch.empty(S, dtype=torch.int32, device=p_max.device)
+    if n_rows is None:
+        n_rows = torch.empty(S, dtype=torch.int32, device=p_max.device)
+    code = _lib.lib().mars_block_sync_accept(
+        _ptr(p_max), _ptr(top_id), _ptr(tau), _ptr(unfrozen), _ptr(block_tokens), _ptr(n_kept),
+        _ptr(n_rows), S, B, Bc, _POLICY.get(policy, -1), _ptr(status), _stream(stream))
+    check("mars_block_sync_accept", code)
+    return n_kept, n_rows
+
+
+def mars_block_freeze(k_rows, v_rows, k_cache, v_cache, block_table, cache_len, unfrozen,
+                      B_cache: int, *, status=None, stream=None):
+    """Append rows 0..B_cache-1 of k_rows/v_rows [S,R,Hkv,d] to the paged cache if every
+    unfrozen[s] == B_cache (decided on the GPU); cache_len grows by B_cache then."""
+    dt = k_rows.dtype
+    for t, n in ((k_rows, "k_rows"), (v_rows, "v_rows"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _need(t, n, dt, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(unfrozen, "unfrozen", torch.int32, 1)
+    S, R, Hkv, d = k_rows.shape
+    num_pages, _, page, _ = k_cache.shape
+    code = _lib.lib().mars_block_freeze(
+        _ptr(k_rows), _ptr(v_rows), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(cache_len), _ptr(unfrozen), S, R, int(B_cache), Hkv, d, page,
+        block_table.shape[1], num_pages, _DT.get(dt, -1), _ptr(status), _stream(stream))
+    check("mars_block_freeze", code)
 
 
 def mars_lmhead_workspace_bytes(N, V):

@@ -37,17 +37,21 @@ struct CommitArgs {
   int S, B, Hkv, D, page_size, max_pages, num_pages;
 };
 
+// Accepted count of one row of B max-probabilities: the leading run of
+// p >= tau (a NaN compares false and stops the run), at least 1.
+__device__ __forceinline__ int accepted_count(const float* pr, int B, float tau) {
+  int n = 0;
+  while (n < B && pr[n] >= tau) ++n;
+  return n < 1 ? 1 : n;
+}
+
 template <int ES>  // element size in bytes (2 = bf16, 4 = fp32)
 __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
   __shared__ int sh_page[kMaxB];
   __shared__ int sh_len, sh_nc;
   const int s = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) {
-    const float tau = p.tau[s];
-    const float* pr = p.p_max + (size_t)s * p.B;
-    int n = 0;
-    while (n < p.B && pr[n] >= tau) ++n;  // NaN compares false
-    if (n < 1) n = 1;
+    const int n = accepted_count(p.p_max + (size_t)s * p.B, p.B, p.tau[s]);
     const int len = p.cache_len[s];
     const long long cap = (long long)p.max_pages * p.page_size;
     int nc = 0;
@@ -129,8 +133,20 @@ struct AppendArgs {
   const int32_t* block_table;
   int32_t* cache_len;
   int32_t* status;
+  const int32_t* gate;  // NULL, or: append only if gate[s] == gate_full for every s
+  int gate_full;
+  int src_rows;         // rows per sequence in k_rows / v_rows (>= T)
   int S, T, Hkv, D, page_size, max_pages, num_pages;
 };
+
+// Whether the gate holds for the whole batch (every thread of the block takes
+// part; the result is block-uniform).
+__device__ __forceinline__ bool gate_open(const AppendArgs& p) {
+  if (!p.gate) return true;
+  int ok = 1;
+  for (int i = threadIdx.x; i < p.S; i += blockDim.x) ok &= p.gate[i] == p.gate_full;
+  return __syncthreads_and(ok) != 0;
+}
 
 constexpr int kAppendMaxRowBytes = 512;  // head_dim * element size staged per V row
 
@@ -142,6 +158,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   extern __shared__ __attribute__((aligned(16))) char sv[];
   __shared__ int sh_page[64];  // page of each window position; -1 skip (flagged), -2 not ours
   const int s = blockIdx.y, tid = threadIdx.x;
+  if (!gate_open(p)) return;
   const int len = p.cache_len[s];
   if (len < 0) {
     if (blockIdx.x == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
@@ -171,7 +188,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   const int chunks = rowbytes / 16;
   // a position with a page (pg >= 0) lies in [len, min(len + T, cap)): its row
   // index and slot fit in int
-  const size_t row0 = (size_t)s * p.T;  // first row of this sequence
+  const size_t row0 = (size_t)s * p.src_rows;  // first row of this sequence
   for (int idx = tid; idx < 64 * p.Hkv * chunks; idx += 256) {
     const int ch = idx % chunks;
     const int kvh = (idx / chunks) % p.Hkv;
@@ -249,6 +266,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
 
 // After the copy (same stream): cache_len[s] advances by the rows that fit.
 __global__ __launch_bounds__(256) void kv_append_len_kernel(AppendArgs p) {
+  if (!gate_open(p)) return;
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= p.S) return;
   const int len = p.cache_len[s];
@@ -326,15 +344,18 @@ extern "C" const char* mars_strerror(int code) {
 
 extern "C" int mars_version(void) { return 100; }
 
-extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_cache,
-                              void* v_cache, const int32_t* block_table, int32_t* cache_len,
-                              int32_t S, int32_t T, int32_t n_kv_heads, int32_t head_dim,
-                              int32_t page_size, int32_t max_pages, int32_t num_pages,
-                              int32_t dtype, int32_t* status, void* stream) {
+namespace {
+// Common path of the plain append and the gated block freeze.
+int run_append(const void* k_rows, const void* v_rows, void* k_cache, void* v_cache,
+               const int32_t* block_table, int32_t* cache_len, const int32_t* gate,
+               int32_t gate_full, int32_t src_rows, int32_t S, int32_t T, int32_t n_kv_heads,
+               int32_t head_dim, int32_t page_size, int32_t max_pages, int32_t num_pages,
+               int32_t dtype, int32_t* status, void* stream) {
   MARS_REQUIRE(k_rows && v_rows && k_cache && v_cache && block_table && cache_len,
                MARS_ERR_NULL);
   MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
   MARS_REQUIRE(S >= 1 && S <= 65535 && T >= 1 && T <= (1 << 30), MARS_ERR_SHAPE);
+  MARS_REQUIRE(src_rows >= T && src_rows <= (1 << 30), MARS_ERR_SHAPE);
   MARS_REQUIRE(n_kv_heads >= 1 && head_dim >= 8 && head_dim % 8 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(page_size >= 1 && max_pages >= 1 && num_pages >= 1, MARS_ERR_SHAPE);
   MARS_REQUIRE((long long)max_pages * page_size <= (1LL << 30), MARS_ERR_SHAPE);
@@ -343,7 +364,7 @@ extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_ca
                MARS_ERR_UNSUPPORTED);
   MARS_REQUIRE(mars_aligned16(k_rows) && mars_aligned16(v_rows) && mars_aligned16(k_cache) &&
                    mars_aligned16(v_cache) && mars_aligned16(block_table) &&
-                   mars_aligned16(cache_len),
+                   mars_aligned16(cache_len) && mars_aligned16(gate),
                MARS_ERR_ALIGN);
   AppendArgs a;
   a.k_rows = (const char*)k_rows;
@@ -353,6 +374,9 @@ extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_ca
   a.block_table = block_table;
   a.cache_len = cache_len;
   a.status = status;
+  a.gate = gate;
+  a.gate_full = gate_full;
+  a.src_rows = src_rows;
   a.S = S;
   a.T = T;
   a.Hkv = n_kv_heads;
@@ -368,5 +392,111 @@ extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_ca
   else
     hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(256), lds, st, a);
   hipLaunchKernelGGL(kv_append_len_kernel, dim3((S + 255) / 256), dim3(256), 0, st, a);
+  return mars_launch_status();
+}
+}  // namespace
+
+extern "C" int mars_kv_append(const void* k_rows, const void* v_rows, void* k_cache,
+                              void* v_cache, const int32_t* block_table, int32_t* cache_len,
+                              int32_t S, int32_t T, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t max_pages, int32_t num_pages,
+                              int32_t dtype, int32_t* status, void* stream) {
+  return run_append(k_rows, v_rows, k_cache, v_cache, block_table, cache_len, nullptr, 0, T, S,
+                    T, n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype, status,
+                    stream);
+}
+
+extern "C" int mars_block_freeze(const void* k_rows, const void* v_rows, void* k_cache,
+                                 void* v_cache, const int32_t* block_table, int32_t* cache_len,
+                                 const int32_t* unfrozen, int32_t S, int32_t R, int32_t B_cache,
+                                 int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                 int32_t max_pages, int32_t num_pages, int32_t dtype,
+                                 int32_t* status, void* stream) {
+  MARS_REQUIRE(unfrozen, MARS_ERR_NULL);
+  MARS_REQUIRE(B_cache >= 1 && B_cache <= R, MARS_ERR_SHAPE);
+  return run_append(k_rows, v_rows, k_cache, v_cache, block_table, cache_len, unfrozen, B_cache,
+                    R, S, B_cache, n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype,
+                    status, stream);
+}
+
+// ------------------------------------------------ batch-synchronous accept ----
+namespace {
+
+struct SyncArgs {
+  const float* p_max;
+  const int32_t* top_id;
+  const float* tau;
+  int32_t* unfrozen;
+  int32_t* block_tokens;
+  int32_t* n_kept;
+  int32_t* n_rows;
+  int32_t* status;
+  int S, B, B_cache, policy;
+};
+
+// One workgroup for the whole batch: the block either froze for every
+// sequence or for none, and policy 0 needs the batch minimum of the accepted
+// counts, so the step is one block-wide decision.
+__global__ __launch_bounds__(1024) void block_sync_accept_kernel(SyncArgs p) {
+  __shared__ int wave_min[16];
+  const int tid = threadIdx.x;
+  int full = 1, nmin = 0x7FFFFFFF, bad = 0;
+  for (int s = tid; s < p.S; s += 1024) {
+    const int u = p.unfrozen[s];
+    bad |= u < 0 || u > p.B_cache;
+    full &= u == p.B_cache;
+    nmin = min(nmin, accepted_count(p.p_max + (size_t)s * p.B, p.B, p.tau[s]));
+  }
+  if (__syncthreads_or(bad) && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+  // the forward of this step froze the block iff every block was full
+  const bool froze = __syncthreads_and(full) != 0;
+  for (int o = 32; o > 0; o >>= 1) nmin = min(nmin, __shfl_xor(nmin, o));
+  if ((tid & 63) == 0) wave_min[tid >> 6] = nmin;
+  __syncthreads();
+  nmin = wave_min[0];
+  for (int w = 1; w < 16; ++w) nmin = min(nmin, wave_min[w]);
+  for (int s = tid; s < p.S; s += 1024) {
+    int32_t* toks = p.block_tokens + (size_t)s * p.B_cache;
+    int u = min(max(p.unfrozen[s], 0), p.B_cache);
+    if (froze) {
+      u = 0;
+      for (int i = 0; i < p.B_cache; ++i) toks[i] = -1;
+    }
+    const int n = p.policy == 0 ? nmin
+                                : accepted_count(p.p_max + (size_t)s * p.B, p.B, p.tau[s]);
+    const int keep = min(n, p.B_cache - u);
+    for (int i = 0; i < keep; ++i) toks[u + i] = p.top_id[(size_t)s * p.B + i];
+    p.unfrozen[s] = u + keep;
+    p.n_kept[s] = keep;
+    p.n_rows[s] = u + keep + p.B;
+  }
+}
+
+}  // namespace
+
+extern "C" int mars_block_sync_accept(const float* p_max, const int32_t* top_id,
+                                      const float* tau, int32_t* unfrozen,
+                                      int32_t* block_tokens, int32_t* n_kept, int32_t* n_rows,
+                                      int32_t S, int32_t B, int32_t B_cache, int32_t policy,
+                                      int32_t* status, void* stream) {
+  MARS_REQUIRE(p_max && top_id && tau && unfrozen && block_tokens && n_kept && n_rows,
+               MARS_ERR_NULL);
+  MARS_REQUIRE(S >= 1 && S <= (1 << 24) && B >= 1 && B <= kMaxB, MARS_ERR_SHAPE);
+  MARS_REQUIRE(B_cache >= 1 && B_cache <= 4096, MARS_ERR_SHAPE);
+  MARS_REQUIRE(policy == 0 || policy == 1, MARS_ERR_SHAPE);
+  SyncArgs a;
+  a.p_max = p_max;
+  a.top_id = top_id;
+  a.tau = tau;
+  a.unfrozen = unfrozen;
+  a.block_tokens = block_tokens;
+  a.n_kept = n_kept;
+  a.n_rows = n_rows;
+  a.status = status;
+  a.S = S;
+  a.B = B;
+  a.B_cache = B_cache;
+  a.policy = policy;
+  hipLaunchKernelGGL(block_sync_accept_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, a);
   return mars_launch_status();
 }

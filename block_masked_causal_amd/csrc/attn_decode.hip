@@ -34,7 +34,8 @@ inline int decode_chunk(int S, int Hkv, int nqt) {
   (void)nqt;
   return 512;
 }
-constexpr int kMaxQT = 4;    // at most 4 query tiles of 32 packed rows
+constexpr int kMaxQT = 4;    // query tiles of 32 packed rows per workgroup
+constexpr int kMaxRows = 64; // new rows per sequence
 
 struct DecodeArgs {
   const bf16_t* q;
@@ -44,11 +45,13 @@ struct DecodeArgs {
   const bf16_t* v_cache;
   const int32_t* block_table;
   const int32_t* cache_len;
+  const int32_t* n_rows;  // NULL: every sequence has B new rows; else n_rows[s] (<= B)
   bf16_t* o;
   float* part_o;   // [S][Hkv][nsplit][nrows_pad][D]
   float* part_ml;  // [S][Hkv][nsplit][nrows_pad][2]
   int32_t* status;
   int S, B, Hq, Hkv, group, page_size, max_pages, num_pages, nsplit, nrows_pad, chunk;
+  int qgroups;  // workgroups (of kMaxQT query tiles) per (chunk, KV head, sequence)
   float scale_log2;
 };
 
@@ -134,13 +137,20 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int n) {
 
 // PS = the page size when it is a compile-time constant (16 or 32, the block
 // granularities the method uses), or 0 for any other multiple of 16.
+__device__ __forceinline__ int rows_of(const DecodeArgs& p, int s) {
+  return p.n_rows ? min(max(p.n_rows[s], 0), p.B) : p.B;
+}
+
 template <int D, int PS>
 __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs p) {
-  const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int split = blockIdx.x, s = blockIdx.z;
+  const int kvh = blockIdx.y / p.qgroups, qg = blockIdx.y % p.qgroups;
   const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
   const int j = lane & 31, hf = lane >> 5;
-  const int nrows = p.group * p.B;
-  if (wq * 32 >= nrows) return;  // wave-uniform: no barriers in this kernel
+  const int rs = rows_of(p, s);  // new rows of this sequence
+  const int nrows = p.group * rs;
+  const int tq = qg * kMaxQT + wq;  // this wave's query tile
+  if (tq * 32 >= nrows) return;  // wave-uniform: no barriers in this kernel
 
   int len = p.cache_len[s];
   const int cap = p.max_pages * p.page_size;
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   const bool single = len <= p.chunk;  // the only chunk: write the final output
 
   // Packed query row of this lane: j' = r * g + head_in_group.
-  const int qi = wq * 32 + j;
+  const int qi = tq * 32 + j;
   const bool qvalid = qi < nrows;
   const int qr = qvalid ? qi / p.group : 0;
   const int qh = kvh * p.group + (qvalid ? qi % p.group : 0);
@@ -267,32 +277,37 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- the B new rows, causal among themselves (chunk 0 only) --------------
+  // ---- the new rows, causal among themselves (chunk 0 only) ----------------
   if (split == 0) {
-    bf16x8 ka[D / 16];
-    {
-      const bf16_t* kr =
-          p.k_new + (((size_t)s * p.B + (j < p.B ? j : 0)) * p.Hkv + kvh) * D + 8 * hf;
+    for (int n0 = 0; n0 < rs; n0 += 32) {
+      bf16x8 ka[D / 16];
+      {
+        const bool kv = n0 + j < rs;
+        const bf16_t* kr =
+            p.k_new + (((size_t)s * p.B + (kv ? n0 + j : 0)) * p.Hkv + kvh) * D + 8 * hf;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) ka[c] = j < p.B ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
-    }
-    bf16x8 va[D / 32][2];
+        for (int c = 0; c < D / 16; ++c) ka[c] = kv ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
+      }
+      bf16x8 va[D / 32][2];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int d = 32 * i + j;
+      for (int i = 0; i < D / 32; ++i) {
+        const int d = 32 * i + j;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
+        for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = 16 * kc + (e < 4 ? 4 * hf + e : 8 + 4 * hf + (e - 4));
-          va[i][kc][e] = key < p.B ? p.v_new[(((size_t)s * p.B + key) * p.Hkv + kvh) * D + d]
-                                   : (bf16_t)0.f;
+          for (int e = 0; e < 8; ++e) {
+            const int key = n0 + 16 * kc + (e < 4 ? 4 * hf + e : 8 + 4 * hf + (e - 4));
+            va[i][kc][e] = key < rs
+                               ? p.v_new[(((size_t)s * p.B + key) * p.Hkv + kvh) * D + d]
+                               : (bf16_t)0.f;
+          }
         }
       }
+      // new row n0 + t is visible to packed row j' iff n0 + t <= r(j'): a per-lane mask
+      const int vis = qr - n0 + 1;  // visible keys of this step
+      const uint32_t live = vis <= 0 ? 0u : vis >= 32 ? 0xFFFFFFFFu : ((1u << vis) - 1u);
+      dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
     }
-    // new row n is visible to packed row j' iff n <= r(j'): a per-lane key bitmask
-    const uint32_t live = qr + 1 >= 32 ? 0xFFFFFFFFu : ((1u << (qr + 1)) - 1u);
-    dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
   }
 
   // ---- partial result for this chunk ---------------------------------------
@@ -337,6 +352,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
   const int qi = wave % nrows;
   const int kvh = (wave / nrows) % p.Hkv;
   const int s = wave / (nrows * p.Hkv);
+  if (qi >= p.group * rows_of(p, s)) return;  // not a row of this sequence
   int len = p.cache_len[s];
   len = min(max(len, 0), p.max_pages * p.page_size);
   const int nsp = max(1, (len + p.chunk - 1) / p.chunk);
@@ -382,8 +398,10 @@ size_t decode_ws_bytes(int S, int B, int Hq, int Hkv, int D, int page_size, int 
 }
 
 bool decode_sizes_ok(int S, int B, int Hq, int Hkv, int D, int page_size, int max_pages) {
-  if (S < 1 || B < 1 || B > 32 || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
-  if ((Hq / Hkv) * B > 32 * kMaxQT) return false;
+  if (S < 1 || B < 1 || B > kMaxRows || Hq < 1 || Hkv < 1 || Hq % Hkv) return false;
+  if (Hq > 4096) return false;
+  const int nqt = ((Hq / Hkv) * B + 31) / 32;
+  if ((long long)Hkv * ((nqt + kMaxQT - 1) / kMaxQT) > 65535) return false;
   if (page_size < 16 || page_size % 16 || max_pages < 1) return false;
   if (S > 65535 || Hkv > 65535) return false;
   if ((long long)max_pages * page_size > (1LL << 30)) return false;
@@ -402,14 +420,14 @@ extern "C" size_t mars_decode_workspace_bytes(int32_t S, int32_t B, int32_t n_q_
                          nullptr);
 }
 
-extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const void* v_new,
-                                      const void* k_cache, const void* v_cache,
-                                      const int32_t* block_table, const int32_t* cache_len,
-                                      void* o, int32_t S, int32_t B, int32_t n_q_heads,
-                                      int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
-                                      int32_t max_pages, int32_t num_pages, int32_t dtype,
-                                      float softmax_scale, void* workspace,
-                                      size_t workspace_bytes, int32_t* status, void* stream) {
+namespace {
+// Common path of both entry points; n_rows NULL means B rows for every sequence.
+int run_decode(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+               const void* v_cache, const int32_t* block_table, const int32_t* cache_len,
+               const int32_t* n_rows, void* o, int32_t S, int32_t B, int32_t n_q_heads,
+               int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t max_pages,
+               int32_t num_pages, int32_t dtype, float softmax_scale, void* workspace,
+               size_t workspace_bytes, int32_t* status, void* stream) {
   MARS_REQUIRE(q && k_new && v_new && k_cache && v_cache && block_table && cache_len && o,
                MARS_ERR_NULL);
   MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
@@ -421,7 +439,7 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   MARS_REQUIRE(mars_aligned16(q) && mars_aligned16(k_new) && mars_aligned16(v_new) &&
                    mars_aligned16(k_cache) && mars_aligned16(v_cache) &&
                    mars_aligned16(block_table) && mars_aligned16(cache_len) &&
-                   mars_aligned16(o) && mars_aligned16(workspace),
+                   mars_aligned16(o) && mars_aligned16(workspace) && mars_aligned16(n_rows),
                MARS_ERR_ALIGN);
   int nsplit = 0, nrows_pad = 0;
   const size_t need = decode_ws_bytes(S, B, n_q_heads, n_kv_heads, head_dim, page_size,
@@ -436,6 +454,7 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   a.v_cache = (const bf16_t*)v_cache;
   a.block_table = block_table;
   a.cache_len = cache_len;
+  a.n_rows = n_rows;
   a.o = (bf16_t*)o;
   const size_t rows = (size_t)S * n_kv_heads * nsplit * nrows_pad;
   const size_t ob_al = (rows * head_dim * sizeof(float) + 255) & ~(size_t)255;
@@ -458,10 +477,13 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
 
   hipStream_t st = (hipStream_t)stream;
   const int nqt = nrows_pad / 32;
-  const int merge_waves = S * n_kv_heads * a.group * B;
-  dim3 grid(nsplit, n_kv_heads, S);
-  const size_t qlds = (size_t)nqt * (head_dim / 16) * 64 * 16;
-  const dim3 blk(64 * nqt);
+  const int wg_tiles = nqt < kMaxQT ? nqt : kMaxQT;
+  a.qgroups = (nqt + kMaxQT - 1) / kMaxQT;
+  const long long merge_waves = (long long)S * n_kv_heads * a.group * B;
+  MARS_REQUIRE(merge_waves < (1LL << 31), MARS_ERR_SHAPE);
+  dim3 grid(nsplit, n_kv_heads * a.qgroups, S);
+  const size_t qlds = (size_t)wg_tiles * (head_dim / 16) * 64 * 16;
+  const dim3 blk(64 * wg_tiles);
 #define MARS_DECODE_LAUNCH(D_, PS_) \
   hipLaunchKernelGGL((decode_split_kernel<D_, PS_>), grid, blk, qlds, st, a)
   if (head_dim == 128) {
@@ -477,4 +499,35 @@ extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const vo
   }
 #undef MARS_DECODE_LAUNCH
   return mars_launch_status();
+}
+}  // namespace
+
+extern "C" int mars_attn_block_decode(const void* q, const void* k_new, const void* v_new,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* cache_len,
+                                      void* o, int32_t S, int32_t B, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                      int32_t max_pages, int32_t num_pages, int32_t dtype,
+                                      float softmax_scale, void* workspace,
+                                      size_t workspace_bytes, int32_t* status, void* stream) {
+  return run_decode(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, nullptr, o, S,
+                    B, n_q_heads, n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype,
+                    softmax_scale, workspace, workspace_bytes, status, stream);
+}
+
+extern "C" int mars_attn_block_decode_rows(const void* q, const void* k_new, const void* v_new,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_table,
+                                           const int32_t* cache_len, const int32_t* n_rows,
+                                           void* o, int32_t S, int32_t R, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t head_dim,
+                                           int32_t page_size, int32_t max_pages,
+                                           int32_t num_pages, int32_t dtype,
+                                           float softmax_scale, void* workspace,
+                                           size_t workspace_bytes, int32_t* status,
+                                           void* stream) {
+  MARS_REQUIRE(n_rows, MARS_ERR_NULL);
+  return run_decode(q, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_rows, o, S, R,
+                    n_q_heads, n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype,
+                    softmax_scale, workspace, workspace_bytes, status, stream);
 }

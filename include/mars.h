@@ -10,9 +10,15 @@
  * path of that method:
  *
  *   mars_attn_two_stream    two-stream masked attention forward (training form)
+ *   mars_attn_two_stream_bwd  its dq, dk, dv (training)
+ *   mars_attn_causal        causal attention over any length (no-cache prefill)
  *   mars_attn_block_decode  B mask queries against a paged block-level KV cache
+ *   mars_attn_block_decode_rows  the same with a per-sequence row count
  *   mars_lmhead_confidence  LM-head GEMM + per-position argmax / max-softmax
  *   mars_accept_commit      left-to-right acceptance + KV commit of the prefix
+ *   mars_kv_append          paged KV append of a prompt
+ *   mars_block_sync_accept  acceptance under the batch-synchronous block cache
+ *   mars_block_freeze       freezes a full block into the paged cache
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -133,6 +139,54 @@ int mars_kv_append(const void* k_rows, const void* v_rows, void* k_cache, void* 
                    int32_t num_pages, int32_t dtype, int32_t* status, void* stream);
 
 /*
+ * Acceptance under the batch-synchronous block cache (papernotes.org notes,
+ * key design 4 (关键设计 4): the prefix cache grows by whole blocks of B_cache
+ * tokens once every sequence of the batch has filled the block; the batch
+ * advances by the smallest accepted count, faster sequences waiting at the
+ * block boundary).
+ *
+ * p_max, top_id [S, B] and tau [S] as for mars_accept_commit (the accepted
+ * count n_s is the same leading-run rule). State, device memory owned by the
+ * caller and updated in place: unfrozen [S] int32, tokens accepted since the
+ * last frozen block (0 .. B_cache; start at 0); block_tokens [S, B_cache]
+ * int32, their ids (-1 past unfrozen[s]). One step:
+ *   1. if unfrozen[s] == B_cache for every s, the forward of this step froze
+ *      the block (see mars_block_freeze): unfrozen restarts at 0 and
+ *      block_tokens at -1;
+ *   2. policy 0 (batch minimum): every sequence keeps min over s of n_s,
+ *      capped at B_cache - unfrozen[s]; policy 1 (wait at the boundary):
+ *      sequence s keeps n_s, capped the same way;
+ *   3. the kept top ids are written to block_tokens[s, unfrozen[s] ...] and
+ *      unfrozen[s] grows by the kept count.
+ * Outputs: n_kept [S] int32 (the kept count), n_rows [S] int32 =
+ * unfrozen[s] + B, the new-row count of the next forward (for
+ * mars_attn_block_decode_rows). One workgroup for the whole batch.
+ * status optional: MARS_STATUS_CACHE_OVERFLOW if an unfrozen count was outside
+ * [0, B_cache] (it is clamped). Limits: S <= 2^24, B <= 64, B_cache <= 4096.
+ */
+int mars_block_sync_accept(const float* p_max, const int32_t* top_id, const float* tau,
+                           int32_t* unfrozen, int32_t* block_tokens, int32_t* n_kept,
+                           int32_t* n_rows, int32_t S, int32_t B, int32_t B_cache,
+                           int32_t policy, int32_t* status, void* stream);
+
+/*
+ * Freeze the block into the paged cache: if unfrozen[s] == B_cache for every
+ * s (checked on the device), the first B_cache rows of k_rows / v_rows
+ * [S, R, n_kv_heads, head_dim] (the K/V of the forward whose first rows are
+ * the block's tokens) are appended at cache_len[s] as by mars_kv_append, and
+ * cache_len[s] grows by B_cache; otherwise nothing is written (notes, key
+ * design 4 (关键设计 4): the cache is frozen by one forward at the block
+ * crossing). Run it after that forward's attention and before
+ * mars_block_sync_accept of the same step, on the same stream. Same dtypes,
+ * layouts, limits and status flags as mars_kv_append; B_cache <= R.
+ */
+int mars_block_freeze(const void* k_rows, const void* v_rows, void* k_cache, void* v_cache,
+                      const int32_t* block_table, int32_t* cache_len, const int32_t* unfrozen,
+                      int32_t S, int32_t R, int32_t B_cache, int32_t n_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t max_pages, int32_t num_pages,
+                      int32_t dtype, int32_t* status, void* stream);
+
+/*
  * Two-stream MARS attention backward: dq, dk, dv of mars_attn_two_stream.
  *
  * Defines: the pages train the unchanged model on L_mask + L_AR through the
@@ -192,7 +246,7 @@ size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L, int32_
  *          max_pages * page_size (the excess is ignored), MARS_STATUS_BAD_PAGE
  *          for a table entry outside [0, num_pages) (its keys are dropped).
  * Supported: dtype MARS_BF16, head_dim 64 or 128, page_size a multiple of 16,
- *          1 <= B <= 32, (n_q_heads / n_kv_heads) * B <= 128.
+ *          1 <= B <= 64, n_q_heads <= 4096.
  */
 int mars_attn_block_decode(const void* q, const void* k_new, const void* v_new,
                            const void* k_cache, const void* v_cache,
@@ -202,6 +256,27 @@ int mars_attn_block_decode(const void* q, const void* k_new, const void* v_new,
                            int32_t num_pages, int32_t dtype, float softmax_scale,
                            void* workspace, size_t workspace_bytes, int32_t* status,
                            void* stream);
+
+/*
+ * Block-decode attention with a per-sequence number of new rows: the forward
+ * of the batch-synchronous block cache (notes, key design 4 (关键设计 4)),
+ * whose new rows for sequence s are the u_s tokens accepted since the last
+ * frozen block followed by the B [MASK] rows.
+ *
+ * As mars_attn_block_decode with B replaced by R, the row capacity of q,
+ * k_new, v_new and o ([S, R, ...]), plus n_rows [S] int32 (device): sequence s
+ * uses its first min(max(n_rows[s], 0), R) rows; row r of them attends to the
+ * cache prefix and to new rows 0 .. r. Output rows past n_rows[s] are not
+ * written. Workspace: mars_decode_workspace_bytes(S, R, ...).
+ */
+int mars_attn_block_decode_rows(const void* q, const void* k_new, const void* v_new,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* cache_len,
+                                const int32_t* n_rows, void* o, int32_t S, int32_t R,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                int32_t page_size, int32_t max_pages, int32_t num_pages,
+                                int32_t dtype, float softmax_scale, void* workspace,
+                                size_t workspace_bytes, int32_t* status, void* stream);
 
 /* Workspace bytes mars_attn_block_decode needs for these sizes (0 on bad sizes). */
 size_t mars_decode_workspace_bytes(int32_t S, int32_t B, int32_t n_q_heads, int32_t n_kv_heads,

@@ -117,8 +117,8 @@ def test_causal_and_append_argument_checks():
 def test_decode_argument_checks():
     assert dec(q=None) == _lib.MARS_ERR_NULL
     assert dec(dtype=5) == _lib.MARS_ERR_DTYPE
-    assert dec(B=33) == _lib.MARS_ERR_SHAPE
-    assert dec(Hq=28, Hkv=4, B=32) == _lib.MARS_ERR_SHAPE  # 7 * 32 packed rows > 128
+    assert dec(B=65) == _lib.MARS_ERR_SHAPE                 # more than 64 new rows
+    assert dec(Hq=6, Hkv=4) == _lib.MARS_ERR_SHAPE          # heads not a multiple
     assert dec(page=8) == _lib.MARS_ERR_SHAPE
     assert dec(page=24) == _lib.MARS_ERR_SHAPE
     assert dec(num_pages=0) == _lib.MARS_ERR_SHAPE
@@ -130,6 +130,35 @@ def test_decode_argument_checks():
     assert dec(ws_bytes=need - 1) == _lib.MARS_ERR_WORKSPACE
     assert dec(ws=None) == _lib.MARS_ERR_WORKSPACE
     assert mars.mars_decode_workspace_bytes(2, 4, 4, 2, 96, 16, 4) == 0
+
+
+def test_block_cache_argument_checks():
+    L_ = mars.lib()
+    rows = lambda **kw: L_.mars_attn_block_decode_rows(
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("n_rows", FAKE), FAKE, 2,
+        kw.get("R", 8), 4, 2, 128, 16, 4, 8, 1, 0.0, FAKE, kw.get("ws_bytes", 1 << 30), None,
+        None)
+    assert rows(n_rows=None) == _lib.MARS_ERR_NULL
+    assert rows(R=65) == _lib.MARS_ERR_SHAPE
+    assert rows(n_rows=MIS) == _lib.MARS_ERR_ALIGN
+    assert rows(ws_bytes=16) == _lib.MARS_ERR_WORKSPACE
+    acc = lambda **kw: L_.mars_block_sync_accept(
+        kw.get("p", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("S", 4), kw.get("B", 4),
+        kw.get("Bc", 16), kw.get("policy", 0), None, None)
+    assert acc(p=None) == _lib.MARS_ERR_NULL
+    assert acc(B=65) == _lib.MARS_ERR_SHAPE
+    assert acc(Bc=0) == _lib.MARS_ERR_SHAPE
+    assert acc(policy=2) == _lib.MARS_ERR_SHAPE
+    assert acc(S=0) == _lib.MARS_ERR_SHAPE
+    frz = lambda **kw: L_.mars_block_freeze(
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("u", FAKE), 2, kw.get("R", 20),
+        kw.get("Bc", 16), 2, kw.get("d", 64), 16, 4, 8, kw.get("dt", 1), None, None)
+    assert frz(u=None) == _lib.MARS_ERR_NULL
+    assert frz(Bc=21) == _lib.MARS_ERR_SHAPE                # block larger than the rows
+    assert frz(Bc=0) == _lib.MARS_ERR_SHAPE
+    assert frz(dt=3) == _lib.MARS_ERR_DTYPE
+    assert frz(d=1024) == _lib.MARS_ERR_UNSUPPORTED
+    assert frz(u=MIS) == _lib.MARS_ERR_ALIGN
 
 
 def test_decode_workspace_grows_with_capacity():
