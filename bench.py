@@ -21,7 +21,8 @@ kernels run on. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), the no-cache causal prefill and the paged KV
-append, and the CPU oracle timed on a bounded sample.
+append, a 64-step batch-synchronous block-cache loop under both batch
+policies, and the CPU oracle timed on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
 
 `roofline.traffic` is the HBM bytes one launch moves, from two rocprofv3
@@ -55,6 +56,8 @@ DEC = dict(S=64, B=4, Hq=28, Hkv=4, d=128, lo=512, hi=4096, page=16)
 LM = dict(D=3584, V=152064)
 PRE = dict(batch=8, T=4096 + 4, Hq=14, Hkv=2, d=64)              # no-cache prefill, 0.5B
 APP = dict(S=64, T=2048, Hkv=4, d=128, page=16)                  # prompt KV append, 7B
+BCL = dict(S=16, B=4, B_cache=16, Hq=28, Hkv=4, d=128, lo=512, hi=2048, page=16, steps=64,
+           tau=0.95)                                               # block cache, 7B, batch 16
 LOOP = dict(S=256, B=8, Hq=28, Hkv=4, d=128, lo=128, hi=2048, page=16, steps=64, switch=32)
 
 
@@ -440,6 +443,10 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
 
     # batched decode loop with a live tau switch
     out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
+
+    # the batch-synchronous block cache, both batch policies
+    out["block_cache_loop"] = {pol: block_cache_loop(mars, synth, torch, dev, pol)
+                               for pol in ("min", "wait")}
     return out
 
 
@@ -542,6 +549,75 @@ def causal_prefill(mars, synth, torch, dev, traffic):
     del KR, VR, kc, vc, bt, cl
     torch.cuda.empty_cache()
     return res
+
+
+def block_cache_loop(mars, synth, torch, dev, policy):
+    """The batch-synchronous block cache at the 7B shape: per step, block-decode
+    attention over each sequence's unfrozen tokens + B masks, the block freeze,
+    the confidence of the B mask rows and the batch-synchronous acceptance.
+    The synthetic logits (one planted peak per row) and the step's Q/K/V rows
+    are written outside the timed events."""
+    c = BCL
+    R = c["B_cache"] + c["B"]
+    log(f"block-cache loop ({policy}): S={c['S']} B={c['B']} B_cache={c['B_cache']}, "
+        f"{c['steps']} steps, tau {c['tau']}")
+    di = synth.decode_inputs(1010, c["S"], R, c["Hq"], c["Hkv"], c["d"], c["lo"], c["hi"],
+                             c["page"], extra_capacity=c["B"] * c["steps"] + c["B_cache"])
+    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+    bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
+    del di
+    N = c["S"] * c["B"]
+    pool = synth.PeakedLogitsPool(1010, N, LM["V"], taus=(c["tau"],))
+    pool_dev = torch.from_numpy(pool.pool).to(dev)
+    logits = torch.empty_like(pool_dev)
+    rows = torch.arange(N, device=dev)
+    tau = torch.full((c["S"],), c["tau"], dtype=torch.float32, device=dev)
+    unfrozen = torch.zeros(c["S"], dtype=torch.int32, device=dev)
+    toks = torch.full((c["S"], c["B_cache"]), -1, dtype=torch.int32, device=dev)
+    n_rows = torch.full((c["S"],), c["B"], dtype=torch.int32, device=dev)
+    kept = torch.empty(c["S"], dtype=torch.int32, device=dev)
+    o = torch.empty((c["S"], R, c["Hq"], c["d"]), dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(mars.mars_decode_workspace_bytes(c["S"], R, c["Hq"], c["Hkv"], c["d"],
+                                                       c["page"], bt.shape[1]),
+                      dtype=torch.uint8, device=dev)
+    lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8, device=dev)
+    top = torch.empty(N, dtype=torch.int32, device=dev)
+    pm = torch.empty(N, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    total_ms, kept_total, frozen = 0.0, 0, 0
+    len0 = int(cl.sum().item())
+    for step in range(c["steps"]):
+        q, kn, vn = synth.decode_step_tensors(1010, step, c["S"], R, c["Hq"], c["Hkv"], c["d"])
+        Q, KN, VN = to_dev(q, dev), to_dev(kn, dev), to_dev(vn, dev)
+        ids, peak, _ = pool.peaks(step)
+        logits.copy_(pool_dev)
+        logits[rows, torch.from_numpy(ids).to(dev)] = torch.from_numpy(peak).to(dev)
+        a, b = ev(), ev()
+        a.record()
+        mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, n_rows=n_rows, o=o, workspace=dws,
+                                    status=status)
+        mars.mars_block_freeze(KN, VN, kc, vc, bt, cl, unfrozen, c["B_cache"], status=status)
+        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws,
+                                    status=status)
+        mars.mars_block_sync_accept(pm.view(c["S"], c["B"]), top.view(c["S"], c["B"]), tau,
+                                    unfrozen, toks, policy=policy, n_kept=kept, n_rows=n_rows,
+                                    status=status)
+        b.record()
+        torch.cuda.synchronize()
+        total_ms += a.elapsed_time(b)
+        kept_total += int(kept.sum().item())
+    frozen = (int(cl.sum().item()) - len0) // (c["B_cache"] * c["S"])
+    return {
+        "config": dict(c, policy=policy),
+        "accepted_tokens_per_s": round(kept_total / (total_ms * 1e-3), 1),
+        "ms_per_step": round(total_ms / c["steps"], 4),
+        "mean_kept_per_seq_per_step": round(kept_total / (c["steps"] * c["S"]), 4),
+        "blocks_frozen": frozen,
+        "status_flags": int(status.item()),
+        "note": "per step: block-decode attention over unfrozen + B mask rows, block freeze, "
+                "confidence over S*B x 152064 fp32 logits, batch-synchronous acceptance",
+    }
 
 
 def decode_loop(mars, synth, torch, dev, status):

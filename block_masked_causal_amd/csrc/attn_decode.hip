@@ -17,7 +17,12 @@
 // The cache of one sequence is cut into 512-key chunks (split-K). Each workgroup handles one (chunk, KV head, sequence) and writes an
 // unnormalised partial (O, running max, running sum); a merge kernel combines
 // the chunks. A sequence that fits in one chunk is written out directly.
-// Chunk 0 also handles the B new rows (causal among themselves).
+// Chunk 0 also handles the new rows (causal among themselves). Their number
+// may differ per sequence (at most 64): under the batch-synchronous block
+// cache (notes, key design 4) a sequence's new rows are its tokens accepted
+// since the last frozen block followed by the B masks. Packed rows beyond
+// kMaxQT query tiles go to further workgroups of the same (chunk, KV head,
+// sequence), which read the same K/V.
 #include "mars_common.hpp"
 
 using namespace mars;

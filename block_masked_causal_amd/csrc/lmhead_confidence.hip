@@ -9,8 +9,10 @@
 //  * lmhead_gemm_kernel: logits[N, V] = hidden[N, D] . W[V, D]^T on the
 //    32x32x16 bf16 MFMA with fp32 accumulation. A 512-thread workgroup owns
 //    all of up to 256 rows and 256 vocabulary entries, so each weight row is
-//    read from HBM once; K is staged through double-buffered LDS 64 (or 32)
-//    at a time, with the weight loads issued two stages ahead.
+//    read from HBM once; K is staged 32 at a time through a 4-stage LDS ring
+//    filled by direct global->LDS loads (three stages in flight). With
+//    logits == NULL the epilogue reduces the tile to per-row confidence
+//    partials instead of storing logits (conf_merge_wide_kernel finishes).
 //  * conf_partial_kernel: a row is cut into chunks; each workgroup streams one
 //    chunk once, keeping per-thread (max, first argmax, sum of exp relative to
 //    the running max), and reduces them in the workgroup (sums in fp64).
