@@ -197,3 +197,64 @@ def test_block_cache_loop_matches_oracle(policy):
     assert froze_seen >= 1
     assert np.array_equal(cache_bits(kc), synth.bf16_round(rkc).view(np.int16))
     assert np.array_equal(cache_bits(vc), synth.bf16_round(rvc).view(np.int16))
+
+
+def test_decode_rows_counts_are_clamped():
+    """n_rows outside [0, R] is clamped: above R uses all R rows, below 0 none."""
+    say("[block rows] n_rows clamped to [0, R]")
+    S, R, Hq, Hkv, D, page = 3, 6, 4, 2, 64, 16
+    d = synth.decode_inputs(4600, S, R, Hq, Hkv, D, 5, 40, page)
+    args = [to_dev(d.q), to_dev(d.k_new), to_dev(d.v_new), to_dev(d.k_cache), to_dev(d.v_cache),
+            to_dev(d.block_table), to_dev(d.cache_len)]
+    o = torch.full((S, R, Hq, D), 3.0, dtype=torch.bfloat16, device=DEV)
+    mars.mars_attn_block_decode(*args, n_rows=to_dev(np.array([R + 5, -2, 1 << 20], np.int32)),
+                                o=o)
+    full = mars.mars_attn_block_decode(*args)
+    torch.cuda.synchronize()
+    ob, fb = bf16_bits(o), bf16_bits(full)
+    assert np.array_equal(ob[0], fb[0]) and np.array_equal(ob[2], fb[2])
+    assert np.all(o[1].float().cpu().numpy() == 3.0)
+
+
+def test_block_sync_accept_flags_out_of_range_state():
+    """An unfrozen count outside [0, B_cache] raises the status flag and is
+    treated as its clamp."""
+    say("[block accept] corrupt unfrozen counts are flagged and clamped")
+    S, B, Bc = 3, 4, 8
+    p = np.full((S, B), 0.95, dtype=np.float32)
+    ids = np.arange(S * B, dtype=np.int32).reshape(S, B)
+    tau = np.full(S, 0.5, dtype=np.float32)
+    u = np.array([-3, 2, 11], dtype=np.int32)
+    toks = np.full((S, Bc), -1, dtype=np.int32)
+    toks[1, :2] = [7, 8]
+    toks[2, :] = np.arange(Bc)
+    ud, td = to_dev(u), to_dev(toks)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kept, nrows = mars.mars_block_sync_accept(to_dev(p), to_dev(ids), to_dev(tau), ud, td,
+                                              policy="wait", status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & mars.STATUS_CACHE_OVERFLOW
+    rk, ru, rt, _, rn = oracle.block_sync_step(p, ids, tau, np.clip(u, 0, Bc), toks, Bc, "wait")
+    assert np.array_equal(kept.cpu().numpy(), rk)
+    assert np.array_equal(ud.cpu().numpy(), ru)
+    assert np.array_equal(td.cpu().numpy(), rt)
+    assert np.array_equal(nrows.cpu().numpy(), rn)
+
+
+def test_block_freeze_flags_overflow_and_keeps_what_fits():
+    say("[block freeze] a sequence without room: flagged, rows that fit are frozen")
+    S, R, Bc, Hkv, D, page = 3, 12, 8, 2, 64, 16
+    d = synth.decode_inputs(4700, S, R, 2 * Hkv, Hkv, D, 20, 20, page, extra_capacity=Bc)
+    cap = d.max_pages * page
+    lens = np.array([20, cap - 3, 20], dtype=np.int32)   # sequence 1 has room for 3 rows
+    kc, vc, cl = to_dev(d.k_cache), to_dev(d.v_cache), to_dev(lens)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mars.mars_block_freeze(to_dev(d.k_new), to_dev(d.v_new), kc, vc, to_dev(d.block_table), cl,
+                           to_dev(np.full(S, Bc, np.int32)), Bc, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & mars.STATUS_CACHE_OVERFLOW
+    assert list(cl.cpu().numpy()) == [20 + Bc, cap, 20 + Bc]
+    rk, rv, _, _ = oracle.commit(d.k_cache.f32, d.v_cache.f32, d.block_table, lens, d.k_new.f32,
+                                 d.v_new.f32, np.array([Bc, 3, Bc]), page)
+    assert np.array_equal(cache_bits(kc), synth.bf16_round(rk).view(np.int16))
+    assert np.array_equal(cache_bits(vc), synth.bf16_round(rv).view(np.int16))
