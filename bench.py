@@ -21,8 +21,9 @@ kernels run on. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), the no-cache causal prefill and the paged KV
-append, a 64-step batch-synchronous block-cache loop under both batch
-policies, and the CPU oracle timed on a bounded sample.
+append, a 64-step decode loop at the 7B shape under the batch-synchronous
+block cache (both batch policies), per-token commit and one-token AR, and
+the CPU oracle timed on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
 
 `roofline.traffic` is the HBM bytes one launch moves, from two rocprofv3
@@ -444,9 +445,15 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
     # batched decode loop with a live tau switch
     out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
 
-    # the batch-synchronous block cache, both batch policies
-    out["block_cache_loop"] = {pol: block_cache_loop(mars, synth, torch, dev, pol)
-                               for pol in ("min", "wait")}
+    # the batch-synchronous block cache (both batch policies) beside per-token
+    # commit and one-token-per-step AR decoding, on the same confidence draws
+    pol = {p_: block_cache_loop(mars, synth, torch, dev, p_)
+           for p_ in ("min", "wait", "per_token", "ar")}
+    pol["note"] = ("per step: decode attention, confidence over the step's rows x 152064 "
+                   "fp32 logits, acceptance (+ block freeze or commit); the model layers "
+                   "around attention are not part of this path, so these are not the "
+                   "pages' end-to-end wall-clock ratios")
+    out["decode_policies"] = pol
     return out
 
 
@@ -552,21 +559,29 @@ def causal_prefill(mars, synth, torch, dev, traffic):
 
 
 def block_cache_loop(mars, synth, torch, dev, policy):
-    """The batch-synchronous block cache at the 7B shape: per step, block-decode
-    attention over each sequence's unfrozen tokens + B masks, the block freeze,
-    the confidence of the B mask rows and the batch-synchronous acceptance.
-    The synthetic logits (one planted peak per row) and the step's Q/K/V rows
-    are written outside the timed events."""
+    """Decode loop at the 7B shape under one commit policy; the same seeded
+    confidence draws (planted-peak logits) drive every policy.
+
+    "min" / "wait": the batch-synchronous block cache. Per step: block-decode
+    attention over each sequence's unfrozen tokens + B masks, the block
+    freeze, the confidence of the B mask rows, the batch-synchronous
+    acceptance. "per_token": every accepted token is committed at once
+    (block decode over B rows, confidence, accept + commit). "ar": one token
+    per step (B = 1) with a KV cache. The logits and the step's Q/K/V rows
+    are written outside the timed events.
+    """
     c = BCL
-    R = c["B_cache"] + c["B"]
-    log(f"block-cache loop ({policy}): S={c['S']} B={c['B']} B_cache={c['B_cache']}, "
+    block = policy in ("min", "wait")
+    Bm = 1 if policy == "ar" else c["B"]
+    R = c["B_cache"] + Bm if block else Bm
+    log(f"decode policy {policy}: S={c['S']} B={Bm} B_cache={c['B_cache']}, "
         f"{c['steps']} steps, tau {c['tau']}")
     di = synth.decode_inputs(1010, c["S"], R, c["Hq"], c["Hkv"], c["d"], c["lo"], c["hi"],
                              c["page"], extra_capacity=c["B"] * c["steps"] + c["B_cache"])
     kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
     bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
     del di
-    N = c["S"] * c["B"]
+    N = c["S"] * Bm
     pool = synth.PeakedLogitsPool(1010, N, LM["V"], taus=(c["tau"],))
     pool_dev = torch.from_numpy(pool.pool).to(dev)
     logits = torch.empty_like(pool_dev)
@@ -574,8 +589,10 @@ def block_cache_loop(mars, synth, torch, dev, policy):
     tau = torch.full((c["S"],), c["tau"], dtype=torch.float32, device=dev)
     unfrozen = torch.zeros(c["S"], dtype=torch.int32, device=dev)
     toks = torch.full((c["S"], c["B_cache"]), -1, dtype=torch.int32, device=dev)
-    n_rows = torch.full((c["S"],), c["B"], dtype=torch.int32, device=dev)
+    n_rows = torch.full((c["S"],), Bm, dtype=torch.int32, device=dev)
     kept = torch.empty(c["S"], dtype=torch.int32, device=dev)
+    acc_ids = torch.empty((c["S"], Bm), dtype=torch.int32, device=dev)
+    cpos = torch.empty((c["S"], Bm), dtype=torch.int32, device=dev)
     o = torch.empty((c["S"], R, c["Hq"], c["d"]), dtype=torch.bfloat16, device=dev)
     dws = torch.empty(mars.mars_decode_workspace_bytes(c["S"], R, c["Hq"], c["Hkv"], c["d"],
                                                        c["page"], bt.shape[1]),
@@ -585,7 +602,7 @@ def block_cache_loop(mars, synth, torch, dev, policy):
     pm = torch.empty(N, dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    total_ms, kept_total, frozen = 0.0, 0, 0
+    total_ms, kept_total = 0.0, 0
     len0 = int(cl.sum().item())
     for step in range(c["steps"]):
         q, kn, vn = synth.decode_step_tensors(1010, step, c["S"], R, c["Hq"], c["Hkv"], c["d"])
@@ -595,29 +612,38 @@ def block_cache_loop(mars, synth, torch, dev, policy):
         logits[rows, torch.from_numpy(ids).to(dev)] = torch.from_numpy(peak).to(dev)
         a, b = ev(), ev()
         a.record()
-        mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, n_rows=n_rows, o=o, workspace=dws,
-                                    status=status)
-        mars.mars_block_freeze(KN, VN, kc, vc, bt, cl, unfrozen, c["B_cache"], status=status)
+        if block:
+            mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, n_rows=n_rows, o=o,
+                                        workspace=dws, status=status)
+            mars.mars_block_freeze(KN, VN, kc, vc, bt, cl, unfrozen, c["B_cache"],
+                                   status=status)
+        else:
+            mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, o=o, workspace=dws,
+                                        status=status)
         mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws,
                                     status=status)
-        mars.mars_block_sync_accept(pm.view(c["S"], c["B"]), top.view(c["S"], c["B"]), tau,
-                                    unfrozen, toks, policy=policy, n_kept=kept, n_rows=n_rows,
-                                    status=status)
+        if block:
+            mars.mars_block_sync_accept(pm.view(c["S"], Bm), top.view(c["S"], Bm), tau,
+                                        unfrozen, toks, policy=policy, n_kept=kept,
+                                        n_rows=n_rows, status=status)
+        else:
+            mars.mars_accept_commit(pm.view(c["S"], Bm), top.view(c["S"], Bm), tau, KN, VN, kc,
+                                    vc, bt, cl, n_accepted=kept, accepted_ids=acc_ids,
+                                    commit_pos=cpos, status=status)
         b.record()
         torch.cuda.synchronize()
         total_ms += a.elapsed_time(b)
         kept_total += int(kept.sum().item())
-    frozen = (int(cl.sum().item()) - len0) // (c["B_cache"] * c["S"])
-    return {
-        "config": dict(c, policy=policy),
+    res = {
+        "config": dict(c, policy=policy, B=Bm),
         "accepted_tokens_per_s": round(kept_total / (total_ms * 1e-3), 1),
         "ms_per_step": round(total_ms / c["steps"], 4),
         "mean_kept_per_seq_per_step": round(kept_total / (c["steps"] * c["S"]), 4),
-        "blocks_frozen": frozen,
         "status_flags": int(status.item()),
-        "note": "per step: block-decode attention over unfrozen + B mask rows, block freeze, "
-                "confidence over S*B x 152064 fp32 logits, batch-synchronous acceptance",
     }
+    if block:
+        res["blocks_frozen"] = (int(cl.sum().item()) - len0) // (c["B_cache"] * c["S"])
+    return res
 
 
 def decode_loop(mars, synth, torch, dev, status):
