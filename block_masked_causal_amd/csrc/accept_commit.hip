@@ -7,11 +7,13 @@
 // below tau, and always accept the first. The accepted tokens then join the
 // persistent prefix KV cache (notes, key design 4 / 关键设计 4).
 //
-// One workgroup per sequence. Lane 0 makes the (tiny, sequential) decision and
-// resolves the destination page of each committed row; then the whole
-// workgroup copies the accepted rows: K rows as 16-byte vectors into the
-// [page][head][slot][d] pages, V rows element-wise into the transposed
-// [page][head][d][slot] pages, with consecutive threads on consecutive slots.
+// One workgroup per sequence. Wave 0 takes the decision with one lane per
+// position (a ballot of p >= tau; the accepted count is the run of passing
+// positions from the first) and resolves the destination page of each
+// committed row in parallel; then the whole workgroup copies the accepted
+// rows: K rows as 16-byte vectors into the [page][head][slot][d] pages, V rows
+// element-wise into the transposed [page][head][d][slot] pages, with
+// consecutive threads on consecutive slots.
 #include "mars_common.hpp"
 
 using namespace mars;
@@ -50,34 +52,41 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
   __shared__ int sh_page[kMaxB];
   __shared__ int sh_len, sh_nc;
   const int s = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) {
-    const int n = accepted_count(p.p_max + (size_t)s * p.B, p.B, p.tau[s]);
+  if (tid < 64) {
+    // Wave 0, lane r = position r: the accepted count is the run of set bits
+    // at the bottom of the ballot of p >= tau (a NaN compares false), at
+    // least 1; then each accepted row resolves its page in parallel and the
+    // commit keeps the rows before the first one that cannot be placed.
+    const int r = tid;
+    const bool pass = r < p.B && p.p_max[(size_t)s * p.B + r] >= p.tau[s];
+    const uint64_t pm = __ballot(pass);
+    const int n = max(pm == ~0ull ? 64 : __builtin_ctzll(~pm), 1);
     const int len = p.cache_len[s];
     const long long cap = (long long)p.max_pages * p.page_size;
-    int nc = 0;
-    int32_t flags = 0;
-    for (int r = 0; r < n; ++r) {
+    int pg = -1;
+    int32_t flag = 0;
+    if (r < n) {
       const long long pos = (long long)len + r;
       if (len < 0 || pos >= cap) {
-        flags |= MARS_STATUS_CACHE_OVERFLOW;
-        break;
+        flag = MARS_STATUS_CACHE_OVERFLOW;
+      } else {
+        pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
+        if (pg < 0 || pg >= p.num_pages) flag = MARS_STATUS_BAD_PAGE;
       }
-      const int pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
-      if (pg < 0 || pg >= p.num_pages) {
-        flags |= MARS_STATUS_BAD_PAGE;
-        break;
-      }
-      sh_page[r] = pg;
-      ++nc;
     }
-    if (flags) status_or(p.status, flags);
-    p.n_accepted[s] = n;
-    for (int r = 0; r < p.B; ++r) {
+    const uint64_t gm = __ballot(r < n && flag == 0);
+    const int nc = gm == ~0ull ? 64 : __builtin_ctzll(~gm);  // rows placed
+    if (r == nc && r < n) status_or(p.status, flag);          // the first failure
+    if (r < nc) sh_page[r] = pg;
+    if (r < p.B) {
       p.accepted_ids[(size_t)s * p.B + r] = r < n ? p.top_id[(size_t)s * p.B + r] : -1;
       p.commit_pos[(size_t)s * p.B + r] = r < nc ? len + r : -1;
     }
-    sh_len = len;
-    sh_nc = nc;
+    if (r == 0) {
+      p.n_accepted[s] = n;
+      sh_len = len;
+      sh_nc = nc;
+    }
   }
   __syncthreads();
   const int len = sh_len, nc = sh_nc;
@@ -116,15 +125,15 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
 
 // ---------------------------------------------------------------- append ----
 // Append T rows per sequence to the paged cache (the prefill's K/V): row r of
-// sequence s goes to position cache_len[s] + r. Grid (ceil((T + 7) / 64), S):
-// workgroup x of sequence s owns the 64 cache positions starting at
-// (cache_len[s] rounded down to a multiple of 8) + 64 x, so that every group of
-// 8 positions it writes is 8-aligned. It resolves the page of each position in
-// parallel, copies K rows straight through ([page][head][slot][d] keeps a row
-// contiguous), and stages V one head at a time in LDS so that it can write
-// the transposed V layout ([page][head][d][slot]) as runs of 8 slots, one
-// 16-byte store per run of 8 bf16 values, where the page size is a multiple
-// of 8; other page sizes take element stores.
+// sequence s goes to position cache_len[s] + r. Grid (ceil((T + 7) / 64), S,
+// KV heads): workgroup (x, s, h) owns head h of the 64 cache positions
+// starting at (cache_len[s] rounded down to a multiple of 8) + 64 x, so that
+// every group of 8 positions it writes is 8-aligned. It resolves the page of
+// each position in parallel, copies the K rows straight through
+// ([page][head][slot][d] keeps a row contiguous), and stages the V rows in LDS
+// so that it can write the transposed V layout ([page][head][d][slot]) as runs
+// of 8 slots, one 16-byte store per run of 8 bf16 values, where the page size
+// is a multiple of 8; other page sizes take element stores.
 struct AppendArgs {
   const char* k_rows;
   const char* v_rows;
@@ -157,11 +166,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   // (dynamic LDS of 64 * (head_dim * ES + 4) bytes)
   extern __shared__ __attribute__((aligned(16))) char sv[];
   __shared__ int sh_page[64];  // page of each window position; -1 skip (flagged), -2 not ours
-  const int s = blockIdx.y, tid = threadIdx.x;
+  const int s = blockIdx.y, kvh = blockIdx.z, tid = threadIdx.x;
   if (!gate_open(p)) return;
   const int len = p.cache_len[s];
   if (len < 0) {
-    if (blockIdx.x == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+    if (blockIdx.x == 0 && kvh == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
     return;
   }
   const long long wbase = (long long)(len & ~7) + 64LL * blockIdx.x;
@@ -171,12 +180,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
     int pg = -2;
     if (pos >= len && pos < (long long)len + p.T) {
       if (pos >= cap) {
-        status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+        if (kvh == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
         pg = -1;
       } else {
         pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
         if (pg < 0 || pg >= p.num_pages) {
-          status_or(p.status, MARS_STATUS_BAD_PAGE);
+          if (kvh == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
           pg = -1;
         }
       }
@@ -189,10 +198,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   // a position with a page (pg >= 0) lies in [len, min(len + T, cap)): its row
   // index and slot fit in int
   const size_t row0 = (size_t)s * p.src_rows;  // first row of this sequence
-  for (int idx = tid; idx < 64 * p.Hkv * chunks; idx += 256) {
+  for (int idx = tid; idx < 64 * chunks; idx += 256) {
     const int ch = idx % chunks;
-    const int kvh = (idx / chunks) % p.Hkv;
-    const int t = idx / (chunks * p.Hkv);
+    const int t = idx / chunks;
     const int pg = sh_page[t];
     if (pg < 0) continue;
     const int pos = (int)(wbase + t);
@@ -203,8 +211,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   }
   const int rs = rowbytes + 4;
   const bool runs = (p.page_size % 8) == 0;
-  for (int kvh = 0; kvh < p.Hkv; ++kvh) {
-    __syncthreads();  // the previous head's column reads are done
+  {
     for (int idx = tid; idx < 64 * chunks; idx += 256) {
       const int ch = idx % chunks;
       const int t = idx / chunks;
@@ -385,7 +392,7 @@ int run_append(const void* k_rows, const void* v_rows, void* k_cache, void* v_ca
   a.max_pages = max_pages;
   a.num_pages = num_pages;
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((T + 7 + 63) / 64, S);
+  const dim3 grid((T + 7 + 63) / 64, S, n_kv_heads);
   const size_t lds = 64 * ((size_t)head_dim * (dtype == MARS_BF16 ? 2 : 4) + 4);
   if (dtype == MARS_BF16)
     hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), lds, st, a);
