@@ -109,6 +109,18 @@ __device__ __forceinline__ void dec_softmax(f32x16& sc, bf16x8 (&pb)[2], f32x16 
     pb[r >> 3][r & 7] = (bf16_t)e;
   }
   l += rsum;
+  // pb[kc] holds keys 16kc + 4hf + (0..3) and 16kc + 8 + 4hf + (0..3). The two
+  // wave halves swap dwords 2-3 (half 0) with dwords 0-1 (half 1), so that half
+  // hf holds keys 16kc + 8hf + (0..7) in order: the V^T operand of those keys
+  // is then one 16-byte read of consecutive slots.
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const u32x4 w = __builtin_bit_cast(u32x4, pb[kc]);
+    const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    const u32x4 x = {a[0], b[0], a[1], b[1]};
+    pb[kc] = __builtin_bit_cast(bf16x8, x);
+  }
 }
 
 template <int D>
@@ -131,13 +143,12 @@ __device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x
   dec_pv<D>(va, pb, o);
 }
 
-// Keeps the first n (0..4) bf16 values of a 4-key V group, zeroes the rest.
-__device__ __forceinline__ u32x2 keep_first(u32x2 v, int n) {
-  if (n >= 4) return v;
-  if (n <= 0) return u32x2{};
-  if (n == 1) return u32x2{v[0] & 0xFFFFu, 0u};
-  if (n == 2) return u32x2{v[0], 0u};
-  return u32x2{v[0], v[1] & 0xFFFFu};
+// Keeps the first n (0..8) bf16 values of an 8-key V group, zeroes the rest.
+__device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int n) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e >= n) v[e] = (bf16_t)0.f;
+  return v;
 }
 
 // PS = the page size when it is a compile-time constant (16 or 32, the block
@@ -217,41 +228,29 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
   };
-  // V group of 4 keys starting at step offset 16kc + 4hf (+ 8 for the second)
-  auto v_page = [&](int c0, int kc, int second) {
-    return __shfl(mypage, (c0 + 16 * kc + 8 * second + 4 * hf) / ps - pg0);
+  // V group of 8 keys starting at step offset 16kc + 8hf (one page: pages
+  // hold a multiple of 16 slots)
+  auto v_page = [&](int c0, int kc) {
+    return __shfl(mypage, (c0 + 16 * kc + 8 * hf) / ps - pg0);
   };
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
-      const bf16_t* v0 = vbase + (size_t)max(v_page(c0, kc, 0), 0) * kpage + (k0 % ps);
-      const bf16_t* v1 = vbase + (size_t)max(v_page(c0, kc, 1), 0) * kpage + (k1 % ps);
+      const int k0 = c0 + 16 * kc + 8 * hf;
+      const bf16_t* v0 = vbase + (size_t)max(v_page(c0, kc), 0) * kpage + (k0 % ps);
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const size_t dofs = (size_t)(32 * i + j) * ps;
-        const u32x2 lo = *(const u32x2*)(v0 + dofs);
-        const u32x2 hi = *(const u32x2*)(v1 + dofs);
-        const u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
-        va[i][kc] = __builtin_bit_cast(bf16x8, packed);
-      }
+      for (int i = 0; i < D / 32; ++i)
+        va[i][kc] = *(const bf16x8*)(v0 + (size_t)(32 * i + j) * ps);
     }
   };
   // past the chunk end or on a bad page: zero V (stale slots may hold anything)
   auto zero_v_tail = [&](int c0) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const int k0 = c0 + 16 * kc + 4 * hf, k1 = k0 + 8;
-      const int n0 = v_page(c0, kc, 0) < 0 ? 0 : k_hi - k0;
-      const int n1 = v_page(c0, kc, 1) < 0 ? 0 : k_hi - k1;
+      const int k0 = c0 + 16 * kc + 8 * hf;
+      const int n0 = v_page(c0, kc) < 0 ? 0 : k_hi - k0;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const u32x4 w = __builtin_bit_cast(u32x4, va[i][kc]);
-        const u32x2 lo = keep_first(u32x2{w[0], w[1]}, n0);
-        const u32x2 hi = keep_first(u32x2{w[2], w[3]}, n1);
-        const u32x4 packed = {lo[0], lo[1], hi[0], hi[1]};
-        va[i][kc] = __builtin_bit_cast(bf16x8, packed);
-      }
+      for (int i = 0; i < D / 32; ++i) va[i][kc] = keep_first(va[i][kc], n0);
     }
   };
 
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
         for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int key = n0 + 16 * kc + (e < 4 ? 4 * hf + e : 8 + 4 * hf + (e - 4));
+            const int key = n0 + 16 * kc + 8 * hf + e;
             va[i][kc][e] = key < rs
                                ? p.v_new[(((size_t)s * p.B + key) * p.Hkv + kvh) * D + d]
                                : (bf16_t)0.f;
