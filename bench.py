@@ -10,9 +10,10 @@ that are resident in HBM before timing starts:
   2. one block-decode step at the Qwen2.5-7B shape: 64 sequences with cached
      prefixes U[512, 4096], B = 4 mask queries, 28/4 heads, head_dim 128:
      decode attention over the paged cache -> LM head (3584 x 152064, bf16
-     weights) with the confidence reduced in the GEMM epilogue (no logits
-     written) -> acceptance (tau cycling 1.0 / 0.9 / 0.7) + KV commit of the
-     accepted prefix.
+     weights, packed once at setup into the GEMM's tile layout) with the
+     confidence reduced in the GEMM epilogue (no logits written) ->
+     acceptance (tau cycling 1.0 / 0.9 / 0.7) + KV commit of the accepted
+     prefix.
 
 The headline `value` is the useful (unmasked) TFLOP/s of the two-stream
 attention; `accepted_tokens_per_s` is the decode step's accepted tokens per
@@ -209,6 +210,10 @@ def main():
     h, w = synth.lmhead_inputs(1004, N, LM["D"], LM["V"])
     H, W = to_dev(h, dev), to_dev(w, dev)
     del w
+    # the LM-head weights are packed once, as at model load: the same products,
+    # read as contiguous 16 KiB blocks per GEMM stage
+    W = mars.mars_lmhead_pack(W)
+    torch.cuda.synchronize()
     logits = torch.empty((N, LM["V"]), dtype=torch.float32, device=dev)
     top = torch.empty(N, dtype=torch.int32, device=dev)
     pm = torch.empty(N, dtype=torch.float32, device=dev)

@@ -57,6 +57,10 @@ SIGNATURES = {
     "mars_lmhead_confidence": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _sz,
                                               _p, _p]),
     "mars_lmhead_workspace_bytes": (_sz, [_i32, _i32]),
+    "mars_lmhead_packed_bytes": (_sz, [_i32, _i32]),
+    "mars_lmhead_pack": (ctypes.c_int, [_p, _p, _i32, _i32, _p]),
+    "mars_lmhead_confidence_packed": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p,
+                                                     _sz, _p, _p]),
     "mars_accept_commit": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "mars_strerror": (ctypes.c_char_p, [ctypes.c_int]),

@@ -241,19 +241,47 @@ def mars_lmhead_workspace_bytes(N, V):
     return int(_lib.lib().mars_lmhead_workspace_bytes(N, V))
 
 
+class PackedLMHead:
+    """LM-head weights in the GEMM's tile layout (from mars_lmhead_pack)."""
+
+    def __init__(self, data, vocab: int, dim: int):
+        self.data, self.vocab, self.dim = data, vocab, dim
+
+
+def mars_lmhead_pack(w_lm, *, stream=None) -> PackedLMHead:
+    """Pack W [V, D] bf16 once for mars_lmhead_confidence (same results, contiguous
+    weight reads)."""
+    _need(w_lm, "w_lm", torch.bfloat16, 2)
+    V, D = w_lm.shape
+    n = int(_lib.lib().mars_lmhead_packed_bytes(D, V))
+    if n == 0:
+        raise ValueError("packing needs D >= 32, D % 32 == 0, V >= 4 and V % 4 == 0")
+    data = torch.empty(n // 2, dtype=torch.bfloat16, device=w_lm.device)
+    check("mars_lmhead_pack", _lib.lib().mars_lmhead_pack(_ptr(w_lm), _ptr(data), D, V,
+                                                            _stream(stream)))
+    return PackedLMHead(data, V, D)
+
+
 def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None,
                            workspace=None, status=None, stream=None, fused=False):
-    """LM head + confidence. With hidden [N,D] bf16 and w_lm [V,D] bf16, writes fp32
-    logits [N,V] (or, with fused=True, writes no logits and returns None for them);
-    with hidden None, `logits` is the input. Returns (logits, top_id int32 [N],
-    p_max fp32 [N])."""
+    """LM head + confidence. With hidden [N,D] bf16 and w_lm [V,D] bf16 (or a
+    PackedLMHead), writes fp32 logits [N,V] (or, with fused=True, writes no logits and
+    returns None for them); with hidden None, `logits` is the input. Returns (logits,
+    top_id int32 [N], p_max fp32 [N])."""
+    packed = isinstance(w_lm, PackedLMHead)
     if hidden is not None:
         _need(hidden, "hidden", torch.bfloat16, 2)
-        _need(w_lm, "w_lm", torch.bfloat16, 2)
         N, D = hidden.shape
-        V = w_lm.shape[0]
-        if w_lm.shape[1] != D:
-            raise ValueError("w_lm must be [V, D]")
+        if packed:
+            _need(w_lm.data, "w_lm", torch.bfloat16, 1)
+            V = w_lm.vocab
+            if w_lm.dim != D:
+                raise ValueError("packed LM head has a different hidden size")
+        else:
+            _need(w_lm, "w_lm", torch.bfloat16, 2)
+            V = w_lm.shape[0]
+            if w_lm.shape[1] != D:
+                raise ValueError("w_lm must be [V, D]")
         if fused:
             if logits is not None:
                 raise ValueError("fused=True writes no logits; pass logits=None")
@@ -275,6 +303,14 @@ def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None
     need = mars_lmhead_workspace_bytes(N, V)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if packed:
+        if hidden is None:
+            raise ValueError("a packed LM head needs hidden states")
+        code = _lib.lib().mars_lmhead_confidence_packed(
+            _ptr(hidden), _ptr(w_lm.data), _ptr(logits), N, D, V, _ptr(top_id), _ptr(p_max),
+            _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))
+        check("mars_lmhead_confidence_packed", code)
+        return logits, top_id, p_max
     code = _lib.lib().mars_lmhead_confidence(
         _ptr(hidden), _ptr(w_lm), _ptr(logits), N, D, V, _ptr(top_id), _ptr(p_max),
         _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))

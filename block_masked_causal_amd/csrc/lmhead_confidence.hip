@@ -77,7 +77,8 @@ __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 struct GemmArgs {
   const bf16_t* hidden;
-  const bf16_t* w;
+  const bf16_t* w;   // [V, D] rows, or packed: [nvt][D / GK][GN][GK] (one stage contiguous)
+  int packed;
   float* logits;     // unfused: [N, V] fp32
   ConfPart* part;    // fused: [N][nvt] partials, one per vocabulary tile
   int32_t* status;
@@ -110,8 +111,10 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   // buffer views of this tile's rows: rows past N (or V) read as zeros
   const u32x4 rh = rsrc_words(p.hidden + (size_t)n0 * p.D,
                               (uint32_t)((size_t)min(GM, p.N - n0) * p.D * sizeof(bf16_t)));
-  const u32x4 rw = rsrc_words(p.w + (size_t)v0 * p.D,
-                              (uint32_t)((size_t)min(GN, p.V - v0) * p.D * sizeof(bf16_t)));
+  // the packed layout holds every tile whole (rows past V are zeros)
+  const u32x4 rw = rsrc_words(
+      p.w + (size_t)v0 * p.D,
+      (uint32_t)((size_t)(p.packed ? GN : min(GN, p.V - v0)) * p.D * sizeof(bf16_t)));
   // stage kt: wave w fills blocks w, w + 8, ... (hidden tile first, then weights)
   auto issue = [&](int kt, bf16_t* st) {
 #pragma unroll
@@ -120,8 +123,14 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
       const bool is_a = blk < GABLK;
       const int rb = (is_a ? blk : blk - GABLK) * GROWS_BLK;
       const int row = rb + lane / GCPR, slot = lane % GCPR;
-      const uint32_t off = (uint32_t)((size_t)row * p.D * sizeof(bf16_t)) +
-                           (uint32_t)(kt * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row));
+      // row-major: 64 bytes of each of the tile's rows; packed: one
+      // contiguous 16 KiB block per stage
+      const uint32_t off =
+          (is_a || !p.packed)
+              ? (uint32_t)((size_t)row * p.D * sizeof(bf16_t)) +
+                    (uint32_t)(kt * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row))
+              : (uint32_t)(kt * GN * GK * sizeof(bf16_t)) +
+                    (uint32_t)(row * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row));
       lds_dma16(is_a ? rh : rw, st + (is_a ? 0 : GM * GK) + rb * GK, off);
     }
   };
@@ -409,6 +418,28 @@ __global__ __launch_bounds__(256) void conf_merge_wide_kernel(ConfArgs p) {
   }
 }
 
+// Weight packing: W [V, D] -> [nvt][D / GK][GN][GK], rows past V zero, so that
+// every GEMM stage reads one contiguous 16 KiB block of weights (a row-major
+// stage is 64 bytes from each of 256 rows 2D bytes apart). One 16-byte chunk
+// per thread, in packed order.
+__global__ __launch_bounds__(256) void lmhead_pack_kernel(const bf16_t* __restrict__ w,
+                                                          bf16_t* __restrict__ wp, int D,
+                                                          int V, long long chunks) {
+  constexpr int CPR = GK / 8;  // chunks per packed row
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < chunks;
+       i += (long long)gridDim.x * 256) {
+    const long long tile = i / (GN * CPR);
+    const int within = (int)(i % (GN * CPR));
+    const int r = within / CPR, c8 = within % CPR;
+    const long long vt = tile / (D / GK);
+    const int kt = (int)(tile % (D / GK));
+    const long long v = vt * GN + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (v < V) val = *(const u32x4*)(w + v * D + kt * GK + c8 * 8);
+    *(u32x4*)(wp + i * 8) = val;
+  }
+}
+
 void conf_layout(int N, int V, int* nchunk, int* chunk) {
   int c = std::max(1, std::min(32, (2048 + N - 1) / N));
   c = std::min(c, std::max(1, (V + 1023) / 1024));
@@ -437,10 +468,10 @@ extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
   return (size_t)N * std::max(nchunk, nvt) * sizeof(ConfPart);
 }
 
-extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits,
-                                      int32_t N, int32_t D, int32_t V, int32_t* top_id,
-                                      float* p_max, void* workspace, size_t workspace_bytes,
-                                      int32_t* status, void* stream) {
+namespace {
+int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, int32_t N,
+               int32_t D, int32_t V, int32_t* top_id, float* p_max, void* workspace,
+               size_t workspace_bytes, int32_t* status, void* stream) {
   MARS_REQUIRE(top_id && p_max, MARS_ERR_NULL);
   MARS_REQUIRE(!hidden || w_lm, MARS_ERR_NULL);
   MARS_REQUIRE(hidden || logits, MARS_ERR_NULL);  // logits may be omitted only when fused
@@ -472,6 +503,7 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
     GemmArgs g;
     g.hidden = (const bf16_t*)hidden;
     g.w = (const bf16_t*)w_lm;
+    g.packed = packed;
     g.logits = logits;
     g.part = (ConfPart*)workspace;
     g.status = status;
@@ -494,4 +526,41 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
   hipLaunchKernelGGL(conf_partial_kernel, dim3(c.nchunk, N), dim3(256), 0, st, c);
   hipLaunchKernelGGL(conf_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, c);
   return mars_launch_status();
+}
+}  // namespace
+
+extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits,
+                                      int32_t N, int32_t D, int32_t V, int32_t* top_id,
+                                      float* p_max, void* workspace, size_t workspace_bytes,
+                                      int32_t* status, void* stream) {
+  return run_lmhead(hidden, w_lm, 0, logits, N, D, V, top_id, p_max, workspace,
+                    workspace_bytes, status, stream);
+}
+
+extern "C" size_t mars_lmhead_packed_bytes(int32_t D, int32_t V) {
+  if (D < 32 || D % 32 || V < 4 || V % 4) return 0;
+  return (size_t)((V + GN - 1) / GN) * GN * D * sizeof(bf16_t);
+}
+
+extern "C" int mars_lmhead_pack(const void* w_lm, void* w_packed, int32_t D, int32_t V,
+                                void* stream) {
+  MARS_REQUIRE(w_lm && w_packed, MARS_ERR_NULL);
+  MARS_REQUIRE(mars_lmhead_packed_bytes(D, V) > 0, MARS_ERR_SHAPE);
+  MARS_REQUIRE((double)GN * D * 2 < 4294967295.0, MARS_ERR_SHAPE);
+  MARS_REQUIRE(mars_aligned16(w_lm) && mars_aligned16(w_packed), MARS_ERR_ALIGN);
+  const long long chunks = (long long)((V + GN - 1) / GN) * GN * D / 8;
+  const long long blocks = std::min<long long>((chunks + 255) / 256, 1 << 20);
+  hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, (const bf16_t*)w_lm, (bf16_t*)w_packed, D, V, chunks);
+  return mars_launch_status();
+}
+
+extern "C" int mars_lmhead_confidence_packed(const void* hidden, const void* w_packed,
+                                             float* logits, int32_t N, int32_t D, int32_t V,
+                                             int32_t* top_id, float* p_max, void* workspace,
+                                             size_t workspace_bytes, int32_t* status,
+                                             void* stream) {
+  MARS_REQUIRE(hidden && w_packed, MARS_ERR_NULL);
+  return run_lmhead(hidden, w_packed, 1, logits, N, D, V, top_id, p_max, workspace,
+                    workspace_bytes, status, stream);
 }

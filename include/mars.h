@@ -15,6 +15,7 @@
  *   mars_attn_block_decode  B mask queries against a paged block-level KV cache
  *   mars_attn_block_decode_rows  the same with a per-sequence row count
  *   mars_lmhead_confidence  LM-head GEMM + per-position argmax / max-softmax
+ *   mars_lmhead_confidence_packed  the same on weights packed by mars_lmhead_pack
  *   mars_accept_commit      left-to-right acceptance + KV commit of the prefix
  *   mars_kv_append          paged KV append of a prompt
  *   mars_block_sync_accept  acceptance under the batch-synchronous block cache
@@ -313,6 +314,27 @@ int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits, 
 
 /* Workspace bytes mars_lmhead_confidence needs (0 on bad sizes). */
 size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V);
+
+/*
+ * Weight packing for the LM-head GEMM (done once, when the weights are
+ * loaded). A row-major W [V, D] makes each 32-wide K stage of the GEMM read 64
+ * bytes from each of 256 rows 2D bytes apart; the packed layout
+ * [ceil(V / 256)][D / 32][256][32] bf16 (rows past V are zeros) makes every
+ * stage one contiguous 16 KiB block. The products, and so the logits, ids and
+ * probabilities, are bit-identical to the row-major call.
+ *
+ * mars_lmhead_packed_bytes: size of the packed buffer (0 unless D >= 32,
+ * D % 32 == 0, V >= 4 and V % 4 == 0). mars_lmhead_pack: w_lm [V, D] bf16 ->
+ * w_packed (that many bytes, 16-byte aligned), enqueued on `stream`.
+ * mars_lmhead_confidence_packed: as mars_lmhead_confidence with an LM head
+ * (hidden and w_packed required, logits NULL for the fused form).
+ */
+size_t mars_lmhead_packed_bytes(int32_t D, int32_t V);
+int mars_lmhead_pack(const void* w_lm, void* w_packed, int32_t D, int32_t V, void* stream);
+int mars_lmhead_confidence_packed(const void* hidden, const void* w_packed, float* logits,
+                                  int32_t N, int32_t D, int32_t V, int32_t* top_id,
+                                  float* p_max, void* workspace, size_t workspace_bytes,
+                                  int32_t* status, void* stream);
 
 /*
  * Left-to-right acceptance + KV commit of the accepted prefix.

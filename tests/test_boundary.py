@@ -189,6 +189,24 @@ def test_lmhead_argument_checks():
     assert mars.mars_lmhead_workspace_bytes(16, 1001) == 0
 
 
+def test_lmhead_packing_argument_checks():
+    L_ = mars.lib()
+    assert L_.mars_lmhead_packed_bytes(3584, 152064) == 594 * 256 * 3584 * 2
+    assert L_.mars_lmhead_packed_bytes(64, 1000) == 4 * 256 * 64 * 2   # padded to 1024 rows
+    assert L_.mars_lmhead_packed_bytes(48, 1000) == 0                   # D % 32 != 0
+    assert L_.mars_lmhead_packed_bytes(64, 1002) == 0                   # V % 4 != 0
+    assert L_.mars_lmhead_pack(None, FAKE, 64, 1000, None) == _lib.MARS_ERR_NULL
+    assert L_.mars_lmhead_pack(FAKE, FAKE, 48, 1000, None) == _lib.MARS_ERR_SHAPE
+    assert L_.mars_lmhead_pack(MIS, FAKE, 64, 1000, None) == _lib.MARS_ERR_ALIGN
+    pk = lambda **kw: L_.mars_lmhead_confidence_packed(
+        kw.get("h", FAKE), kw.get("w", FAKE), None, 16, kw.get("D", 64), 1000, FAKE, FAKE,
+        FAKE, kw.get("ws", 1 << 20), None, None)
+    assert pk(h=None) == _lib.MARS_ERR_NULL      # a packed head needs hidden states
+    assert pk(w=None) == _lib.MARS_ERR_NULL
+    assert pk(D=48) == _lib.MARS_ERR_SHAPE
+    assert pk(ws=16) == _lib.MARS_ERR_WORKSPACE
+
+
 def ac(p=FAKE, S=4, B=4, Hkv=2, d=32, page=16, max_pages=4, num_pages=16, dtype=1, kc=FAKE):
     return mars.lib().mars_accept_commit(p, FAKE, FAKE, FAKE, FAKE, kc, FAKE, FAKE, FAKE, FAKE,
                                          FAKE, FAKE, S, B, Hkv, d, page, max_pages, num_pages,

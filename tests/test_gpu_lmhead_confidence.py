@@ -165,3 +165,30 @@ def test_full_size_qwen7b_fused_confidence():
     ref = oracle.lmhead(h.f32[rows], w.f32)
     rid, rp = oracle.confidence(ref)
     assert np.max(np.abs(pf[rows] / rp - 1)) <= 1e-3
+
+
+@pytest.mark.parametrize("N,D,V", [(40, 256, 1000), (300, 512, 5000), (256, 3584, 152064)])
+def test_packed_weights_are_bitwise_the_row_major_call(N, D, V):
+    """The packed layout changes only which bytes a stage reads together: the
+    logits, ids and probabilities are bit-identical to the row-major call, and
+    the packed buffer is W padded to whole 256-row tiles in [tile][K/32][256][32]."""
+    say(f"[lmhead packed] N={N} D={D} V={V}")
+    h, w = synth.lmhead_inputs(5100 + N, N, D, V)
+    H, W = to_dev(h), to_dev(w)
+    pw = mars.mars_lmhead_pack(W)
+    lg, ids, p = mars.mars_lmhead_confidence(H, W)
+    lg2, ids2, p2 = mars.mars_lmhead_confidence(H, pw)
+    _, ids3, p3 = mars.mars_lmhead_confidence(H, W, fused=True)
+    _, ids4, p4 = mars.mars_lmhead_confidence(H, pw, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(lg.view(torch.int32), lg2.view(torch.int32))
+    assert torch.equal(ids, ids2) and torch.equal(p.view(torch.int32), p2.view(torch.int32))
+    assert torch.equal(ids3, ids4) and torch.equal(p3.view(torch.int32), p4.view(torch.int32))
+    if V <= 5000:
+        nvt = -(-V // 256)
+        wb = np.zeros((nvt * 256, D), dtype=np.uint16)
+        wb[:V] = w.bits
+        want = wb.reshape(nvt, 256, D // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+        got = pw.data.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want)
+
