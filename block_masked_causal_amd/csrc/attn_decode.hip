@@ -13,10 +13,11 @@
 // exactly once, straight from HBM into MFMA operands:
 //   * S^T = K Q^T: lane (key i, half hf) reads 16 bytes of its key's row.
 //   * O^T = V^T P^T: the V pages are stored transposed ([d][slot]), so the A
-//     operand of lane (dim, hf) is two 8-byte reads of consecutive slots.
-// The cache of one sequence is cut into 512-key chunks (split-K). Each workgroup handles one (chunk, KV head, sequence) and writes an
-// unnormalised partial (O, running max, running sum); a merge kernel combines
-// the chunks. A sequence that fits in one chunk is written out directly.
+//     operand of lane (dim, hf) is one 16-byte read of 8 consecutive slots
+//     (the probabilities are regrouped between the wave halves to match).
+// The cache of one sequence is cut into 512-key chunks (split-K). Each
+// workgroup handles one (chunk, KV head, sequence) and writes an unnormalised
+// partial (O, running max, running sum); a merge kernel combines the chunks. A sequence that fits in one chunk is written out directly.
 // Chunk 0 also handles the new rows (causal among themselves). Their number
 // may differ per sequence (at most 64): under the batch-synchronous block
 // cache (notes, key design 4) a sequence's new rows are its tokens accepted
