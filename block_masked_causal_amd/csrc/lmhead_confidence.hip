@@ -59,16 +59,11 @@ __device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, flo
 constexpr int GM = 256;
 constexpr int GN = 256;
 constexpr int GT = 512;                 // threads per workgroup
-constexpr int WNT = GN / 64;            // 32-wide vocab MFMA tiles per wave
 constexpr int GK = 32;                  // K per stage
 constexpr int GSTAGES = 4;
 constexpr int GCPR = GK / 8;            // 16-byte chunks per tile row
 constexpr int GROWS_BLK = 64 / GCPR;    // rows per 1 KiB direct-load block
 constexpr int GABLK = GM / GROWS_BLK;   // blocks per hidden tile
-constexpr int GWBLK = GN / GROWS_BLK;   // blocks per weight tile
-constexpr int GBPW = (GABLK + GWBLK) / (GT / 64);  // blocks per wave per stage
-constexpr int GSTAGE_EL = (GM + GN) * GK;          // elements per stage
-static_assert((GABLK + GWBLK) % (GT / 64) == 0 && GBPW < 8, "stage split");
 
 // Rows sit in LDS unpadded; chunk c of row r is stored at chunk c ^ gswz(r),
 // which keeps 16 consecutive rows read at one chunk on 16 distinct groups of
@@ -79,6 +74,8 @@ struct GemmArgs {
   const bf16_t* hidden;
   const bf16_t* w;   // [V, D] rows, or packed: [nvt][D / GK][GN][GK] (one stage contiguous)
   int packed;
+  int v_base;        // first vocabulary entry of this launch's tiles
+  int tile0;         // index of this launch's first tile among the row's partials
   float* logits;     // unfused: [N, V] fp32
   ConfPart* part;    // fused: [N][nvt] partials, one per vocabulary tile
   int32_t* status;
@@ -93,8 +90,14 @@ struct GemmArgs {
 // (two halves of two waves): FUSED reduces them in registers to the
 // confidence partial (max, first argmax, sum exp(l - max)) and writes no
 // logits.
-template <bool FUSED>
+// TN: vocabulary entries per workgroup (GN, or GN / 2 for the tail tiles).
+template <bool FUSED, int TN>
 __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
+  constexpr int WNT = TN / 64;            // 32-wide vocab MFMA tiles per wave
+  constexpr int GWBLK = TN / GROWS_BLK;   // blocks per weight tile
+  constexpr int GBPW = (GABLK + GWBLK) / (GT / 64);  // blocks per wave per stage
+  constexpr int GSTAGE_EL = (GM + TN) * GK;          // elements per stage
+  static_assert((GABLK + GWBLK) % (GT / 64) == 0 && GBPW < 8, "stage split");
   __shared__ __attribute__((aligned(16))) bf16_t st0[GSTAGE_EL];
   __shared__ __attribute__((aligned(16))) bf16_t st1[GSTAGE_EL];
   __shared__ __attribute__((aligned(16))) bf16_t st2[GSTAGE_EL];
@@ -104,17 +107,21 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
   const int wn = w >> 1, wv = w & 1;
-  const int v0 = blockIdx.x * GN;
+  const int v0 = p.v_base + blockIdx.x * TN;
   const int n0 = blockIdx.y * GM;
   const int nk = p.D / GK;
 
   // buffer views of this tile's rows: rows past N (or V) read as zeros
   const u32x4 rh = rsrc_words(p.hidden + (size_t)n0 * p.D,
                               (uint32_t)((size_t)min(GM, p.N - n0) * p.D * sizeof(bf16_t)));
-  // the packed layout holds every tile whole (rows past V are zeros)
-  const u32x4 rw = rsrc_words(
-      p.w + (size_t)v0 * p.D,
-      (uint32_t)((size_t)(p.packed ? GN : min(GN, p.V - v0)) * p.D * sizeof(bf16_t)));
+  // the packed layout holds every GN-row tile whole (rows past V are zeros);
+  // a narrower tile reads its rows inside one packed tile
+  const int prow0 = v0 % GN;  // first row inside the packed tile
+  const u32x4 rw =
+      p.packed ? rsrc_words(p.w + (size_t)(v0 / GN) * GN * p.D,
+                            (uint32_t)((size_t)GN * p.D * sizeof(bf16_t)))
+               : rsrc_words(p.w + (size_t)v0 * p.D,
+                            (uint32_t)((size_t)min(TN, p.V - v0) * p.D * sizeof(bf16_t)));
   // stage kt: wave w fills blocks w, w + 8, ... (hidden tile first, then weights)
   auto issue = [&](int kt, bf16_t* st) {
 #pragma unroll
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
               ? (uint32_t)((size_t)row * p.D * sizeof(bf16_t)) +
                     (uint32_t)(kt * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row))
               : (uint32_t)(kt * GN * GK * sizeof(bf16_t)) +
-                    (uint32_t)(row * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row));
+                    (uint32_t)((prow0 + row) * GK * sizeof(bf16_t)) + 16 * (slot ^ gswz(row));
       lds_dma16(is_a ? rh : rw, st + (is_a ? 0 : GM * GK) + rb * GK, off);
     }
   };
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
       bf16x8 wf[WNT], hfr[2];
 #pragma unroll
       for (int t = 0; t < WNT; ++t)
-        wf[t] = *(const bf16x8*)(Wt + (wv * (GN / 2) + 32 * t + j) * GK + koff[ks]);
+        wf[t] = *(const bf16x8*)(Wt + (wv * (TN / 2) + 32 * t + j) * GK + koff[ks]);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         hfr[t] = *(const bf16x8*)(A + (wn * 64 + 32 * t + j) * GK + koff[ks]);
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   }
   bf16_t* const gl = st0;  // free after the K loop: the epilogue's exchange area
 
-  const int vb = v0 + wv * (GN / 2) + 4 * hf;  // + 32 va + 8 (r / 4) + r % 4
+  const int vb = v0 + wv * (TN / 2) + 4 * hf;  // + 32 va + 8 (r / 4) + r % 4
   if constexpr (!FUSED) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
           out.m = pm[b];
           out.idx = pi[b];
           out.s = ps[b];
-          p.part[(size_t)n * p.nvt + blockIdx.x] = out;
+          p.part[(size_t)n * p.nvt + p.tile0 + blockIdx.x] = out;
         }
       }
     }
@@ -453,10 +460,43 @@ void conf_layout(int N, int V, int* nchunk, int* chunk) {
 }  // namespace
 
 namespace {
+// One GN-wide tile per workgroup and one workgroup per CU at a time (the LDS
+// ring): tiles run in rounds of one per CU. When the last round would be at
+// most half full, its tiles are cut in two and run as GN / 2-wide tiles,
+// which finish in about half a round (the vocabulary order of the partials
+// is kept: main tiles first, then the tail's).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
 template <bool FUSED>
-int launch_gemm(dim3 grid, hipStream_t st, const GemmArgs& g) {
-  hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED>), grid, dim3(GT), 0, st, g);
-  return MARS_OK;
+int launch_gemm(GemmArgs g, int row_tiles, hipStream_t st) {
+  const int full = (g.V + GN - 1) / GN;
+  const int ncu = cu_count();
+  int main_tiles = full;
+  if (row_tiles == 1 && ncu > 0 && full > ncu) {
+    const int r = full % ncu;
+    if (r > 0 && 2 * r <= ncu) main_tiles = full - r;
+  }
+  const int tail_v = g.V - main_tiles * GN;  // entries left to the half-width tiles
+  const int tail_tiles = tail_v > 0 ? (tail_v + GN / 2 - 1) / (GN / 2) : 0;
+  g.nvt = main_tiles + tail_tiles;
+  g.v_base = 0;
+  g.tile0 = 0;
+  if (main_tiles > 0)
+    hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED, GN>), dim3(main_tiles, row_tiles), dim3(GT),
+                       0, st, g);
+  if (tail_tiles > 0) {
+    g.v_base = main_tiles * GN;
+    g.tile0 = main_tiles;
+    hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED, GN / 2>), dim3(tail_tiles, row_tiles),
+                       dim3(GT), 0, st, g);
+  }
+  return g.nvt;
 }
 }  // namespace
 
@@ -464,7 +504,8 @@ extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
   if (N < 1 || V < 4 || V % 4) return 0;
   int nchunk, chunk;
   conf_layout(N, V, &nchunk, &chunk);
-  const int nvt = (V + GN - 1) / GN;  // fused path: one partial per vocabulary tile
+  // fused path: one partial per vocabulary tile; bounded by tiles of GN / 2
+  const int nvt = 2 * ((V + GN - 1) / GN);
   return (size_t)N * std::max(nchunk, nvt) * sizeof(ConfPart);
 }
 
@@ -510,13 +551,12 @@ int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, 
     g.N = N;
     g.D = D;
     g.V = V;
-    g.nvt = (V + GN - 1) / GN;
-    dim3 grid(g.nvt, (N + GM - 1) / GM);
+    const int row_tiles = (N + GM - 1) / GM;
     const bool fused = logits == nullptr;
-    const int rc = fused ? launch_gemm<true>(grid, st, g) : launch_gemm<false>(grid, st, g);
-    if (rc != MARS_OK) return rc;
+    const int nvt = fused ? launch_gemm<true>(g, row_tiles, st)
+                          : launch_gemm<false>(g, row_tiles, st);
     if (fused) {
-      c.nchunk = g.nvt;
+      c.nchunk = nvt;
       c.chunk = GN;
       hipLaunchKernelGGL(conf_merge_wide_kernel, dim3(N), dim3(256), 0, st, c);
       return mars_launch_status();
