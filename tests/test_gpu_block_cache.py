@@ -258,3 +258,48 @@ def test_block_freeze_flags_overflow_and_keeps_what_fits():
                                  d.v_new.f32, np.array([Bc, 3, Bc]), page)
     assert np.array_equal(cache_bits(kc), synth.bf16_round(rk).view(np.int16))
     assert np.array_equal(cache_bits(vc), synth.bf16_round(rv).view(np.int16))
+
+
+def test_full_size_block_cache_step_sampled_sequences():
+    """The benchmarked block-cache shape (Qwen2.5-7B heads, S=16, B=4, B_cache=16,
+    prefixes U[512, 2048]): one step with every block full (ragged rows up to
+    B_cache + B = 20, the freeze, the acceptance), the attention checked on
+    sampled sequences, the integer state on all."""
+    S, B, Bc, Hq, Hkv, D, page = 16, 4, 16, 28, 4, 128, 16
+    R = Bc + B
+    say(f"[block full size] S={S} R={R} heads {Hq}/{Hkv} d={D}")
+    d = synth.decode_inputs(4800, S, R, Hq, Hkv, D, 512, 2048, page, extra_capacity=Bc)
+    rng = np.random.default_rng(4801)
+    u = np.full(S, Bc, dtype=np.int32)
+    nrows = (u + B).astype(np.int32)
+    nrows[3] = 7                                # a sequence that waits with fewer rows
+    toks = rng.integers(0, 152064, size=(S, Bc)).astype(np.int32)
+    kc, vc, bt, cl = to_dev(d.k_cache), to_dev(d.v_cache), to_dev(d.block_table), to_dev(d.cache_len)
+    KN, VN = to_dev(d.k_new), to_dev(d.v_new)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o = mars.mars_attn_block_decode(to_dev(d.q), KN, VN, kc, vc, bt, cl, n_rows=to_dev(nrows),
+                                    status=status)
+    ud, td = to_dev(u), to_dev(toks)
+    mars.mars_block_freeze(KN, VN, kc, vc, bt, cl, ud, Bc, status=status)
+    p = rng.uniform(0.0, 1.0, size=(S, B)).astype(np.float32)
+    ids = rng.integers(0, 152064, size=(S, B)).astype(np.int32)
+    tau = np.full(S, 0.5, dtype=np.float32)
+    kept, nr = mars.mars_block_sync_accept(to_dev(p), to_dev(ids), to_dev(tau), ud, td,
+                                           policy="min", status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    seqs = [0, 3, S - 1]
+    ref = oracle.attn_block_decode_rows(d.q.f32, d.k_new.f32, d.v_new.f32, d.k_cache.f32,
+                                        d.v_cache.f32, d.block_table, d.cache_len, nrows, page,
+                                        seqs=seqs)
+    og = from_dev(o)
+    for s in seqs:
+        assert max_abs(og[s, :nrows[s]], ref[s]) <= 2e-2, s
+    _, _, rl, froze = oracle.block_freeze(d.k_cache.f32, d.v_cache.f32, d.block_table,
+                                          d.cache_len, d.k_new.f32, d.v_new.f32, u, Bc, page)
+    rk, ru, rt, _, rn = oracle.block_sync_step(p, ids, tau, u, toks, Bc, "min")
+    assert froze and np.array_equal(cl.cpu().numpy(), rl)
+    assert np.array_equal(kept.cpu().numpy(), rk)
+    assert np.array_equal(ud.cpu().numpy(), ru)
+    assert np.array_equal(td.cpu().numpy(), rt)
+    assert np.array_equal(nr.cpu().numpy(), rn)
