@@ -166,14 +166,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
   // (dynamic LDS of 64 * (head_dim * ES + 4) bytes)
   extern __shared__ __attribute__((aligned(16))) char sv[];
   __shared__ int sh_page[64];  // page of each window position; -1 skip (flagged), -2 not ours
-  const int s = blockIdx.y, kvh = blockIdx.z, tid = threadIdx.x;
+  // heads fastest: the workgroups of one window read neighbouring slices of
+  // the same source rows
+  const int s = blockIdx.y, kvh = blockIdx.x % p.Hkv, win = blockIdx.x / p.Hkv;
+  const int tid = threadIdx.x;
   if (!gate_open(p)) return;
   const int len = p.cache_len[s];
   if (len < 0) {
-    if (blockIdx.x == 0 && kvh == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
+    if (blockIdx.x == 0 && tid == 0) status_or(p.status, MARS_STATUS_CACHE_OVERFLOW);
     return;
   }
-  const long long wbase = (long long)(len & ~7) + 64LL * blockIdx.x;
+  const long long wbase = (long long)(len & ~7) + 64LL * win;
   const long long cap = (long long)p.max_pages * p.page_size;
   if (tid < 64) {
     const long long pos = wbase + tid;
@@ -392,7 +395,9 @@ int run_append(const void* k_rows, const void* v_rows, void* k_cache, void* v_ca
   a.max_pages = max_pages;
   a.num_pages = num_pages;
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((T + 7 + 63) / 64, S, n_kv_heads);
+  const long long nwg = (long long)((T + 7 + 63) / 64) * n_kv_heads;
+  MARS_REQUIRE(nwg <= 2147483647LL, MARS_ERR_SHAPE);
+  const dim3 grid((unsigned)nwg, S);
   const size_t lds = 64 * ((size_t)head_dim * (dtype == MARS_BF16 ? 2 : 4) + 4);
   if (dtype == MARS_BF16)
     hipLaunchKernelGGL(kv_append_kernel<2>, grid, dim3(256), lds, st, a);
