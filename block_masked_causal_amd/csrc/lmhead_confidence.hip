@@ -8,7 +8,7 @@
 //
 //  * lmhead_gemm_kernel: logits[N, V] = hidden[N, D] . W[V, D]^T on the
 //    32x32x16 bf16 MFMA with fp32 accumulation. A 512-thread workgroup owns
-//    all of up to 256 rows and 256 vocabulary entries, so each weight row is
+//    all of up to 256 rows and 320 vocabulary entries, so each weight row is
 //    read from HBM once; K is staged 32 at a time through a 4-stage LDS ring
 //    filled by direct global->LDS loads (three stages in flight). With
 //    logits == NULL the epilogue reduces the tile to per-row confidence
@@ -50,14 +50,16 @@ __device__ __forceinline__ void conf_combine(float& m1, int& i1, double& s1, flo
 
 // ------------------------------------------------------------------ GEMM ----
 // Workgroup tile: GM rows (all positions, up to 256) x GN vocabulary entries;
-// 8 waves as 4 (rows) x 2 (vocab), each wave 64 x 128 outputs, so each pair
-// of fragments read from LDS feeds eight MFMAs and each weight row is read
-// from HBM once. K advances GK = 32 per stage through a ring of GSTAGES = 4
+// 8 waves as 4 (rows) x 2 (vocab), each wave 64 x 160 outputs, so each seven
+// fragments read from LDS feed ten MFMAs and each weight row is read from HBM
+// once. GN = 320 because 152064 / 320 = 476 tiles fill two rounds of one tile
+// per CU on 256 CUs (256-wide tiles left a 2.32-round grid). K advances GK = 32 per stage through a ring of GSTAGES = 4
 // LDS stages filled by direct global->LDS loads: three stages are always in
 // flight while one is multiplied (one 64-wide stage in flight, as a register
 // staged pipeline allows, left each workgroup waiting on memory latency).
 constexpr int GM = 256;
-constexpr int GN = 256;
+constexpr int GN = 320;
+constexpr int GN_TAIL = 64;  // tail tiles: divide GN, so none straddles a packed tile
 constexpr int GT = 512;                 // threads per workgroup
 constexpr int GK = 32;                  // K per stage
 constexpr int GSTAGES = 4;
@@ -85,19 +87,24 @@ struct GemmArgs {
 // logits^T = W . hidden^T: the MFMA A operand is a 32-entry slice of the
 // vocabulary, B a 32-position slice, so lane (j, hf) of tile (va, pb) holds
 // position n0 + wn*64 + 32 pb + j and vocabulary entries
-// v0 + wv*128 + 32 va + 8 (r / 4) + 4 hf + r % 4, r = 0..15. A position's
-// 256 entries of the workgroup tile are thus 64 values in each of 4 lanes
+// v0 + wv*TN/2 + 32 va + 8 (r / 4) + 4 hf + r % 4, r = 0..15. A position's
+// TN entries of the workgroup tile are thus TN/4 values in each of 4 lanes
 // (two halves of two waves): FUSED reduces them in registers to the
 // confidence partial (max, first argmax, sum exp(l - max)) and writes no
 // logits.
-// TN: vocabulary entries per workgroup (GN, or GN / 2 for the tail tiles).
+// TN: vocabulary entries per workgroup (GN, or GN_TAIL for the tail tiles).
+// A stage is GM / 16 + TN / 16 direct loads of 1 KiB; when they do not split
+// evenly over the 8 waves, the first GXTRA waves issue one more, and each wave
+// waits for its own count.
 template <bool FUSED, int TN>
 __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
   constexpr int WNT = TN / 64;            // 32-wide vocab MFMA tiles per wave
   constexpr int GWBLK = TN / GROWS_BLK;   // blocks per weight tile
-  constexpr int GBPW = (GABLK + GWBLK) / (GT / 64);  // blocks per wave per stage
+  constexpr int GNBLK = GABLK + GWBLK;                // 1 KiB blocks per stage
+  constexpr int GBPW = (GNBLK + GT / 64 - 1) / (GT / 64);  // blocks of the busiest wave
+  constexpr int GXTRA = GNBLK % (GT / 64);  // waves below this issue GBPW, the rest GBPW - 1
   constexpr int GSTAGE_EL = (GM + TN) * GK;          // elements per stage
-  static_assert((GABLK + GWBLK) % (GT / 64) == 0 && GBPW < 8, "stage split");
+  static_assert(TN % 64 == 0 && 2 * GBPW < 16, "stage split");
   __shared__ __attribute__((aligned(16))) bf16_t st0[GSTAGE_EL];
   __shared__ __attribute__((aligned(16))) bf16_t st1[GSTAGE_EL];
   __shared__ __attribute__((aligned(16))) bf16_t st2[GSTAGE_EL];
@@ -127,6 +134,7 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < GBPW; ++i) {
       const int blk = w + (GT / 64) * i;
+      if (blk >= GNBLK) break;  // wave-uniform
       const bool is_a = blk < GABLK;
       const int rb = (is_a ? blk : blk - GABLK) * GROWS_BLK;
       const int row = rb + lane / GCPR, slot = lane % GCPR;
@@ -172,14 +180,23 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
     }
   };
 
+  // wait until at most S stages of this wave's loads are in flight (a wave's
+  // loads per stage: GBPW, or GBPW - 1 past the first GXTRA waves)
+  auto wait_stages = [&](auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
+    if (GXTRA == 0 || w < GXTRA)
+      wait_vm_upto<S * GBPW>();
+    else
+      wait_vm_upto<S * (GBPW - 1)>();
+  };
   // prologue: stages 0..2 in flight, wait for stage 0
   issue(0, st0);
   if (nk > 1) issue(1, st1);
   if (nk > 2) issue(2, st2);
   if (nk > 2)
-    wait_vm_upto<2 * GBPW>();
+    wait_stages(std::integral_constant<int, 2>{});
   else if (nk > 1)
-    wait_vm_upto<GBPW>();
+    wait_stages(std::integral_constant<int, 1>{});
   else
     wait_vm_upto<0>();
   __builtin_amdgcn_s_barrier();
@@ -193,9 +210,9 @@ __global__ __launch_bounds__(GT, 2) void lmhead_gemm_kernel(GemmArgs p) {
     compute(cur);
     // stage kt + 1 has landed once at most the stages issued after it are in flight
     if (kt + 3 < nk)
-      wait_vm_upto<2 * GBPW>();
+      wait_stages(std::integral_constant<int, 2>{});
     else if (kt + 2 < nk)
-      wait_vm_upto<GBPW>();
+      wait_stages(std::integral_constant<int, 1>{});
     else
       wait_vm_upto<0>();
     __builtin_amdgcn_s_barrier();
@@ -390,8 +407,7 @@ __global__ __launch_bounds__(256) void conf_merge_kernel(ConfArgs p) {
   p.p_max[row] = (float)(1.0 / S);
 }
 
-// Merge of many partials per row (the fused path: one per 256-entry vocabulary
-// tile): one workgroup per row, each thread folds a strided subset in order,
+// Merge of many partials per row (the fused path: one per vocabulary tile): one workgroup per row, each thread folds a strided subset in order,
 // then a fixed butterfly over the wave and a fixed order over the 4 waves.
 __global__ __launch_bounds__(256) void conf_merge_wide_kernel(ConfArgs p) {
   const int row = blockIdx.x;
@@ -426,8 +442,8 @@ __global__ __launch_bounds__(256) void conf_merge_wide_kernel(ConfArgs p) {
 }
 
 // Weight packing: W [V, D] -> [nvt][D / GK][GN][GK], rows past V zero, so that
-// every GEMM stage reads one contiguous 16 KiB block of weights (a row-major
-// stage is 64 bytes from each of 256 rows 2D bytes apart). One 16-byte chunk
+// every GEMM stage reads one contiguous 20 KiB block of weights (a row-major
+// stage is 64 bytes from each of 320 rows 2D bytes apart). One 16-byte chunk
 // per thread, in packed order.
 __global__ __launch_bounds__(256) void lmhead_pack_kernel(const bf16_t* __restrict__ w,
                                                           bf16_t* __restrict__ wp, int D,
@@ -461,10 +477,10 @@ void conf_layout(int N, int V, int* nchunk, int* chunk) {
 
 namespace {
 // One GN-wide tile per workgroup and one workgroup per CU at a time (the LDS
-// ring): tiles run in rounds of one per CU. When the last round would be at
-// most half full, its tiles are cut in two and run as GN / 2-wide tiles,
-// which finish in about half a round (the vocabulary order of the partials
-// is kept: main tiles first, then the tail's).
+// ring): tiles run in rounds of one per CU. When the last round's tiles, cut
+// into GN_TAIL-wide tiles, would still fit one round, they run that way and
+// finish well before a full round (the vocabulary order of the partials is
+// kept: main tiles first, then the tail's).
 int cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -480,10 +496,10 @@ int launch_gemm(GemmArgs g, int row_tiles, hipStream_t st) {
   int main_tiles = full;
   if (row_tiles == 1 && ncu > 0 && full > ncu) {
     const int r = full % ncu;
-    if (r > 0 && 2 * r <= ncu) main_tiles = full - r;
+    if (r > 0 && (GN / GN_TAIL) * r <= ncu) main_tiles = full - r;
   }
-  const int tail_v = g.V - main_tiles * GN;  // entries left to the half-width tiles
-  const int tail_tiles = tail_v > 0 ? (tail_v + GN / 2 - 1) / (GN / 2) : 0;
+  const int tail_v = g.V - main_tiles * GN;  // entries left to the narrow tiles
+  const int tail_tiles = tail_v > 0 ? (tail_v + GN_TAIL - 1) / GN_TAIL : 0;
   g.nvt = main_tiles + tail_tiles;
   g.v_base = 0;
   g.tile0 = 0;
@@ -493,7 +509,7 @@ int launch_gemm(GemmArgs g, int row_tiles, hipStream_t st) {
   if (tail_tiles > 0) {
     g.v_base = main_tiles * GN;
     g.tile0 = main_tiles;
-    hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED, GN / 2>), dim3(tail_tiles, row_tiles),
+    hipLaunchKernelGGL((lmhead_gemm_kernel<FUSED, GN_TAIL>), dim3(tail_tiles, row_tiles),
                        dim3(GT), 0, st, g);
   }
   return g.nvt;
@@ -504,8 +520,8 @@ extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
   if (N < 1 || V < 4 || V % 4) return 0;
   int nchunk, chunk;
   conf_layout(N, V, &nchunk, &chunk);
-  // fused path: one partial per vocabulary tile; bounded by tiles of GN / 2
-  const int nvt = 2 * ((V + GN - 1) / GN);
+  // fused path: one partial per vocabulary tile; bounded by tiles of GN_TAIL
+  const int nvt = (GN / GN_TAIL) * ((V + GN - 1) / GN);
   return (size_t)N * std::max(nchunk, nvt) * sizeof(ConfPart);
 }
 
@@ -521,7 +537,7 @@ int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, 
   MARS_REQUIRE((double)N * V < 9.0e18, MARS_ERR_SHAPE);
   if (hidden) {
     MARS_REQUIRE(D >= 32 && D % 32 == 0, MARS_ERR_SHAPE);
-    // buffer views address one 256-row tile with 32-bit byte offsets
+    // buffer views address one GN-row tile with 32-bit byte offsets
     MARS_REQUIRE((double)GN * D * 2 < 4294967295.0, MARS_ERR_SHAPE);
   }
   MARS_REQUIRE(mars_aligned16(hidden) && mars_aligned16(w_lm) && mars_aligned16(logits) &&

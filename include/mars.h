@@ -318,9 +318,9 @@ size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V);
 /*
  * Weight packing for the LM-head GEMM (done once, when the weights are
  * loaded). A row-major W [V, D] makes each 32-wide K stage of the GEMM read 64
- * bytes from each of 256 rows 2D bytes apart; the packed layout
- * [ceil(V / 256)][D / 32][256][32] bf16 (rows past V are zeros) makes every
- * stage one contiguous 16 KiB block. The products, and so the logits, ids and
+ * bytes from each of 320 rows 2D bytes apart; the packed layout
+ * [ceil(V / 320)][D / 32][320][32] bf16 (rows past V are zeros) makes every
+ * stage one contiguous 20 KiB block. The products, and so the logits, ids and
  * probabilities, are bit-identical to the row-major call.
  *
  * mars_lmhead_packed_bytes: size of the packed buffer (0 unless D >= 32,

@@ -191,8 +191,8 @@ def test_lmhead_argument_checks():
 
 def test_lmhead_packing_argument_checks():
     L_ = mars.lib()
-    assert L_.mars_lmhead_packed_bytes(3584, 152064) == 594 * 256 * 3584 * 2
-    assert L_.mars_lmhead_packed_bytes(64, 1000) == 4 * 256 * 64 * 2   # padded to 1024 rows
+    assert L_.mars_lmhead_packed_bytes(3584, 152064) == 476 * 320 * 3584 * 2
+    assert L_.mars_lmhead_packed_bytes(64, 1000) == 4 * 320 * 64 * 2   # padded to 1280 rows
     assert L_.mars_lmhead_packed_bytes(48, 1000) == 0                   # D % 32 != 0
     assert L_.mars_lmhead_packed_bytes(64, 1002) == 0                   # V % 4 != 0
     assert L_.mars_lmhead_pack(None, FAKE, 64, 1000, None) == _lib.MARS_ERR_NULL

@@ -121,11 +121,13 @@ def test_full_size_qwen7b_lmhead_sampled_rows():
 
 
 @pytest.mark.parametrize("N,D,V", [(40, 256, 1000), (300, 96, 516), (256, 3584, 1024),
-                                   (7, 64, 260)])
+                                   (7, 64, 260), (64, 256, 82020)])
 def test_fused_confidence_equals_unfused_and_oracle(N, D, V):
     """GEMM epilogue reduction (no logits written) against the two-pass path on the same
     device logits (ids bit-exact, p to 1e-6 relative) and against the fp64 oracle.
-    Shapes cover a partial last vocabulary tile, two row tiles, and a K step of 32."""
+    Shapes cover a partial last vocabulary tile, two row tiles, a K step of 32, and
+    (V = 82020 on 256 CUs) 256 full 320-wide tiles followed by a 100-entry tail that
+    runs as 64-wide tiles, the last one partial."""
     say(f"[lmhead fused] N={N} D={D} V={V}")
     h, w = synth.lmhead_inputs(5200 + N, N, D, V)
     H, W = to_dev(h), to_dev(w)
@@ -167,11 +169,12 @@ def test_full_size_qwen7b_fused_confidence():
     assert np.max(np.abs(pf[rows] / rp - 1)) <= 1e-3
 
 
-@pytest.mark.parametrize("N,D,V", [(40, 256, 1000), (300, 512, 5000), (256, 3584, 152064)])
+@pytest.mark.parametrize("N,D,V", [(40, 256, 1000), (300, 512, 5000), (64, 256, 82020),
+                                   (256, 3584, 152064)])
 def test_packed_weights_are_bitwise_the_row_major_call(N, D, V):
     """The packed layout changes only which bytes a stage reads together: the
     logits, ids and probabilities are bit-identical to the row-major call, and
-    the packed buffer is W padded to whole 256-row tiles in [tile][K/32][256][32]."""
+    the packed buffer is W padded to whole 320-row tiles in [tile][K/32][320][32]."""
     say(f"[lmhead packed] N={N} D={D} V={V}")
     h, w = synth.lmhead_inputs(5100 + N, N, D, V)
     H, W = to_dev(h), to_dev(w)
@@ -185,10 +188,10 @@ def test_packed_weights_are_bitwise_the_row_major_call(N, D, V):
     assert torch.equal(ids, ids2) and torch.equal(p.view(torch.int32), p2.view(torch.int32))
     assert torch.equal(ids3, ids4) and torch.equal(p3.view(torch.int32), p4.view(torch.int32))
     if V <= 5000:
-        nvt = -(-V // 256)
-        wb = np.zeros((nvt * 256, D), dtype=np.uint16)
+        nvt = -(-V // 320)
+        wb = np.zeros((nvt * 320, D), dtype=np.uint16)
         wb[:V] = w.bits
-        want = wb.reshape(nvt, 256, D // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+        want = wb.reshape(nvt, 320, D // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
         got = pw.data.cpu().view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(got, want)
 
