@@ -35,11 +35,11 @@ CALLS = {
     "block_decode_attention": (["attn_decode.hip", "mars_common.hpp"],
                                ["decode_split_kernel", "decode_merge_kernel"]),
     "lmhead_confidence_fused": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                ["lmhead_gemm_kernel<true, 256>",
-                                 "lmhead_gemm_kernel<true, 128>", "conf_merge_wide_kernel"]),
+                                ["lmhead_gemm_kernel<true, 320>",
+                                 "lmhead_gemm_kernel<true, 64>", "conf_merge_wide_kernel"]),
     "lmhead_gemm_plus_confidence": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                    ["lmhead_gemm_kernel<false, 256>",
-                                     "lmhead_gemm_kernel<false, 128>", "conf_partial_kernel",
+                                    ["lmhead_gemm_kernel<false, 320>",
+                                     "lmhead_gemm_kernel<false, 64>", "conf_partial_kernel",
                                      r"conf_merge_kernel\("]),
     "accept_commit": (["accept_commit.hip", "mars_common.hpp"], ["accept_commit_kernel"]),
     "kv_append": (["accept_commit.hip", "mars_common.hpp"],
