@@ -83,6 +83,21 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
 }
 
+// Tiles read both ways (the backward's K, Q and dO tiles: rows for one
+// product, transposed for another) use one permutation that keeps both read
+// patterns on all 64 banks: the bit reversal of the row's index into swz_k's
+// range. swz_k alone leaves the transposing reads 2-way (d = 64) or 4-way
+// (d = 128) conflicted, and swz_v leaves the row reads 4-way conflicted.
+template <int D>
+__device__ __forceinline__ int swz_b(int r) {
+  if (D == 64) {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+  }
+  const int x = r & 15;
+  return ((x & 1) << 3) | ((x & 2) << 1) | ((x >> 1) & 2) | ((x >> 3) & 1);
+}
+
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 
   auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
 
-  // K and V tiles: direct global -> LDS loads, rows XOR-permuted for row reads
+  // K and V tiles: direct global -> LDS loads, rows XOR-permuted (swz_b) so
+  // that both the row reads and the transposing K reads hit all 64 banks
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto issue_tile = [&](int it, bf16_t* st) {
     const int c0 = tile_c0(it);
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
         const int u = blk * 64 + lane;
         const int row = u / C::CPR, slot = u % C::CPR;
         const uint32_t off = (uint32_t)(((c0 + row) * rs) * sizeof(bf16_t)) +
-                             16 * (slot ^ swz_k<D>(row));
+                             16 * (slot ^ swz_b<D>(row));
         lds_load16(rk, st + blk * 512, off);
         lds_load16(rv, st + C::TSZ + blk * 512, off);
       }
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
   // row reads (K for S^T, V for dP^T): row j (+ 32 n), chunk 2c + hf
   int kad[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) kad[c] = j * D + 8 * ((2 * c + hf) ^ swz_k<D>(j));
+  for (int c = 0; c < D / 16; ++c) kad[c] = j * D + 8 * ((2 * c + hf) ^ swz_b<D>(j));
   // transposing K reads: 16-lane group g reads keys 4 (g / 2) + lane % 16 / 4
   // (+ 8 e, + 16 kc) at columns 32 i + 16 (g % 2) + 4 (lane % 4)
   int ktr[2][D / 32];
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
       const int row = 4 * hf + ((lane & 15) >> 2) + 8 * e;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
-        ktr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_k<D>(row)) + 4 * (lane & 1);
+        ktr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_b<D>(row)) + 4 * (lane & 1);
     }
   }
 
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
         const int u = blk * 64 + lane;
         const int row = u / C::CPR, slot = u % C::CPR;
         lds_load16(rv, vtile + blk * 512,
-                   (uint32_t)(((k0 + row) * rs) * sizeof(bf16_t)) + 16 * (slot ^ swz_k<D>(row)));
+                   (uint32_t)(((k0 + row) * rs) * sizeof(bf16_t)) + 16 * (slot ^ swz_b<D>(row)));
       }
     }
   }
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
         const int u = blk * 64 + lane;
         const int row = u / C::CPR, slot = u % C::CPR;
         const uint32_t off = (uint32_t)(((q0 + row) * qs) * sizeof(bf16_t)) +
-                             16 * (slot ^ swz_k<D>(row));
+                             16 * (slot ^ swz_b<D>(row));
         lds_load16(rq, st + blk * 512, off);
         lds_load16(rdo, st + C::QSZ + blk * 512, off);
       }
@@ -530,8 +531,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   int qad[D / 16], vad[D / 16], qtr[2][D / 32];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    qad[c] = j * D + 8 * ((2 * c + hf) ^ swz_k<D>(j));
-    vad[c] = (32 * w + j) * D + 8 * ((2 * c + hf) ^ swz_k<D>(32 * w + j));
+    qad[c] = j * D + 8 * ((2 * c + hf) ^ swz_b<D>(j));
+    vad[c] = (32 * w + j) * D + 8 * ((2 * c + hf) ^ swz_b<D>(32 * w + j));
   }
   {
     const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
       const int row = 4 * hf + ((lane & 15) >> 2) + 8 * e;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
-        qtr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_k<D>(row)) + 4 * (lane & 1);
+        qtr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_b<D>(row)) + 4 * (lane & 1);
     }
   }
 
