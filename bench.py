@@ -211,7 +211,7 @@ def main():
     H, W = to_dev(h, dev), to_dev(w, dev)
     del w
     # the LM-head weights are packed once, as at model load: the same products,
-    # read as contiguous 16 KiB blocks per GEMM stage
+    # read as contiguous 20 KiB blocks per GEMM stage
     W = mars.mars_lmhead_pack(W)
     torch.cuda.synchronize()
     logits = torch.empty((N, LM["V"]), dtype=torch.float32, device=dev)
