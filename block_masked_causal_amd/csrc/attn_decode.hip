@@ -365,20 +365,45 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
 
   const size_t base = (((size_t)s * p.Hkv + kvh) * p.nsplit) * p.nrows_pad + qi;
   const size_t stride = p.nrows_pad;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, p.part_ml[(base + sp * stride) * 2]);
-  const float Mb = M == -INFINITY ? 0.f : M;
   constexpr int PER = D / 64;
+  // Chunks are taken kMergeBatch at a time with all their loads in flight
+  // (one memory round trip per batch, not two per chunk), in chunk order. A
+  // later batch that raises the maximum rescales what came before; with at
+  // most kMergeBatch chunks the arithmetic is a single fixed-order pass.
+  constexpr int kMergeBatch = 8;
+  float M = -INFINITY, lsum = 0.f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  for (int sp = 0; sp < nsp; ++sp) {
-    const size_t row = base + sp * stride;
-    const float w = fast_exp2(p.part_ml[row * 2] - Mb);
-    lsum += w * p.part_ml[row * 2 + 1];
+  for (int sp0 = 0; sp0 < nsp; sp0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * p.part_o[row * D + lane * PER + e];
+    for (int t = 0; t < kMergeBatch; ++t) {
+      const bool in = sp0 + t < nsp;
+      const size_t row = base + (size_t)(in ? sp0 + t : sp0) * stride;
+      mv[t] = in ? p.part_ml[row * 2] : -INFINITY;
+      lv[t] = in ? p.part_ml[row * 2 + 1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[t][e] = in ? p.part_o[row * D + lane * PER + e] : 0.f;
+    }
+    float mt = M;
+#pragma unroll
+    for (int t = 0; t < kMergeBatch; ++t) mt = fmaxf(mt, mv[t]);
+    const float mb = mt == -INFINITY ? 0.f : mt;
+    if (M != -INFINITY && M != mt) {  // a later batch raised the maximum
+      const float sc = fast_exp2(M - mb);
+      lsum *= sc;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] *= sc;
+    }
+#pragma unroll
+    for (int t = 0; t < kMergeBatch; ++t) {
+      const float w = mv[t] == -INFINITY ? 0.f : fast_exp2(mv[t] - mb);
+      lsum += w * lv[t];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += w * ov[t][e];
+    }
+    M = mt;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int r = qi / p.group, h = kvh * p.group + qi % p.group;
