@@ -249,9 +249,9 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
   pv(3, p3);
 }
 
-// Workgroup = nw waves, each owning one (query head, 32-row tile). The heads
-// of one GQA group that share a K/V head sit side by side (gh heads x rt row
-// tiles = nw), so every K/V tile staged through LDS feeds 32 * nw query rows.
+// Workgroup = nw waves, each owning one (query head, 32-row tile): gh heads of
+// one GQA group x rt row tiles, so every K/V tile staged through LDS feeds
+// 32 * nw query rows. The launcher uses gh = 1, rt = 4 at both head sizes.
 template <int D>
 __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p) {
   using C = Cfg<D>;
