@@ -63,6 +63,11 @@ def test_fp32_matches_oracle(b, L, B, Hq, Hkv, d):
     (1, 256, 4, 8, 2, 128, 0),
     (1, 128, 4, 8, 2, 64, 0),
     (1, 256, 16, 4, 1, 128, 0),
+    # d = 128 with a 7-head GQA group (the 7B grouping): batch x KV heads = 8
+    # takes the XCD-striped workgroup order, 1 KV head the fallback order;
+    # both ragged (2L not a multiple of the 128-row workgroup tile)
+    (2, 84, 4, 28, 4, 128, 0),
+    (1, 100, 4, 7, 1, 128, 0),
 ])
 def test_bf16_matches_oracle(b, L, B, Hq, Hkv, d, mode):
     eo, el, _ = run_case(2000 + L, b, L, B, Hq, Hkv, d, "bf16", mode=mode)
