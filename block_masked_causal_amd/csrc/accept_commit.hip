@@ -47,10 +47,13 @@ __device__ __forceinline__ int accepted_count(const float* pr, int B, float tau)
   return n < 1 ? 1 : n;
 }
 
+constexpr int kCommitStageBytes = 16384;  // LDS staging of V rows in the commit
+
 template <int ES>  // element size in bytes (2 = bf16, 4 = fp32)
 __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
   __shared__ int sh_page[kMaxB];
   __shared__ int sh_len, sh_nc;
+  __shared__ __attribute__((aligned(16))) char vst[kCommitStageBytes];
   const int s = blockIdx.x, tid = threadIdx.x;
   if (tid < 64) {
     // Wave 0, lane r = position r: the accepted count is the run of set bits
@@ -105,21 +108,58 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
         ch * 16;
     *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_new + src);
   }
-  // V: [page][head][d][slot], one element per thread, slot fastest
-  for (int idx = tid; idx < nc * p.Hkv * p.D; idx += 256) {
-    const int r = idx % nc;
-    const int d = (idx / nc) % p.D;
-    const int kvh = idx / (nc * p.D);
-    const int pos = len + r;
-    const size_t src = ((((size_t)s * p.B + r) * p.Hkv + kvh) * p.D + d) * ES;
-    const size_t dst =
-        ((((size_t)sh_page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
-    if (ES == 2)
-      *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_new + src);
-    else
-      *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_new + src);
+  // V: [page][head][d][slot]. The accepted rows of one head are staged in LDS
+  // with 16-byte loads (a row is contiguous in v_new), then written one element
+  // per thread, slot fastest, so that neighbouring lanes store neighbouring
+  // slots. Rows too long for the staging buffer take the element path directly.
+  const int vrs = rowbytes + 4;  // padded LDS row stride
+  if (vrs <= kCommitStageBytes) {
+    const int G = kCommitStageBytes / vrs;  // rows per pass
+    for (int kvh = 0; kvh < p.Hkv; ++kvh) {
+      for (int r0 = 0; r0 < nc; r0 += G) {
+        const int g = min(G, nc - r0);
+        for (int idx = tid; idx < g * chunks; idx += 256) {
+          const int ch = idx % chunks;
+          const int r = idx / chunks;
+          const u32x4 x = *(const u32x4*)(p.v_new + (((size_t)s * p.B + r0 + r) * p.Hkv + kvh) *
+                                                        rowbytes + ch * 16);
+          uint32_t* d4 = (uint32_t*)(vst + r * vrs + ch * 16);
+          d4[0] = x[0];
+          d4[1] = x[1];
+          d4[2] = x[2];
+          d4[3] = x[3];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < g * p.D; idx += 256) {
+          const int r = idx % g;
+          const int d = idx / g;
+          const int pos = len + r0 + r;
+          const size_t dst = ((((size_t)sh_page[r0 + r] * p.Hkv + kvh) * p.D + d) * p.page_size +
+                              pos % p.page_size) * ES;
+          if (ES == 2)
+            *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(vst + r * vrs + d * 2);
+          else
+            *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(vst + r * vrs + d * 4);
+        }
+        __syncthreads();
+      }
+    }
+  } else {
+    for (int idx = tid; idx < nc * p.Hkv * p.D; idx += 256) {
+      const int r = idx % nc;
+      const int d = (idx / nc) % p.D;
+      const int kvh = idx / (nc * p.D);
+      const int pos = len + r;
+      const size_t src = ((((size_t)s * p.B + r) * p.Hkv + kvh) * p.D + d) * ES;
+      const size_t dst =
+          ((((size_t)sh_page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
+      if (ES == 2)
+        *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_new + src);
+      else
+        *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_new + src);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (tid == 0) p.cache_len[s] = len + nc;
 }
 
