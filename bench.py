@@ -22,7 +22,7 @@ kernels run on. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), the no-cache causal prefill and the paged KV
-append, a 64-step decode loop at the 7B shape under the batch-synchronous
+append, acceptance + commit with every row accepted, a 64-step decode loop at the 7B shape under the batch-synchronous
 block cache (both batch policies), per-token commit and one-token AR, and
 the CPU oracle timed on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
@@ -447,6 +447,10 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
     # that fills the paged cache from a prompt
     out["causal_prefill"] = causal_prefill(mars, synth, torch, dev, traffic)
 
+    # acceptance + commit with every row accepted (tau = 0) at the high-load loop's
+    # shape: the largest copy one call makes there
+    out["accept_commit_full"] = accept_commit_full(mars, torch, dev)
+
     # batched decode loop with a live tau switch
     out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
 
@@ -460,6 +464,46 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
                    "pages' end-to-end wall-clock ratios")
     out["decode_policies"] = pol
     return out
+
+
+def accept_commit_full(mars, torch, dev):
+    """mars_accept_commit at S=256, B=8 (Qwen2.5-7B KV heads) with tau = 0, so every
+    row is accepted and committed: 8.4 MB of K/V rows read and written per call."""
+    S, B, Hkv, d, page, steps = 256, 8, 4, 128, 16, 8
+    max_pages = (B * steps + page - 1) // page
+    g = torch.Generator(device="cpu").manual_seed(1010)
+    kc = torch.zeros(S * max_pages, Hkv, page, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros(S * max_pages, Hkv, d, page, dtype=torch.bfloat16, device=dev)
+    bt = torch.randperm(S * max_pages, generator=g).to(torch.int32).reshape(S, max_pages).to(dev)
+    kn = torch.randn(S, B, Hkv, d, generator=g).to(torch.bfloat16).to(dev)
+    vn = torch.randn(S, B, Hkv, d, generator=g).to(torch.bfloat16).to(dev)
+    pm = torch.ones(S, B, dtype=torch.float32, device=dev)
+    top = torch.zeros(S, B, dtype=torch.int32, device=dev)
+    tau = torch.zeros(S, dtype=torch.float32, device=dev)
+    cl = torch.zeros(S, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(4):
+        cl.zero_()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(steps):
+            mars.mars_accept_commit(pm, top, tau, kn, vn, kc, vc, bt, cl)
+        b.record()
+        torch.cuda.synchronize()
+        if rep > 0:
+            times.append(a.elapsed_time(b) / steps)
+    if int(cl.min().item()) != B * steps:
+        raise RuntimeError("full-acceptance commit did not place every row")
+    ms = sum(times) / len(times)
+    nbytes = S * B * Hkv * d * 2 * 2 * 2  # K and V rows, read and written
+    del kc, vc, bt, kn, vn
+    torch.cuda.empty_cache()
+    return {"shape": {"S": S, "B": B, "Hkv": Hkv, "d": d, "page": page}, "ms": round(ms, 4),
+            "roofline": roofline("hbm", nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                 None, nbytes),
+            "note": "tau = 0: all 8 rows of every sequence committed; one call per step"}
 
 
 def two_stream_bwd(mars, synth, torch, dev, traffic):
