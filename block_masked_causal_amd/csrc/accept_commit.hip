@@ -108,12 +108,14 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
         ch * 16;
     *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_new + src);
   }
-  // V: [page][head][d][slot]. The accepted rows of one head are staged in LDS
-  // with 16-byte loads (a row is contiguous in v_new), then written one element
-  // per thread, slot fastest, so that neighbouring lanes store neighbouring
-  // slots. Rows too long for the staging buffer take the element path directly.
+  // V: [page][head][d][slot]. With several rows, the accepted rows of one head
+  // are staged in LDS with 16-byte loads (a row is contiguous in v_new), then
+  // written one element per thread, slot fastest, so that neighbouring lanes
+  // store neighbouring slots. A single row (its loads already contiguous
+  // across lanes) and rows too long for the staging buffer take the element
+  // path directly.
   const int vrs = rowbytes + 4;  // padded LDS row stride
-  if (vrs <= kCommitStageBytes) {
+  if (nc > 1 && vrs <= kCommitStageBytes) {
     const int G = kCommitStageBytes / vrs;  // rows per pass
     for (int kvh = 0; kvh < p.Hkv; ++kvh) {
       for (int r0 = 0; r0 < nc; r0 += G) {
