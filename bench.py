@@ -17,8 +17,9 @@ that are resident in HBM before timing starts:
 
 The headline `value` is the useful (unmasked) TFLOP/s of the two-stream
 attention; `accepted_tokens_per_s` is the decode step's accepted tokens per
-second. Per-kernel times come from HIP events recorded on the stream the
-kernels run on. Extras (skippable with --no-extras): the two-pass LM head
+second over the sum of its segment times. Per-kernel times come from HIP events
+recorded on the stream the kernels run on. `decode_step_unmarked` runs the
+decode step again on its own with events only around the whole run. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), the no-cache causal prefill and the paged KV
@@ -194,7 +195,7 @@ def main():
     O = torch.empty_like(Q)
 
     log("generating decode inputs (7B shape) and LM head")
-    total_steps = args.steps + args.warmup
+    total_steps = 2 * args.steps + args.warmup  # the timed steps, then the decode-only loop
     di = synth.decode_inputs(1004, DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"],
                              DEC["lo"], DEC["hi"], DEC["page"],
                              extra_capacity=DEC["B"] * (total_steps + 2))
@@ -231,25 +232,26 @@ def main():
     timer = Timer(seg)
     dec_lens = []
 
+    def decode_part(i, mark):
+        mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO, workspace=dws,
+                                    status=status)
+        mark()
+        mars.mars_lmhead_confidence(H, W, None, top_id=top, p_max=pm, workspace=lws,
+                                    status=status, fused=True)
+        mark()
+        mars.mars_accept_commit(pm.view(DEC["S"], DEC["B"]), top.view(DEC["S"], DEC["B"]),
+                                taus[i % 3], dkn, dvn, kc, vc, bt, cl, n_accepted=n_acc,
+                                accepted_ids=acc_ids, commit_pos=cpos, status=status)
+        mark()
+
     def step(i, timed):
         if timed:
             timer.start()
         mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O)
         if timed:
             timer.mark()
-        mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO, workspace=dws,
-                                    status=status)
+        decode_part(i, timer.mark if timed else (lambda: None))
         if timed:
-            timer.mark()
-        mars.mars_lmhead_confidence(H, W, None, top_id=top, p_max=pm, workspace=lws,
-                                    status=status, fused=True)
-        if timed:
-            timer.mark()
-        mars.mars_accept_commit(pm.view(DEC["S"], DEC["B"]), top.view(DEC["S"], DEC["B"]),
-                                taus[i % 3], dkn, dvn, kc, vc, bt, cl, n_accepted=n_acc,
-                                accepted_ids=acc_ids, commit_pos=cpos, status=status)
-        if timed:
-            timer.mark()
             timer.stop()
 
     if args.profile_pass:
@@ -295,6 +297,23 @@ def main():
     if st != 0:
         log(f"WARNING: device status flags {st}")
 
+    # The decode step again, on its own and timed as a whole: one HIP event before
+    # the first step and one after the last, none between its kernels (the
+    # markers between segments above add the command processor's gap to each).
+    lens_dec0 = cl.cpu().numpy().copy()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        decode_part(i, lambda: None)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_whole_ms = e0.elapsed_time(e1) / args.steps
+    acc_whole = int((cl.cpu().numpy() - lens_dec0).sum())
+    if int(status.item()) != 0:
+        log(f"WARNING: device status flags {int(status.item())}")
+
     ms_step = wall * 1e3 / args.steps
     t_ts = timer.mean_ms("two_stream")
     t_dec = timer.mean_ms("decode_attn")
@@ -308,7 +327,7 @@ def main():
     mean_len = 0.5 * (lens_before + lens_after)
     dflops, dbytes = decode_flops_bytes(mean_len, DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"])
     lm_flops = 2.0 * N * LM["D"] * LM["V"]
-    nvt = (LM["V"] + 255) // 256
+    nvt = (LM["V"] + 319) // 320  # 320-entry vocabulary tiles
     # fused: W and hidden read once; per-(row, vocabulary tile) partials written and merged
     lmf_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + 2 * N * nvt * 16
     lm_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + N * LM["V"] * 4
@@ -361,6 +380,11 @@ def main():
         },
         "accepted_tokens_per_s": round(acc_tok_s, 1),
         "decode_step_ms": round(decode_ms, 4),
+        "decode_step_unmarked": {
+            "ms": round(dec_whole_ms, 4),
+            "accepted_tokens_per_s": round(acc_whole / (args.steps * dec_whole_ms * 1e-3), 1),
+            "note": "the same decode step run on its own, timed with one event pair around "
+                    "all steps (no markers between its kernels)"},
         "kernel_ms": {k2: round(v2, 4) for k2, v2 in times.items()},
         "roofline": kernels["two_stream_attention"],
         "kernels": kernels,
