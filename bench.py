@@ -19,7 +19,9 @@ The headline `value` is the useful (unmasked) TFLOP/s of the two-stream
 attention; `accepted_tokens_per_s` is the decode step's accepted tokens per
 second over the sum of its segment times. Per-kernel times come from HIP events
 recorded on the stream the kernels run on. `decode_step_unmarked` runs the
-decode step again on its own with events only around the whole run. Extras (skippable with --no-extras): the two-pass LM head
+decode step again on its own with events only around the whole run, and
+`kernel_ms_back_to_back` times the attention and LM-head calls launched 20
+times in a row. Extras (skippable with --no-extras): the two-pass LM head
 (GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
 at the 7B two-stream shape, a 64-step batched decode loop with a live tau
 switch (accepted tokens/s), the no-cache causal prefill and the paged KV
@@ -195,7 +197,8 @@ def main():
     O = torch.empty_like(Q)
 
     log("generating decode inputs (7B shape) and LM head")
-    total_steps = 2 * args.steps + args.warmup  # the timed steps, then the decode-only loop
+    # the timed steps and the decode-only loop both commit
+    total_steps = 2 * args.steps + args.warmup
     di = synth.decode_inputs(1004, DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"],
                              DEC["lo"], DEC["hi"], DEC["page"],
                              extra_capacity=DEC["B"] * (total_steps + 2))
@@ -311,6 +314,30 @@ def main():
     torch.cuda.synchronize()
     dec_whole_ms = e0.elapsed_time(e1) / args.steps
     acc_whole = int((cl.cpu().numpy() - lens_dec0).sum())
+
+    # Each call of the step on its own, launched back to back: one event pair
+    # around 20 launches (after 3 untimed), for comparison with the in-step times
+    def back_to_back(fn, n=20):
+        for _ in range(3):
+            fn()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        for _ in range(n):
+            fn()
+        b_.record()
+        torch.cuda.synchronize()
+        return a_.elapsed_time(b_) / n
+
+    b2b = {
+        "two_stream_attention": back_to_back(
+            lambda: mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O)),
+        "block_decode_attention": back_to_back(
+            lambda: mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO,
+                                                workspace=dws, status=status)),
+        "lmhead_confidence_fused": back_to_back(
+            lambda: mars.mars_lmhead_confidence(H, W, None, top_id=top, p_max=pm,
+                                                workspace=lws, status=status, fused=True)),
+    }  # (the commit kernel is shorter than a host launch, so it is not timed this way)
     if int(status.item()) != 0:
         log(f"WARNING: device status flags {int(status.item())}")
 
@@ -380,6 +407,9 @@ def main():
         },
         "accepted_tokens_per_s": round(acc_tok_s, 1),
         "decode_step_ms": round(decode_ms, 4),
+        "kernel_ms_back_to_back": {k: round(v, 4) for k, v in b2b.items()},
+        "two_stream_back_to_back_tflops": round(ts_flops / (b2b["two_stream_attention"] * 1e-3)
+                                                / 1e12, 3),
         "decode_step_unmarked": {
             "ms": round(dec_whole_ms, 4),
             "accepted_tokens_per_s": round(acc_whole / (args.steps * dec_whole_ms * 1e-3), 1),
