@@ -53,6 +53,15 @@ def test_decode_lengths_on_chunk_and_page_edges():
     assert err <= TOL and st == 0, (err, st)
 
 
+def test_decode_more_than_eight_chunks():
+    """Caches longer than eight 512-key chunks: the merge takes the chunk partials
+    eight at a time and rescales across batches when a later batch raises a row's
+    maximum (4096 keys = exactly eight chunks, then 9, 9, 10 and 18)."""
+    lens = [4096, 4097, 4608, 5120, 9000]
+    err, st = run(3400, len(lens), 4, 8, 2, 128, 0, 9000, 16, lens=lens)
+    assert err <= TOL and st == 0, (err, st)
+
+
 def test_decode_large_batch_uses_512_key_chunks_on_edges():
     """130 sequences x 8 KV heads, 512-key chunks;
     lengths sit on both sides of the chunk and single-chunk boundaries."""
