@@ -26,7 +26,8 @@ comparisons are p >= tau.
 
 Parity-pin status: every function below is pinned by tests other than itself
 (brute force, closed forms, library routines, printed values, central finite
-differences for the attention gradient). None is "parity unpinned".
+differences for the attention gradient), useful_pairs_two_stream included (the
+closed forms L(L+1) and L(2L+1)). None is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -498,6 +499,7 @@ def block_freeze(k_cache, v_cache, block_table, cache_len, k_rows, v_rows, unfro
 
 
 def useful_pairs_two_stream(L: int, B: int, mask_mode: int = 0) -> int:
-    """Number of visible (query, key) pairs per head under the explicit mask."""
+    """Number of visible (query, key) pairs per head under the explicit mask
+    ([notes] 关键设计 1); mask_mode 1 counts plain causal attention over 2L."""
     M = build_mask(L, B) if mask_mode == 0 else causal_mask(2 * L)
     return int(M.sum())

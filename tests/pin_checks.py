@@ -74,6 +74,16 @@ def check_mask_closed_forms(build, cases=((7, 3), (16, 4), (33, 8), (64, 16), (1
         assert not M[:L, L:].any()
 
 
+def check_useful_pairs(count, cases=((1, 1), (5, 2), (7, 3), (16, 4), (33, 8), (12, 1),
+                                      (9, 9), (64, 16), (10, 4))):
+    """Visible (query, key) pairs per head: every MARS row a < L sees a + 1 keys and
+    every mask row t sees t + 1 (whatever B is, B | L or not), so the mask holds
+    L(L + 1) pairs; plain causal attention over 2L positions holds L(2L + 1)."""
+    for L, B in cases:
+        assert count(L, B, 0) == L * (L + 1), (L, B, "mars")
+        assert count(L, B, 1) == L * (2 * L + 1), (L, B, "causal-2L")
+
+
 def check_mask_b1(build, L: int = 11):
     M = build(L, 1)
     for t in range(L):

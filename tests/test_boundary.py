@@ -230,6 +230,156 @@ def test_binding_rejects_cpu_tensors_before_calling():
         mars.mars_attn_two_stream(q, q, q, 4, 2)
 
 
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _shape_error(fn, *args, match, **kw):
+    """The call must fail on the named shape check, not on the GPU-residency check
+    that comes last (these tensors live on the CPU)."""
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def _gpu_error(fn, *args, **kw):
+    """Shapes are right: the only complaint left is that the tensors are on the CPU."""
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fn(*args, **kw)
+
+
+def _decode_set(S=2, B=4, Hq=4, Hkv=2, d=64, pages=6, page=16, max_pages=3):
+    import torch
+    return dict(q=_cpu((S, B, Hq, d)), k_new=_cpu((S, B, Hkv, d)), v_new=_cpu((S, B, Hkv, d)),
+                k_cache=_cpu((pages, Hkv, page, d)), v_cache=_cpu((pages, Hkv, d, page)),
+                block_table=_cpu((S, max_pages), torch.int32), cache_len=_cpu((S,), torch.int32))
+
+
+def test_binding_checks_every_shape_of_the_decode_call():
+    import torch
+    a = _decode_set()
+    call = lambda **kw: mars.mars_attn_block_decode(*[{**a, **kw}[n] for n in (
+        "q", "k_new", "v_new", "k_cache", "v_cache", "block_table", "cache_len")],
+        **{k: v for k, v in kw.items() if k in ("o", "n_rows", "workspace", "status")})
+    _gpu_error(call)
+    _shape_error(call, match="o must have shape", o=_cpu((2, 4, 4, 32)))
+    _shape_error(call, match="k_new must have shape", k_new=_cpu((2, 3, 2, 64)))
+    _shape_error(call, match="v_new must have shape", v_new=_cpu((2, 4, 1, 64)))
+    _shape_error(call, match="k_cache must be", k_cache=_cpu((6, 2, 16, 32)))
+    _shape_error(call, match="v_cache must have shape", v_cache=_cpu((6, 2, 16, 64)))
+    _shape_error(call, match="block_table must have 2 rows",
+                 block_table=_cpu((3, 3), torch.int32))
+    _shape_error(call, match="cache_len must have shape", cache_len=_cpu((3,), torch.int32))
+    _shape_error(call, match="n_rows must have shape", n_rows=_cpu((1,), torch.int32))
+    _shape_error(call, match="workspace holds", workspace=_cpu((16,), torch.uint8))
+    _shape_error(call, match="status must hold", status=_cpu((0,), torch.int32))
+
+
+def test_binding_checks_every_shape_of_accept_commit():
+    import torch
+    a = _decode_set(B=4)
+    S, B = 2, 4
+    base = dict(p_max=_cpu((S, B), torch.float32), top_id=_cpu((S, B), torch.int32),
+                tau=_cpu((S,), torch.float32), k_new=a["k_new"], v_new=a["v_new"],
+                k_cache=a["k_cache"], v_cache=a["v_cache"], block_table=a["block_table"],
+                cache_len=a["cache_len"])
+    names = list(base)
+
+    def call(**kw):
+        args = {**base, **kw}
+        outs = {k: v for k, v in kw.items() if k in ("n_accepted", "accepted_ids",
+                                                      "commit_pos", "status")}
+        return mars.mars_accept_commit(*[args[n] for n in names], **outs)
+
+    _gpu_error(call)
+    _shape_error(call, match="top_id must have shape", top_id=_cpu((S, B + 1), torch.int32))
+    _shape_error(call, match="tau must have shape", tau=_cpu((S + 1,), torch.float32))
+    _shape_error(call, match="cache_len must have shape", cache_len=_cpu((1,), torch.int32))
+    _shape_error(call, match="block_table must have 2 rows",
+                 block_table=_cpu((1, 3), torch.int32))
+    _shape_error(call, match="k_new must have shape", k_new=_cpu((S, B - 1, 2, 64)))
+    _shape_error(call, match="v_new must have shape", v_new=_cpu((S, B, 2, 32)))
+    _shape_error(call, match="k_cache must be", k_cache=_cpu((6, 1, 16, 64)))
+    _shape_error(call, match="v_cache must have shape", v_cache=_cpu((6, 2, 16, 64)))
+    _shape_error(call, match="n_accepted must have shape",
+                 n_accepted=_cpu((S + 1,), torch.int32))
+    _shape_error(call, match="accepted_ids must have shape",
+                 accepted_ids=_cpu((S, B - 1), torch.int32))
+    _shape_error(call, match="commit_pos must have shape",
+                 commit_pos=_cpu((S, 1), torch.int32))
+
+
+def test_binding_checks_shapes_of_append_freeze_and_block_sync():
+    import torch
+    S, T, Hkv, d = 2, 5, 2, 64
+    kr, vr = _cpu((S, T, Hkv, d)), _cpu((S, T, Hkv, d))
+    kc, vc = _cpu((6, Hkv, 16, d)), _cpu((6, Hkv, d, 16))
+    bt, cl = _cpu((S, 3), torch.int32), _cpu((S,), torch.int32)
+    _gpu_error(mars.mars_kv_append, kr, vr, kc, vc, bt, cl)
+    _shape_error(mars.mars_kv_append, kr, _cpu((S, T - 1, Hkv, d)), kc, vc, bt, cl,
+                 match="v_rows must have shape")
+    _shape_error(mars.mars_kv_append, kr, vr, kc, _cpu((6, Hkv, 16, d)), bt, cl,
+                 match="v_cache must have shape")
+    _shape_error(mars.mars_kv_append, kr, vr, kc, vc, bt, _cpu((S + 2,), torch.int32),
+                 match="cache_len must have shape")
+    un = _cpu((S,), torch.int32)
+    _gpu_error(mars.mars_block_freeze, kr, vr, kc, vc, bt, cl, un, 4)
+    _shape_error(mars.mars_block_freeze, kr, vr, kc, vc, bt, cl, _cpu((S + 1,), torch.int32),
+                 4, match="unfrozen must have shape")
+    _shape_error(mars.mars_block_freeze, kr, vr, kc, vc, _cpu((S + 1, 3), torch.int32), cl,
+                 un, 4, match="block_table must have")
+    pm, ids, tau = _cpu((S, 4), torch.float32), _cpu((S, 4), torch.int32), _cpu((S,),
+                                                                               torch.float32)
+    toks = _cpu((S, 8), torch.int32)
+    _gpu_error(mars.mars_block_sync_accept, pm, ids, tau, un, toks)
+    _shape_error(mars.mars_block_sync_accept, pm, ids, _cpu((1,), torch.float32), un, toks,
+                 match="tau must have shape")
+    _shape_error(mars.mars_block_sync_accept, pm, ids, tau, un, _cpu((S + 1, 8), torch.int32),
+                 match="block_tokens must have")
+    _shape_error(mars.mars_block_sync_accept, pm, ids, tau, un, toks,
+                 n_rows=_cpu((S + 1,), torch.int32), match="n_rows must have shape")
+
+
+def test_binding_checks_shapes_of_attention_calls():
+    import torch
+    b, L, Hq, Hkv, d = 1, 8, 4, 2, 64
+    q, k = _cpu((b, 2 * L, Hq, d)), _cpu((b, 2 * L, Hkv, d))
+    _gpu_error(mars.mars_attn_two_stream, q, k, k, L, 2)
+    _shape_error(mars.mars_attn_two_stream, q, k, k, L + 1, 2, match="2L")
+    _shape_error(mars.mars_attn_two_stream, q, k, _cpu((b, 2 * L, Hkv, 32)), L, 2,
+                 match="v must have shape")
+    _shape_error(mars.mars_attn_two_stream, q, k, k, L, 2, o=_cpu((b, 2 * L, Hq, 32)),
+                 match="o must have shape")
+    _shape_error(mars.mars_attn_two_stream, q, k, k, L, 2,
+                 lse=_cpu((b, Hq, L), torch.float32), match="lse must have shape")
+    _shape_error(mars.mars_attn_causal, q, k, k, o=_cpu((b, 2 * L, Hq + 1, d)),
+                 match="o must have shape")
+    lse = _cpu((b, Hq, 2 * L), torch.float32)
+    _gpu_error(mars.mars_attn_two_stream_bwd, q, k, k, q, q, lse, L, 2)
+    _shape_error(mars.mars_attn_two_stream_bwd, q, k, k, q, q, lse, L, 2,
+                 dk=_cpu((b, 2 * L, Hq, d)), match="dk must have shape")
+    _shape_error(mars.mars_attn_two_stream_bwd, q, k, k, q, q, lse, L, 2,
+                 workspace=_cpu((8,), torch.uint8), match="workspace holds")
+    _shape_error(mars.mars_attn_two_stream_bwd, q, k, k, _cpu((b, 2 * L, Hq, 32)), q, lse, L,
+                 2, match="o must have shape")
+
+
+def test_binding_checks_shapes_of_the_lm_head_call():
+    import torch
+    N, D, V = 4, 64, 128
+    h, w = _cpu((N, D)), _cpu((V, D))
+    _gpu_error(mars.mars_lmhead_confidence, h, w)
+    _shape_error(mars.mars_lmhead_confidence, h, _cpu((V, D + 32)), match="w_lm must be")
+    _shape_error(mars.mars_lmhead_confidence, h, w, _cpu((N, V + 4), torch.float32),
+                 match="logits must have shape")
+    _shape_error(mars.mars_lmhead_confidence, h, w, top_id=_cpu((N + 1,), torch.int32),
+                 match="top_id must have shape")
+    _shape_error(mars.mars_lmhead_confidence, h, w, p_max=_cpu((N - 1,), torch.float32),
+                 match="p_max must have shape")
+    _shape_error(mars.mars_lmhead_confidence, None, None, _cpu((N, V), torch.float32),
+                 workspace=_cpu((1,), torch.uint8), match="workspace holds")
+
+
 def test_oracle_is_not_imported_by_the_package():
     import sys
     for name in list(sys.modules):

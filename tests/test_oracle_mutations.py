@@ -329,3 +329,22 @@ def test_block_decode_rows_mutants_are_caught():
                                              page_size)
     assert _fails(pc.check_block_decode_rows_vs_causal, all_rows, oracle.attn_causal)
     assert _fails(pc.check_block_decode_rows_vs_causal, short_prefix, oracle.attn_causal)
+
+
+def test_useful_pair_count_mutants_are_caught():
+    def ignores_mode(L, B, mask_mode=0):
+        return oracle.useful_pairs_two_stream(L, B, 0)
+
+    def causal_over_L(L, B, mask_mode=0):
+        return int(om.causal_mask(L).sum()) if mask_mode else oracle.useful_pairs_two_stream(L, B)
+
+    def from_mask(mutant):
+        def count(L, B, mask_mode=0):
+            if mask_mode:
+                return oracle.useful_pairs_two_stream(L, B, 1)
+            return int(mutant(L, B).sum())
+        count.__name__ = mutant.__name__
+        return count
+
+    for m in (ignores_mode, causal_over_L, from_mask(mask_case3_le), from_mask(mask_no_self)):
+        assert _fails(pc.check_useful_pairs, m), m.__name__

@@ -30,6 +30,19 @@ def test_mask_closed_forms():
     pc.check_mask_closed_forms(oracle.build_mask)
 
 
+def test_useful_pair_count_closed_forms():
+    pc.check_useful_pairs(oracle.useful_pairs_two_stream)
+
+
+def test_bench_useful_flops_agree_with_the_oracle_pair_count():
+    import bench
+    for L, B in ((5, 2), (16, 4), (12, 1), (9, 9), (4096 // 64, 16)):
+        for mode in (0, 1):
+            for d in (32, 64, 128):
+                want = 4 * d * oracle.useful_pairs_two_stream(L, B, mode)
+                assert bench.useful_two_stream_flops(1, L, B, 1, d, mode) == want
+
+
 def test_mask_b1_sees_strictly_earlier_clean_tokens():
     pc.check_mask_b1(oracle.build_mask)
 
