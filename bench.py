@@ -1,40 +1,46 @@
 #!/usr/bin/env python3
 """Benchmark of the MARS hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--profile-pass]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+                    [--profile-pass PLAN_JSON]
 
 A step is one pass of the whole hot path over synthetic, Qwen2.5-shaped inputs
 that are resident in HBM before timing starts:
-  1. two-stream MARS attention forward: batch 8, L = 2048 (2L = 4096), B = 4,
-     14 query / 2 KV heads, head_dim 64, bf16;
-  2. one block-decode step at the Qwen2.5-7B shape: 64 sequences with cached
-     prefixes U[512, 4096], B = 4 mask queries, 28/4 heads, head_dim 128:
-     decode attention over the paged cache -> LM head (3584 x 152064, bf16
-     weights, packed once at setup into the GEMM's tile layout) with the
-     confidence reduced in the GEMM epilogue (no logits written) ->
-     acceptance (tau cycling 1.0 / 0.9 / 0.7) + KV commit of the accepted
-     prefix.
+  1. two-stream MARS attention forward at the Qwen2.5-7B training shape:
+     batch 4, L = 4096 (2L = 8192), B = 16, 28 query / 4 KV heads, head_dim
+     128, bf16 (the headline `value`: useful TFLOP/s of this launch);
+  2. one block-decode step at the 7B shape: 64 sequences with cached prefixes
+     U[512, 4096], B = 4 mask queries: decode attention over the paged cache
+     -> LM head (3584 x 152064, bf16 weights packed once at setup into the
+     GEMM's tile layout) with the confidence reduced in the GEMM epilogue ->
+     acceptance (tau cycling 1.0 / 0.9 / 0.7) + KV commit of the prefix;
+  3. the high-load decode loop: 256 sequences, B = 8, prompts U[128, 2048],
+     64 decode steps (decode attention -> confidence over 2048 x 152064 fp32
+     logits -> acceptance + commit of variable accepted lengths), tau switched
+     from 0.9 to 0.6 before step 32 by one fill of the same tau buffer. The
+     loop restarts from the prompt lengths at every bench step; its per-step
+     Q/K/V rows and synthetic logits (per-row peak probability ~ Beta(5, 1))
+     are materialised in HBM at setup (64 x 1.25 GB of logits).
+`accepted_tokens_per_s` is the loop's accepted tokens over its time (one HIP
+event pair around the 64 steps). Per-segment times come from HIP events
+recorded on the stream the kernels run on.
 
-The headline `value` is the useful (unmasked) TFLOP/s of the two-stream
-attention; `accepted_tokens_per_s` is the decode step's accepted tokens per
-second over the sum of its segment times. Per-kernel times come from HIP events
-recorded on the stream the kernels run on. `decode_step_unmarked` runs the
-decode step again on its own with events only around the whole run, and
-`kernel_ms_back_to_back` times the attention and LM-head calls launched 20
-times in a row. Extras (skippable with --no-extras): the two-pass LM head
-(GEMM writing fp32 logits, then the confidence kernels), the tile-skipping benefit
-at the 7B two-stream shape, a 64-step batched decode loop with a live tau
-switch (accepted tokens/s), the no-cache causal prefill and the paged KV
-append, acceptance + commit with every row accepted, a 64-step decode loop at the 7B shape under the batch-synchronous
-block cache (both batch policies), per-token commit and one-token AR, and
-the CPU oracle timed on a bounded sample.
+Extras (skippable with --no-extras): the 7B two-stream shape in causal-2L
+mode (the tile-skipping benefit), the 0.5B two-stream shape, per-kernel times
+of the decode loop, the two-pass LM head and the confidence alone, the
+attention backward at both training shapes, the causal prefill and the paged
+KV append, the commit sweep, the batch-synchronous block cache beside
+per-token commit and one-token AR, and the CPU oracle timed on bounded
+samples of the 7B two-stream shape, the decode step and the decode loop.
 Prints one JSON line on stdout; progress goes to stderr.
 
 `roofline.traffic` is the HBM bytes one launch moves, from two rocprofv3
-counter runs of `--profile-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled
-by what the counter reads for a plain copy of known size; it is null when the
-kernel sources changed after the counters were taken. `--profile-pass` copies
-a 1 GiB buffer once and then launches every hot-path kernel once.
+counter runs of `--profile-pass` (FETCH_SIZE, then WRITE_SIZE), each scaled by
+what the counter reads for a plain copy of known size; it is null when the
+kernel sources changed after the counters were taken. `--profile-pass PLAN`
+copies a 1 GiB buffer once, then launches every hot-path call once, each
+preceded by a one-element int64 fill that marks where its dispatches begin,
+and writes the order of the calls to PLAN.
 """
 
 from __future__ import annotations
@@ -55,15 +61,16 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # workload shapes
-TS = dict(batch=8, L=2048, B=4, Hq=14, Hkv=2, d=64)           # two-stream, 0.5B shape
-TS7 = dict(batch=4, L=4096, B=16, Hq=28, Hkv=4, d=128)        # two-stream, 7B shape
+TS3 = dict(batch=4, L=4096, B=16, Hq=28, Hkv=4, d=128)        # two-stream, 7B shape (headline)
+TS2 = dict(batch=8, L=2048, B=4, Hq=14, Hkv=2, d=64)           # two-stream, 0.5B shape
 DEC = dict(S=64, B=4, Hq=28, Hkv=4, d=128, lo=512, hi=4096, page=16)
 LM = dict(D=3584, V=152064)
+LOOP = dict(S=256, B=8, Hq=28, Hkv=4, d=128, lo=128, hi=2048, page=16, steps=64, switch=32,
+            tau0=0.9, tau1=0.6)
 PRE = dict(batch=8, T=4096 + 4, Hq=14, Hkv=2, d=64)              # no-cache prefill, 0.5B
 APP = dict(S=64, T=2048, Hkv=4, d=128, page=16)                  # prompt KV append, 7B
 BCL = dict(S=16, B=4, B_cache=16, Hq=28, Hkv=4, d=128, lo=512, hi=2048, page=16, steps=64,
            tau=0.95)                                               # block cache, 7B, batch 16
-LOOP = dict(S=256, B=8, Hq=28, Hkv=4, d=128, lo=128, hi=2048, page=16, steps=64, switch=32)
 
 
 def log(msg):
@@ -76,6 +83,11 @@ def useful_two_stream_flops(batch, L, B, Hq, d, mask_mode=0):
     causal over 2L sees L(2L+1)."""
     pairs = L * (L + 1) if mask_mode == 0 else L * (2 * L + 1)
     return 4.0 * d * pairs * Hq * batch
+
+
+def two_stream_bytes(c):
+    """Q, K, V read once and O written once (bf16)."""
+    return c["batch"] * 2 * c["L"] * c["d"] * 2 * (2 * c["Hq"] + 2 * c["Hkv"])
 
 
 def decode_flops_bytes(cache_len, B, Hq, Hkv, d):
@@ -94,6 +106,16 @@ def to_dev(t, dev):
         return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(
             torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(getattr(t, "f32", t))).to(dev)
+
+
+def cpu_threads():
+    """(threads the oracle's BLAS uses, CPUs in this process's affinity set). The
+    thread count is the affinity set, capped by OMP_NUM_THREADS where that is set
+    (the host's CPU share on a shared GPU machine)."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    n = min(aff, int(env)) if env and env.isdigit() and int(env) > 0 else aff
+    return n, aff
 
 
 class Timer:
@@ -128,6 +150,9 @@ class Timer:
     def mean_ms(self, n):
         return float(np.mean(self.samples[n]))
 
+    def median_ms(self, n):
+        return float(np.median(self.samples[n]))
+
 
 def roofline(bound, achieved, peak, unit, traffic=None, algorithmic_bytes=None):
     r = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
@@ -138,29 +163,240 @@ def roofline(bound, achieved, peak, unit, traffic=None, algorithmic_bytes=None):
     return r
 
 
-def cpu_baseline(q, k, v, budget_s):
-    """The oracle's two-stream attention, timed on whole heads of the 0.5B shape."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    L, B, d = TS["L"], TS["B"], TS["d"]
-    t0 = time.perf_counter()
-    heads = 0
-    for pair in [(b, h) for b in range(TS["batch"]) for h in range(TS["Hq"])]:
-        oracle.attn_two_stream(q.f32, k.f32, v.f32, L, B, pairs=[pair])
-        heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = useful_two_stream_flops(1, L, B, heads, d)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} of {TS['batch'] * TS['Hq']} (batch, head) pairs of the "
-                      f"two-stream 0.5B-shape attention, all {2 * L} rows, float64 numpy "
-                      f"({dt:.1f} s)"}
+def timed(torch, fn, reps=5, warm=2):
+    """Mean ms of `reps` back-to-back launches of fn (one event pair around them)."""
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+
+class TwoStream:
+    """Two-stream attention inputs of one shape, resident on the device."""
+
+    def __init__(self, mars, synth, torch, dev, c, seed, keep_host=False):
+        self.mars, self.c = mars, c
+        q, k, v = synth.two_stream_qkv(seed, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
+        self.Q, self.K, self.V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
+        self.host = (q, k, v) if keep_host else None
+        self.O = torch.empty_like(self.Q)
+
+    def run(self, mask_mode=0):
+        c = self.c
+        self.mars.mars_attn_two_stream(self.Q, self.K, self.V, c["L"], c["B"], o=self.O,
+                                       mask_mode=mask_mode)
+
+
+class DecodeStep:
+    """The 7B block-decode step (64 sequences, B = 4) with the packed LM head."""
+
+    def __init__(self, mars, synth, torch, dev, total_steps, keep_host=False):
+        self.mars, self.torch = mars, torch
+        c = DEC
+        di = synth.decode_inputs(1004, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["lo"],
+                                 c["hi"], c["page"], extra_capacity=c["B"] * (total_steps + 2))
+        self.q, self.kn, self.vn = to_dev(di.q, dev), to_dev(di.k_new, dev), to_dev(di.v_new, dev)
+        self.kc, self.vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+        self.bt, self.cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
+        self.max_pages = di.max_pages
+        self.o = torch.empty_like(self.q)
+        self.dws = torch.empty(mars.mars_decode_workspace_bytes(
+            c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["page"], self.max_pages),
+            dtype=torch.uint8, device=dev)
+        self.N = N = c["S"] * c["B"]
+        h, w = synth.lmhead_inputs(1004, N, LM["D"], LM["V"])
+        self.H, W = to_dev(h, dev), to_dev(w, dev)
+        self.host = (di, h, w) if keep_host else None
+        # the LM-head weights are packed once, as at model load: the same products,
+        # read as contiguous 20 KiB blocks per GEMM stage
+        self.W = mars.mars_lmhead_pack(W)
+        del W
+        self.logits = torch.empty((N, LM["V"]), dtype=torch.float32, device=dev)
+        self.top = torch.empty(N, dtype=torch.int32, device=dev)
+        self.pm = torch.empty(N, dtype=torch.float32, device=dev)
+        self.lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]),
+                               dtype=torch.uint8, device=dev)
+        self.taus = [torch.full((c["S"],), t, dtype=torch.float32, device=dev)
+                     for t in (1.0, 0.9, 0.7)]
+        self.n_acc = torch.empty(c["S"], dtype=torch.int32, device=dev)
+        self.acc_ids = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+        self.cpos = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def attn(self):
+        self.mars.mars_attn_block_decode(self.q, self.kn, self.vn, self.kc, self.vc, self.bt,
+                                         self.cl, o=self.o, workspace=self.dws,
+                                         status=self.status)
+
+    def lmhead(self):
+        self.mars.mars_lmhead_confidence(self.H, self.W, None, top_id=self.top, p_max=self.pm,
+                                         workspace=self.lws, status=self.status, fused=True)
+
+    def lmhead_two_pass(self):
+        self.mars.mars_lmhead_confidence(self.H, self.W, self.logits, top_id=self.top,
+                                         p_max=self.pm, workspace=self.lws, status=self.status)
+
+    def confidence_only(self):
+        self.mars.mars_lmhead_confidence(None, None, self.logits, top_id=self.top, p_max=self.pm,
+                                         workspace=self.lws, status=self.status)
+
+    def accept(self, i):
+        c = DEC
+        self.mars.mars_accept_commit(self.pm.view(c["S"], c["B"]), self.top.view(c["S"], c["B"]),
+                                     self.taus[i % 3], self.kn, self.vn, self.kc, self.vc,
+                                     self.bt, self.cl, n_accepted=self.n_acc,
+                                     accepted_ids=self.acc_ids, commit_pos=self.cpos,
+                                     status=self.status)
+
+
+class DecodeLoop:
+    """The high-load loop (S = 256, B = 8, 64 steps, tau 0.9 -> 0.6), every step's
+    inputs resident on the device."""
+
+    def __init__(self, mars, synth, torch, dev, n_runs, keep_host=False):
+        self.mars, self.torch = mars, torch
+        c = LOOP
+        log(f"  loop cache: S={c['S']} prompts U[{c['lo']},{c['hi']}]")
+        di = synth.decode_inputs(1005, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["lo"],
+                                 c["hi"], c["page"], extra_capacity=c["steps"] * c["B"])
+        self.kc, self.vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+        self.bt = to_dev(di.block_table, dev)
+        self.cl0 = to_dev(di.cache_len, dev)
+        self.cl = self.cl0.clone()
+        self.max_pages = di.max_pages
+        self.host = di if keep_host else None
+        del di
+        log(f"  loop rows: {c['steps']} steps of q / k_new / v_new")
+        self.Q, self.KN, self.VN = [], [], []
+        for s in range(c["steps"]):
+            q, kn, vn = synth.decode_step_tensors(1005, s, c["S"], c["B"], c["Hq"], c["Hkv"],
+                                                  c["d"])
+            self.Q.append(to_dev(q, dev))
+            self.KN.append(to_dev(kn, dev))
+            self.VN.append(to_dev(vn, dev))
+        N = self.N = c["S"] * c["B"]
+        log(f"  loop logits: {c['steps']} x [{N}, {LM['V']}] fp32 (planted Beta(5,1) peaks)")
+        self.pool = synth.PeakedLogitsPool(1005, N, LM["V"], taus=(c["tau0"], c["tau1"]))
+        pool_dev = torch.from_numpy(self.pool.pool).to(dev)
+        rows = torch.arange(N, device=dev)
+        self.logits = []
+        for s in range(c["steps"]):
+            ids, peak, _ = self.pool.peaks(s)
+            lg = pool_dev.clone()
+            lg[rows, torch.from_numpy(ids).to(dev)] = torch.from_numpy(peak).to(dev)
+            self.logits.append(lg)
+        del pool_dev
+        self.tau = torch.full((c["S"],), c["tau0"], dtype=torch.float32, device=dev)
+        self.o = torch.empty((c["S"], c["B"], c["Hq"], c["d"]), dtype=torch.bfloat16, device=dev)
+        self.dws = torch.empty(mars.mars_decode_workspace_bytes(
+            c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["page"], self.max_pages),
+            dtype=torch.uint8, device=dev)
+        self.lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8,
+                               device=dev)
+        self.top = torch.empty(N, dtype=torch.int32, device=dev)
+        self.pm = torch.empty(N, dtype=torch.float32, device=dev)
+        self.n_acc = torch.empty(c["S"], dtype=torch.int32, device=dev)
+        self.acc_ids = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+        self.cpos = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        # cache lengths at the tau switch and at the end of every run
+        self.mid = torch.empty((n_runs, c["S"]), dtype=torch.int32, device=dev)
+        self.end = torch.empty((n_runs, c["S"]), dtype=torch.int32, device=dev)
+
+    def attn(self, s):
+        self.mars.mars_attn_block_decode(self.Q[s], self.KN[s], self.VN[s], self.kc, self.vc,
+                                         self.bt, self.cl, o=self.o, workspace=self.dws,
+                                         status=self.status)
+
+    def conf(self, s):
+        self.mars.mars_lmhead_confidence(None, None, self.logits[s], top_id=self.top,
+                                         p_max=self.pm, workspace=self.lws, status=self.status)
+
+    def accept(self, s):
+        c = LOOP
+        self.mars.mars_accept_commit(self.pm.view(c["S"], c["B"]), self.top.view(c["S"], c["B"]),
+                                     self.tau, self.KN[s], self.VN[s], self.kc, self.vc, self.bt,
+                                     self.cl, n_accepted=self.n_acc, accepted_ids=self.acc_ids,
+                                     commit_pos=self.cpos, status=self.status)
+
+    def run(self, r, marks=None):
+        """One 64-step run from the prompt lengths; run r records its lengths."""
+        c = LOOP
+        self.cl.copy_(self.cl0)
+        self.tau.fill_(c["tau0"])
+        for s in range(c["steps"]):
+            if s == c["switch"]:
+                self.mid[r].copy_(self.cl)
+                self.tau.fill_(c["tau1"])   # live threshold change: same buffer, no rebuild
+            self.attn(s)
+            if marks:
+                marks[0](s)
+            self.conf(s)
+            if marks:
+                marks[1](s)
+            self.accept(s)
+            if marks:
+                marks[2](s)
+        self.end[r].copy_(self.cl)
+
+    def accepted(self, runs):
+        """(total, before the switch, after the switch) accepted tokens of runs."""
+        cl0 = self.cl0.cpu().numpy().astype(np.int64)
+        mid = self.mid[runs].cpu().numpy().astype(np.int64)
+        end = self.end[runs].cpu().numpy().astype(np.int64)
+        return int((end - cl0).sum()), int((mid - cl0).sum()), int((end - mid).sum())
+
+
+def append_inputs(synth, torch, dev):
+    """Rows to append and an empty paged cache with room for them (APP shape)."""
+    a_ = APP
+    di = synth.decode_inputs(1009, a_["S"], 1, a_["Hkv"], a_["Hkv"], a_["d"], 0, 0, a_["page"],
+                             extra_capacity=a_["T"])
+    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
+    bt = to_dev(di.block_table, dev)
+    del di
+    _, kr, vr = synth.decode_step_tensors(1009, 0, a_["S"], a_["T"], a_["Hkv"], a_["Hkv"],
+                                          a_["d"])
+    KR, VR = to_dev(kr, dev), to_dev(vr, dev)
+    cl = torch.zeros(a_["S"], dtype=torch.int32, device=dev)
+    return KR, VR, kc, vc, bt, cl
+
+
+class Backward:
+    def __init__(self, mars, synth, torch, dev, c):
+        self.mars, self.c = mars, c
+        q, k, v = synth.two_stream_qkv(1006, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
+        do, _, _ = synth.two_stream_qkv(1007, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
+        self.Q, self.K, self.V, self.DO = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), \
+            to_dev(do, dev)
+        del q, k, v, do
+        self.o, self.lse = mars.mars_attn_two_stream(self.Q, self.K, self.V, c["L"], c["B"],
+                                                     return_lse=True)
+        self.dq, self.dk, self.dv = (torch.empty_like(self.Q), torch.empty_like(self.K),
+                                     torch.empty_like(self.V))
+        self.ws = torch.empty(mars.lib().mars_attn_two_stream_bwd_workspace_bytes(
+            c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"]), dtype=torch.uint8, device=dev)
+
+    def run(self):
+        c = self.c
+        self.mars.mars_attn_two_stream_bwd(self.Q, self.K, self.V, self.o, self.DO, self.lse,
+                                           c["L"], c["B"], dq=self.dq, dk=self.dk, dv=self.dv,
+                                           workspace=self.ws)
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
 
 
 def main():
@@ -170,12 +406,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="copy 1 GiB once, launch each hot-path kernel once, exit")
+    ap.add_argument("--profile-pass", metavar="PLAN_JSON", default=None,
+                    help="copy 1 GiB once, launch each hot-path call once after a marker "
+                         "fill, write the call order to PLAN_JSON, exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               f"(the MARS hot path here is a single-GPU build).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -191,182 +431,89 @@ def main():
     t_setup = time.perf_counter()
 
     # ---- inputs -------------------------------------------------------------
-    log("generating two-stream inputs (0.5B shape)")
-    q, k, v = synth.two_stream_qkv(1002, TS["batch"], TS["L"], TS["Hq"], TS["Hkv"], TS["d"])
-    Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
-    O = torch.empty_like(Q)
-
-    log("generating decode inputs (7B shape) and LM head")
-    # the timed steps and the decode-only loop both commit
-    total_steps = 2 * args.steps + args.warmup
-    di = synth.decode_inputs(1004, DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"],
-                             DEC["lo"], DEC["hi"], DEC["page"],
-                             extra_capacity=DEC["B"] * (total_steps + 2))
-    dq, dkn, dvn = to_dev(di.q, dev), to_dev(di.k_new, dev), to_dev(di.v_new, dev)
-    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
-    bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
-    cl0 = cl.clone()
-    dO = torch.empty_like(dq)
-    dws = torch.empty(mars.mars_decode_workspace_bytes(DEC["S"], DEC["B"], DEC["Hq"], DEC["Hkv"],
-                                                       DEC["d"], DEC["page"], di.max_pages),
-                      dtype=torch.uint8, device=dev)
-    N = DEC["S"] * DEC["B"]
-    h, w = synth.lmhead_inputs(1004, N, LM["D"], LM["V"])
-    H, W = to_dev(h, dev), to_dev(w, dev)
-    del w
-    # the LM-head weights are packed once, as at model load: the same products,
-    # read as contiguous 20 KiB blocks per GEMM stage
-    W = mars.mars_lmhead_pack(W)
-    torch.cuda.synchronize()
-    logits = torch.empty((N, LM["V"]), dtype=torch.float32, device=dev)
-    top = torch.empty(N, dtype=torch.int32, device=dev)
-    pm = torch.empty(N, dtype=torch.float32, device=dev)
-    lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8,
-                      device=dev)
-    taus = [torch.full((DEC["S"],), t, dtype=torch.float32, device=dev) for t in (1.0, 0.9, 0.7)]
-    n_acc = torch.empty(DEC["S"], dtype=torch.int32, device=dev)
-    acc_ids = torch.empty((DEC["S"], DEC["B"]), dtype=torch.int32, device=dev)
-    cpos = torch.empty((DEC["S"], DEC["B"]), dtype=torch.int32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    log("generating two-stream inputs (7B shape)")
+    ts3 = TwoStream(mars, synth, torch, dev, TS3, 1003, keep_host=not args.no_extras)
+    log("generating decode-step inputs (7B shape) and the LM head")
+    dstep = DecodeStep(mars, synth, torch, dev, args.steps + args.warmup + 8,
+                       keep_host=not args.no_extras)
+    log("generating the decode loop (S=256, B=8, 64 steps)")
+    n_runs = args.warmup + args.steps + (1 if args.profile_pass else 0) + 1
+    loop = DecodeLoop(mars, synth, torch, dev, n_runs, keep_host=not args.no_extras)
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s")
 
-    seg = ["two_stream", "decode_attn", "lmhead_conf", "accept_commit"]
+    seg = ["two_stream", "decode_attn", "lmhead_conf", "accept_commit", "decode_loop"]
     timer = Timer(seg)
-    dec_lens = []
+    null = lambda: None
 
-    def decode_part(i, mark):
-        mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO, workspace=dws,
-                                    status=status)
-        mark()
-        mars.mars_lmhead_confidence(H, W, None, top_id=top, p_max=pm, workspace=lws,
-                                    status=status, fused=True)
-        mark()
-        mars.mars_accept_commit(pm.view(DEC["S"], DEC["B"]), top.view(DEC["S"], DEC["B"]),
-                                taus[i % 3], dkn, dvn, kc, vc, bt, cl, n_accepted=n_acc,
-                                accepted_ids=acc_ids, commit_pos=cpos, status=status)
-        mark()
-
-    def step(i, timed):
-        if timed:
+    def step(i, timed_):
+        mark = timer.mark if timed_ else null
+        if timed_:
             timer.start()
-        mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O)
-        if timed:
-            timer.mark()
-        decode_part(i, timer.mark if timed else (lambda: None))
-        if timed:
+        ts3.run()
+        mark()
+        dstep.attn()
+        mark()
+        dstep.lmhead()
+        mark()
+        dstep.accept(i)
+        mark()
+        loop.run(i)
+        mark()
+        if timed_:
             timer.stop()
 
     if args.profile_pass:
-        n = 1 << 28  # float32 elements: a 1 GiB calibration copy
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        step(0, False)
-        # the two-pass LM head as well (its own traffic line)
-        mars.mars_lmhead_confidence(H, W, logits, top_id=top, p_max=pm, workspace=lws,
-                                    status=status)
-        # and the two-stream backward at the 0.5B shape
-        lse = torch.empty((TS["batch"], TS["Hq"], 2 * TS["L"]), dtype=torch.float32, device=dev)
-        mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O, lse=lse)
-        mars.mars_attn_two_stream_bwd(Q, K, V, O, Q, lse, TS["L"], TS["B"])
-        # and one KV append at the prompt-append shape
-        app = append_inputs(synth, torch, dev)
-        mars.mars_kv_append(*app)
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "copy_bytes": n * 4,
-                          "status_flags": int(status.item())}), flush=True)
+        profile_pass(args.profile_pass, mars, synth, torch, dev, ts3, dstep, loop)
         return
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
-    lens_before = cl.cpu().numpy().copy()
+    lens_before = dstep.cl.cpu().numpy().copy()
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(args.warmup, args.warmup + args.steps):
         step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer.collect()
-    lens_after = cl.cpu().numpy()
-    accepted = int((lens_after - lens_before).sum())
-    st = int(status.item())
+    lens_after = dstep.cl.cpu().numpy()
+    dec_accepted = int((lens_after - lens_before).sum())
+    timed_runs = list(range(args.warmup, args.warmup + args.steps))
+    loop_acc, loop_acc0, loop_acc1 = loop.accepted(timed_runs)
+    st = int(dstep.status.item()) | int(loop.status.item())
     if st != 0:
         log(f"WARNING: device status flags {st}")
-
-    # The decode step again, on its own and timed as a whole: one HIP event before
-    # the first step and one after the last, none between its kernels (the
-    # markers between segments above add the command processor's gap to each).
-    lens_dec0 = cl.cpu().numpy().copy()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        decode_part(i, lambda: None)
-    e1.record()
-    torch.cuda.synchronize()
-    dec_whole_ms = e0.elapsed_time(e1) / args.steps
-    acc_whole = int((cl.cpu().numpy() - lens_dec0).sum())
-
-    # Each call of the step on its own, launched back to back: one event pair
-    # around 20 launches (after 3 untimed), for comparison with the in-step times
-    def back_to_back(fn, n=20):
-        for _ in range(3):
-            fn()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        for _ in range(n):
-            fn()
-        b_.record()
-        torch.cuda.synchronize()
-        return a_.elapsed_time(b_) / n
-
-    b2b = {
-        "two_stream_attention": back_to_back(
-            lambda: mars.mars_attn_two_stream(Q, K, V, TS["L"], TS["B"], o=O)),
-        "block_decode_attention": back_to_back(
-            lambda: mars.mars_attn_block_decode(dq, dkn, dvn, kc, vc, bt, cl, o=dO,
-                                                workspace=dws, status=status)),
-        "lmhead_confidence_fused": back_to_back(
-            lambda: mars.mars_lmhead_confidence(H, W, None, top_id=top, p_max=pm,
-                                                workspace=lws, status=status, fused=True)),
-    }  # (the commit kernel is shorter than a host launch, so it is not timed this way)
-    if int(status.item()) != 0:
-        log(f"WARNING: device status flags {int(status.item())}")
 
     ms_step = wall * 1e3 / args.steps
     t_ts = timer.mean_ms("two_stream")
     t_dec = timer.mean_ms("decode_attn")
     t_lm = timer.mean_ms("lmhead_conf")
     t_acc = timer.mean_ms("accept_commit")
-    ts_flops = useful_two_stream_flops(TS["batch"], TS["L"], TS["B"], TS["Hq"], TS["d"])
+    t_loop = timer.mean_ms("decode_loop")
+    ts_flops = useful_two_stream_flops(TS3["batch"], TS3["L"], TS3["B"], TS3["Hq"], TS3["d"])
     value = ts_flops / (t_ts * 1e-3) / 1e12
+    acc_tok_s = loop_acc / (args.steps * t_loop * 1e-3)
     decode_ms = t_dec + t_lm + t_acc
-    acc_tok_s = accepted / (args.steps * decode_ms * 1e-3)
 
     mean_len = 0.5 * (lens_before + lens_after)
     dflops, dbytes = decode_flops_bytes(mean_len, DEC["B"], DEC["Hq"], DEC["Hkv"], DEC["d"])
+    N = dstep.N
     lm_flops = 2.0 * N * LM["D"] * LM["V"]
     nvt = (LM["V"] + 319) // 320  # 320-entry vocabulary tiles
     # fused: W and hidden read once; per-(row, vocabulary tile) partials written and merged
     lmf_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + 2 * N * nvt * 16
-    lm_bytes = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + N * LM["V"] * 4
-    commit_bytes = accepted / args.steps * DEC["Hkv"] * DEC["d"] * 2 * 2 * 2
+    commit_bytes = dec_accepted / args.steps * DEC["Hkv"] * DEC["d"] * 2 * 2 * 2
 
     from block_masked_causal_amd.profile_summary import load_traffic
     traffic = load_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.json"))
-    b2, L2, Hq2, Hkv2, d2 = TS["batch"], TS["L"], TS["Hq"], TS["Hkv"], TS["d"]
-    ts_bytes = b2 * 2 * L2 * d2 * 2 * (2 * Hq2 + 2 * Hkv2)   # read Q, K, V; write O (bf16)
     kernels = {
         "two_stream_attention": roofline("mfma", value, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                         traffic.get("two_stream_attention"), ts_bytes),
+                                         traffic.get("two_stream_attention"),
+                                         two_stream_bytes(TS3)),
         "block_decode_attention": roofline("hbm", dbytes / (t_dec * 1e-3) / 1e9, PEAK_HBM_GBS,
                                            "GB/s", traffic.get("block_decode_attention"),
                                            dbytes),
@@ -376,16 +523,15 @@ def main():
         "accept_commit": roofline("hbm", commit_bytes / (t_acc * 1e-3) / 1e9, PEAK_HBM_GBS,
                                   "GB/s", traffic.get("accept_commit"), commit_bytes),
     }
+    kernels["two_stream_attention"]["useful_tflops"] = round(value, 3)
     kernels["block_decode_attention"]["useful_tflops"] = round(dflops / (t_dec * 1e-3) / 1e12, 3)
     kernels["lmhead_confidence_fused"]["useful_tflops"] = round(
         lm_flops / (t_lm * 1e-3) / 1e12, 3)
     times = {"two_stream_attention": t_ts, "block_decode_attention": t_dec,
-             "lmhead_confidence_fused": t_lm, "accept_commit": t_acc}
+             "lmhead_confidence_fused": t_lm, "accept_commit": t_acc, "decode_loop": t_loop}
+    medians = {k2: round(timer.median_ms(k2), 4) for k2 in seg}
 
-    extras = {}
-    if not args.no_extras:
-        extras = run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic)
-
+    S5, steps5 = LOOP["S"], LOOP["steps"]
     result = {
         "metric": "MARS-mask attention useful TFLOP/s + accepted tokens/s per decode step",
         "value": round(value, 3),
@@ -398,101 +544,155 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Q/K/V and caches, N(0,0.02) LM head; Qwen2.5 shapes)",
+        "data": "synthetic (seeded N(0,1) Q/K/V, caches and hidden states, N(0,0.02) LM head, "
+                "planted-peak logits with Beta(5,1) peak probabilities; Qwen2.5-7B shapes)",
         "config": {
-            "workload": "two-stream MARS attention fwd b=8 2L=4096 B=4 heads 14/2 d=64 "
+            "workload": "two-stream MARS attention fwd b=4 2L=8192 B=16 heads 28/4 d=128 "
                         "+ block-decode step S=64 B=4 cache U[512,4096] heads 28/4 d=128 "
-                        "page 16, LM head 3584x152064 with fused confidence, accept+commit",
-            "two_stream": TS, "decode": DEC, "lm_head": LM,
+                        "page 16, LM head 3584x152064 with fused confidence, accept+commit "
+                        "+ decode loop S=256 B=8 prompts U[128,2048] 64 steps tau 0.9->0.6 "
+                        "(decode attention, confidence over 2048x152064 logits, "
+                        "accept+commit)",
+            "two_stream": TS3, "decode_step": DEC, "lm_head": LM, "decode_loop": LOOP,
         },
         "accepted_tokens_per_s": round(acc_tok_s, 1),
-        "decode_step_ms": round(decode_ms, 4),
-        "kernel_ms_back_to_back": {k: round(v, 4) for k, v in b2b.items()},
-        "two_stream_back_to_back_tflops": round(ts_flops / (b2b["two_stream_attention"] * 1e-3)
-                                                / 1e12, 3),
-        "decode_step_unmarked": {
-            "ms": round(dec_whole_ms, 4),
-            "accepted_tokens_per_s": round(acc_whole / (args.steps * dec_whole_ms * 1e-3), 1),
-            "note": "the same decode step run on its own, timed with one event pair around "
-                    "all steps (no markers between its kernels)"},
+        "decode_loop": {
+            "ms_per_run": round(t_loop, 4), "ms_per_decode_step": round(t_loop / steps5, 4),
+            "accepted_per_run": round(loop_acc / args.steps, 1),
+            "mean_accepted_per_seq_tau_0.9": round(
+                loop_acc0 / (args.steps * S5 * LOOP["switch"]), 4),
+            "mean_accepted_per_seq_tau_0.6": round(
+                loop_acc1 / (args.steps * S5 * (steps5 - LOOP["switch"])), 4),
+            "note": "accepted tokens/s = accepted tokens of the 64 steps over the time of one "
+                    "event pair around them (decode attention, confidence, accept + commit, "
+                    "the tau fill and the restart of the cache lengths)"},
+        "decode_step": {
+            "ms": round(decode_ms, 4),
+            "accepted_tokens_per_s": round(dec_accepted / (args.steps * decode_ms * 1e-3), 1),
+            "note": "S=64 B=4: the random LM head gives p_max ~ 1e-3, so every tau in "
+                    "{1.0, 0.9, 0.7} accepts exactly one token per sequence"},
         "kernel_ms": {k2: round(v2, 4) for k2, v2 in times.items()},
+        "kernel_ms_median": medians,
         "roofline": kernels["two_stream_attention"],
         "kernels": kernels,
         "status_flags": st,
     }
-    result.update(extras)
     if not args.no_extras:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, args.cpu_budget)
+        result.update(run_extras(mars, synth, torch, dev, ts3, dstep, loop, traffic))
+        log("timing the CPU oracle on bounded samples")
+        result["cpu_baseline"] = cpu_baseline(ts3, args.cpu_budget)
+        result["cpu_baseline_decode_step"] = cpu_baseline_decode_step(synth, dstep)
+        result["cpu_baseline_decode_loop"] = cpu_baseline_decode_loop(synth, loop,
+                                                                      args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 
-def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
-    out = {}
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+# ---------------------------------------------------------------------------
+# profile pass: one launch of every hot-path call, each after a marker fill
+# ---------------------------------------------------------------------------
 
-    # the two-pass LM head: GEMM writing fp32 logits, then the confidence kernels
-    top2 = torch.empty(N, dtype=torch.int32, device=dev)
-    pm2 = torch.empty(N, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        mars.mars_lmhead_confidence(H, W, logits, top_id=top2, p_max=pm2, workspace=lws)
-    a, b = ev(), ev()
-    a.record()
-    for _ in range(10):
-        mars.mars_lmhead_confidence(H, W, logits, top_id=top2, p_max=pm2, workspace=lws)
-    b.record()
+
+def profile_pass(plan_path, mars, synth, torch, dev, ts3, dstep, loop):
+    marker = torch.zeros(1, dtype=torch.int64, device=dev)
+    n = 1 << 28  # float32 elements: a 1 GiB calibration copy
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    t2 = a.elapsed_time(b) / 10
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+    ts2 = TwoStream(mars, synth, torch, dev, TS2, 1002)
+    bw2 = Backward(mars, synth, torch, dev, TS2)
+    bw3 = Backward(mars, synth, torch, dev, TS3)
+    app = append_inputs(synth, torch, dev)
+    lw = loop
+    lw.cl.copy_(lw.cl0)
+    calls = [
+        ("two_stream_attention", lambda: ts3.run(0)),
+        ("two_stream_causal_2L", lambda: ts3.run(1)),
+        ("two_stream_attention_0.5b", lambda: ts2.run(0)),
+        ("block_decode_attention", dstep.attn),
+        ("lmhead_confidence_fused", dstep.lmhead),
+        ("accept_commit", lambda: dstep.accept(1)),
+        ("lmhead_gemm_plus_confidence", dstep.lmhead_two_pass),
+        ("confidence_only", dstep.confidence_only),
+        ("loop_decode_attention", lambda: lw.attn(0)),
+        ("loop_confidence", lambda: lw.conf(0)),
+        ("loop_accept_commit", lambda: lw.accept(0)),
+        ("two_stream_backward_0.5b", bw2.run),
+        ("two_stream_backward_7b", bw3.run),
+        ("kv_append", lambda: mars.mars_kv_append(*app)),
+    ]
+    plan = []
+    for i, (name, fn) in enumerate(calls):
+        torch.cuda.synchronize()
+        marker.fill_(i + 1)
+        fn()
+        torch.cuda.synchronize()
+        plan.append(name)
+    with open(plan_path, "w") as f:
+        json.dump({"copy_bytes": n * 4, "marker": "FillFunctor<long>", "calls": plan}, f)
+    print(json.dumps({"profile_pass": True, "copy_bytes": n * 4, "calls": len(plan),
+                      "status_flags": int(dstep.status.item()) | int(lw.status.item())}),
+          flush=True)
+
+
+# ---------------------------------------------------------------------------
+# extras
+# ---------------------------------------------------------------------------
+
+
+def run_extras(mars, synth, torch, dev, ts3, dstep, loop, traffic):
+    out = {}
+
+    # tile skipping at the 7B two-stream shape: MARS mask vs dense causal over 2L,
+    # both launched back to back
+    log("two-stream 7B shape: MARS mask vs causal-2L, back to back")
+    t_m = timed(torch, lambda: ts3.run(0))
+    t_c = timed(torch, lambda: ts3.run(1))
+    f0 = useful_two_stream_flops(TS3["batch"], TS3["L"], TS3["B"], TS3["Hq"], TS3["d"], 0)
+    f1 = useful_two_stream_flops(TS3["batch"], TS3["L"], TS3["B"], TS3["Hq"], TS3["d"], 1)
+    out["two_stream_7b_back_to_back"] = {
+        "shape": TS3, "mars_ms": round(t_m, 4), "causal_2L_ms": round(t_c, 4),
+        "mars_useful_tflops": round(f0 / (t_m * 1e-3) / 1e12, 2),
+        "causal_2L_useful_tflops": round(f1 / (t_c * 1e-3) / 1e12, 2),
+        "causal_2L_roofline": roofline("mfma", f1 / (t_c * 1e-3) / 1e12, PEAK_BF16_TFLOPS,
+                                       "TFLOP/s", traffic.get("two_stream_causal_2L"),
+                                       two_stream_bytes(TS3)),
+        "skip_speedup": round(t_c / t_m, 3)}
+
+    # the 0.5B two-stream shape
+    log("two-stream 0.5B shape, back to back")
+    ts2 = TwoStream(mars, synth, torch, dev, TS2, 1002)
+    t2 = timed(torch, lambda: ts2.run(0), reps=20, warm=3)
+    f2 = useful_two_stream_flops(TS2["batch"], TS2["L"], TS2["B"], TS2["Hq"], TS2["d"])
+    out["two_stream_0.5b"] = {
+        "shape": TS2, "ms": round(t2, 4),
+        "roofline": roofline("mfma", f2 / (t2 * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic.get("two_stream_attention_0.5b"), two_stream_bytes(TS2))}
+    del ts2
+    torch.cuda.empty_cache()
+
+    # per-kernel times of the decode loop: one more run with events between kernels
+    out["decode_loop_kernels"] = decode_loop_kernels(torch, loop, traffic)
+
+    # the decode step's LM head two-pass (GEMM writing fp32 logits, then the
+    # confidence kernels), and the confidence alone on those logits
+    N = dstep.N
+    t_2p = timed(torch, dstep.lmhead_two_pass, reps=10)
     b2 = LM["V"] * LM["D"] * 2 + N * LM["D"] * 2 + 2 * N * LM["V"] * 4
     out["lmhead_gemm_plus_confidence"] = {
-        "ms": round(t2, 4), "useful_tflops": round(2.0 * N * LM["D"] * LM["V"] / (t2 * 1e-3)
-                                                   / 1e12, 3),
-        "roofline": roofline("hbm", b2 / (t2 * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+        "ms": round(t_2p, 4),
+        "useful_tflops": round(2.0 * N * LM["D"] * LM["V"] / (t_2p * 1e-3) / 1e12, 3),
+        "roofline": roofline("hbm", b2 / (t_2p * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
                              traffic.get("lmhead_gemm_plus_confidence"), b2)}
-
-    # confidence alone on the same logits: splits the LM-head call into GEMM + confidence
-    top = torch.empty(N, dtype=torch.int32, device=dev)
-    pm = torch.empty(N, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws)
-    a, b = ev(), ev()
-    a.record()
-    for _ in range(10):
-        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws)
-    b.record()
-    torch.cuda.synchronize()
-    t_conf = a.elapsed_time(b) / 10
+    t_cf = timed(torch, dstep.confidence_only, reps=10)
     out["confidence_only"] = {
-        "rows": N, "vocab": LM["V"], "ms": round(t_conf, 4),
-        "roofline": roofline("hbm", N * LM["V"] * 4 / (t_conf * 1e-3) / 1e9, PEAK_HBM_GBS,
-                             "GB/s")}
-
-    # tile skipping at the 7B two-stream shape: MARS mask vs dense causal over 2L
-    log("two-stream 7B shape: MARS mask vs causal-2L")
-    q, k, v = synth.two_stream_qkv(1003, TS7["batch"], TS7["L"], TS7["Hq"], TS7["Hkv"], TS7["d"])
-    Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
-    del q, k, v
-    O = torch.empty_like(Q)
-    res = {}
-    for mode in (0, 1):
-        for _ in range(2):
-            mars.mars_attn_two_stream(Q, K, V, TS7["L"], TS7["B"], o=O, mask_mode=mode)
-        a, b = ev(), ev()
-        a.record()
-        for _ in range(5):
-            mars.mars_attn_two_stream(Q, K, V, TS7["L"], TS7["B"], o=O, mask_mode=mode)
-        b.record()
-        torch.cuda.synchronize()
-        res[mode] = a.elapsed_time(b) / 5
-    f0 = useful_two_stream_flops(TS7["batch"], TS7["L"], TS7["B"], TS7["Hq"], TS7["d"], 0)
-    f1 = useful_two_stream_flops(TS7["batch"], TS7["L"], TS7["B"], TS7["Hq"], TS7["d"], 1)
-    out["two_stream_7b"] = {
-        "shape": TS7, "mars_ms": round(res[0], 4), "causal_2L_ms": round(res[1], 4),
-        "mars_useful_tflops": round(f0 / (res[0] * 1e-3) / 1e12, 2),
-        "causal_2L_useful_tflops": round(f1 / (res[1] * 1e-3) / 1e12, 2),
-        "skip_speedup": round(res[1] / res[0], 3)}
-    del Q, K, V, O
-    torch.cuda.empty_cache()
+        "rows": N, "vocab": LM["V"], "ms": round(t_cf, 4),
+        "roofline": roofline("hbm", N * LM["V"] * 4 / (t_cf * 1e-3) / 1e9, PEAK_HBM_GBS,
+                             "GB/s", traffic.get("confidence_only"), N * LM["V"] * 4)}
 
     # two-stream attention backward (dq, dk, dv) at both training shapes
     out["two_stream_bwd"] = two_stream_bwd(mars, synth, torch, dev, traffic)
@@ -501,12 +701,8 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
     # that fills the paged cache from a prompt
     out["causal_prefill"] = causal_prefill(mars, synth, torch, dev, traffic)
 
-    # acceptance + commit with every row accepted (tau = 0) at the high-load loop's
-    # shape: the largest copy one call makes there
+    # acceptance + commit with every row accepted (tau = 0) at the high-load loop's shape
     out["accept_commit_full"] = accept_commit_full(mars, torch, dev)
-
-    # batched decode loop with a live tau switch
-    out["decode_loop"] = decode_loop(mars, synth, torch, dev, status)
 
     # the batch-synchronous block cache (both batch policies) beside per-token
     # commit and one-token-per-step AR decoding, on the same confidence draws
@@ -518,6 +714,62 @@ def run_extras(mars, synth, torch, dev, logits, lws, status, H, W, N, traffic):
                    "pages' end-to-end wall-clock ratios")
     out["decode_policies"] = pol
     return out
+
+
+def decode_loop_kernels(torch, loop, traffic):
+    """One more 64-step run of the decode loop with an event after each kernel, to split
+    its time into decode attention, confidence and accept + commit."""
+    log("decode loop with events between kernels")
+    c = LOOP
+    evs = {k: [] for k in ("a", "b", "c", "d")}
+
+    def ev(key):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        evs[key].append(e)
+
+    lens = []
+    loop.cl.copy_(loop.cl0)
+    loop.tau.fill_(c["tau0"])
+    torch.cuda.synchronize()
+    for s in range(c["steps"]):
+        if s == c["switch"]:
+            loop.tau.fill_(c["tau1"])
+        lens.append(loop.cl.cpu().numpy().astype(np.float64))
+        ev("a")
+        loop.attn(s)
+        ev("b")
+        loop.conf(s)
+        ev("c")
+        loop.accept(s)
+        ev("d")
+    torch.cuda.synchronize()
+    t_att = [a.elapsed_time(b) for a, b in zip(evs["a"], evs["b"])]
+    t_cnf = [a.elapsed_time(b) for a, b in zip(evs["b"], evs["c"])]
+    t_acc = [a.elapsed_time(b) for a, b in zip(evs["c"], evs["d"])]
+    att_bytes = [decode_flops_bytes(ln, c["B"], c["Hq"], c["Hkv"], c["d"])[1] for ln in lens]
+    att_flops = [decode_flops_bytes(ln, c["B"], c["Hq"], c["Hkv"], c["d"])[0] for ln in lens]
+    acc_total = float(np.sum(loop.cl.cpu().numpy().astype(np.int64)
+                             - loop.cl0.cpu().numpy().astype(np.int64)))
+    conf_bytes = loop.N * LM["V"] * 4
+    commit_bytes = acc_total / c["steps"] * c["Hkv"] * c["d"] * 2 * 2 * 2
+    ma, mc, mk = float(np.mean(t_att)), float(np.mean(t_cnf)), float(np.mean(t_acc))
+    return {
+        "decode_attention": {
+            "ms": round(ma, 4),
+            "useful_tflops": round(float(np.mean(att_flops)) / (ma * 1e-3) / 1e12, 3),
+            "roofline": roofline("hbm", float(np.mean(att_bytes)) / (ma * 1e-3) / 1e9,
+                                 PEAK_HBM_GBS, "GB/s", traffic.get("loop_decode_attention"),
+                                 float(np.mean(att_bytes)))},
+        "confidence": {
+            "ms": round(mc, 4),
+            "roofline": roofline("hbm", conf_bytes / (mc * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                 traffic.get("loop_confidence"), conf_bytes)},
+        "accept_commit": {
+            "ms": round(mk, 4),
+            "roofline": roofline("hbm", commit_bytes / (mk * 1e-3) / 1e9, PEAK_HBM_GBS,
+                                 "GB/s", traffic.get("loop_accept_commit"), commit_bytes)},
+        "note": "means over the 64 steps of one run; each kernel's time spans its event pair"}
 
 
 def accept_commit_full(mars, torch, dev):
@@ -564,52 +816,18 @@ def two_stream_bwd(mars, synth, torch, dev, traffic):
     """Backward of the two-stream attention; useful FLOPs = 10 d per visible pair per query
     head (QK^T recomputed, dO V^T, and the dV, dK, dQ products: 2d each)."""
     res = {}
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    for name, c in (("0.5b", TS), ("7b", TS7)):
+    for name, c in (("0.5b", TS2), ("7b", TS3)):
         log(f"two-stream backward, {name} shape")
-        q, k, v = synth.two_stream_qkv(1006, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
-        do, _, _ = synth.two_stream_qkv(1007, c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"])
-        Q, K, V, DO = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev), to_dev(do, dev)
-        del q, k, v, do
-        o, lse = mars.mars_attn_two_stream(Q, K, V, c["L"], c["B"], return_lse=True)
-        dq, dk, dv = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
-        ws = torch.empty(mars.lib().mars_attn_two_stream_bwd_workspace_bytes(
-            c["batch"], c["L"], c["Hq"], c["Hkv"], c["d"]), dtype=torch.uint8, device=dev)
-        call = lambda: mars.mars_attn_two_stream_bwd(Q, K, V, o, DO, lse, c["L"], c["B"], dq=dq,
-                                                     dk=dk, dv=dv, workspace=ws)
-        for _ in range(2):
-            call()
-        a, b = ev(), ev()
-        a.record()
-        for _ in range(5):
-            call()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / 5
+        bw = Backward(mars, synth, torch, dev, c)
+        ms = timed(torch, bw.run)
         fl = 2.5 * useful_two_stream_flops(c["batch"], c["L"], c["B"], c["Hq"], c["d"])
         tf = fl / (ms * 1e-3) / 1e12
         res[name] = {"shape": c, "ms": round(ms, 4), "useful_tflops": round(tf, 2),
                      "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                          traffic.get("two_stream_backward") if name == "0.5b"
-                                          else None)}
-        del Q, K, V, DO, o, lse, dq, dk, dv, ws
+                                          traffic.get(f"two_stream_backward_{name}"))}
+        del bw
         torch.cuda.empty_cache()
     return res
-
-
-def append_inputs(synth, torch, dev):
-    """Rows to append and an empty paged cache with room for them (APP shape)."""
-    a_ = APP
-    di = synth.decode_inputs(1009, a_["S"], 1, a_["Hkv"], a_["Hkv"], a_["d"], 0, 0, a_["page"],
-                             extra_capacity=a_["T"])
-    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
-    bt = to_dev(di.block_table, dev)
-    del di
-    _, kr, vr = synth.decode_step_tensors(1009, 0, a_["S"], a_["T"], a_["Hkv"], a_["Hkv"],
-                                          a_["d"])
-    KR, VR = to_dev(kr, dev), to_dev(vr, dev)
-    cl = torch.zeros(a_["S"], dtype=torch.int32, device=dev)
-    return KR, VR, kc, vc, bt, cl
 
 
 def causal_prefill(mars, synth, torch, dev, traffic):
@@ -623,15 +841,7 @@ def causal_prefill(mars, synth, torch, dev, traffic):
     Q, K, V = to_dev(q, dev), to_dev(k, dev), to_dev(v, dev)
     del q, k, v
     O = torch.empty_like(Q)
-    for _ in range(2):
-        mars.mars_attn_causal(Q, K, V, o=O)
-    a, b = ev(), ev()
-    a.record()
-    for _ in range(5):
-        mars.mars_attn_causal(Q, K, V, o=O)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / 5
+    ms = timed(torch, lambda: mars.mars_attn_causal(Q, K, V, o=O))
     fl = 4.0 * c["d"] * c["Hq"] * c["batch"] * c["T"] * (c["T"] + 1) / 2
     tf = fl / (ms * 1e-3) / 1e12
     res = {"prefill": {"shape": c, "ms": round(ms, 4), "useful_tflops": round(tf, 2),
@@ -749,64 +959,120 @@ def block_cache_loop(mars, synth, torch, dev, policy):
     return res
 
 
-def decode_loop(mars, synth, torch, dev, status):
+# ---------------------------------------------------------------------------
+# the CPU oracle, timed on bounded samples of the same workloads
+# ---------------------------------------------------------------------------
+
+
+def _blas_limit(n):
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=n)
+    except Exception:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline(ts3, budget_s):
+    """The oracle's two-stream attention (explicit 2L x 2L mask, dense fp64 softmax
+    attention) timed on whole (batch, head) pairs of the 7B two-stream shape."""
+    import oracle
+    import synth
+    n, aff = cpu_threads()
+    q, k, v = ts3.host
+    c = TS3
+    pairs = synth.sample_pairs(1003, c["batch"], c["Hq"], c["batch"] * c["Hq"])
+    with _blas_limit(n):
+        t0 = time.perf_counter()
+        done = 0
+        for pair in pairs:
+            oracle.attn_two_stream(q.f32, k.f32, v.f32, c["L"], c["B"], pairs=[pair])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    flops = useful_two_stream_flops(1, c["L"], c["B"], done, c["d"])
+    total_pairs = c["batch"] * c["Hq"]
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n,
+            "affinity_cpus": aff, "kind": "oracle",
+            "sample": f"{done} of {total_pairs} (batch, head) pairs of the two-stream 7B-shape "
+                      f"attention (b=4 2L=8192 B=16 28/4 d=128), all {2 * c['L']} rows each, "
+                      f"float64 numpy with {n} BLAS threads ({dt:.1f} s); the whole launch "
+                      f"would take about {dt * total_pairs / done:.0f} s (linear "
+                      f"extrapolation)"}
+
+
+def cpu_baseline_decode_step(synth, dstep):
+    """The oracle's whole 7B decode step (all 64 sequences): decode attention over the
+    gathered prefix, the fp64 LM-head GEMM, the per-row confidence, the scalar
+    acceptance and commit loops."""
+    import oracle
+    n, aff = cpu_threads()
+    c = DEC
+    di, h, w = dstep.host
+    tau = np.full(c["S"], 0.9, dtype=np.float32)
+    with _blas_limit(n):
+        t0 = time.perf_counter()
+        oracle.attn_block_decode(di.q.f32, di.k_new.f32, di.v_new.f32, di.k_cache.f32,
+                                 di.v_cache.f32, di.block_table, di.cache_len, c["page"])
+        t1 = time.perf_counter()
+        logits = oracle.lmhead(h.f32, w.f32)
+        t2 = time.perf_counter()
+        ids, p = oracle.confidence(logits)
+        nacc, _ = oracle.accept(p.reshape(c["S"], c["B"]), ids.reshape(c["S"], c["B"]), tau)
+        oracle.commit(di.k_cache.f32, di.v_cache.f32, di.block_table, di.cache_len,
+                      di.k_new.f32, di.v_new.f32, nacc, c["page"])
+        t3 = time.perf_counter()
+    dt = t3 - t0
+    return {"value": round(float(nacc.sum()) / dt, 3), "unit": "accepted tokens/s",
+            "cores": n, "affinity_cpus": aff, "kind": "oracle",
+            "ms_per_step": round(dt * 1e3, 1),
+            "split_ms": {"decode_attention": round((t1 - t0) * 1e3, 1),
+                         "lmhead": round((t2 - t1) * 1e3, 1),
+                         "confidence_accept_commit": round((t3 - t2) * 1e3, 1)},
+            "sample": "one whole decode step at S=64 B=4 (28/4 heads, d=128, LM head "
+                      "3584x152064 in float64), tau 0.9"}
+
+
+def cpu_baseline_decode_loop(synth, loop, budget_s):
+    """The oracle on the first steps of the high-load loop: confidence, acceptance and
+    commit on every row, decode attention on 4 of the 256 sequences (its time scaled
+    by 64 for the whole batch, a linear extrapolation)."""
+    import oracle
+    n, aff = cpu_threads()
     c = LOOP
-    log("decode loop: S=256 B=8, 64 steps, tau 0.9 -> 0.6 at step 32")
-    di = synth.decode_inputs(1005, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"], c["lo"], c["hi"],
-                             c["page"], extra_capacity=c["steps"] * c["B"])
-    pool = synth.PeakedLogitsPool(1005, c["S"] * c["B"], LM["V"], taus=(0.9, 0.6))
-    kc, vc = to_dev(di.k_cache, dev), to_dev(di.v_cache, dev)
-    bt, cl = to_dev(di.block_table, dev), to_dev(di.cache_len, dev)
-    del di.k_cache, di.v_cache
-    pool_dev = torch.from_numpy(pool.pool).to(dev)
-    logits = torch.empty_like(pool_dev)
-    N = c["S"] * c["B"]
-    rows = torch.arange(N, device=dev)
-    tau = torch.full((c["S"],), 0.9, dtype=torch.float32, device=dev)
-    o = torch.empty((c["S"], c["B"], c["Hq"], c["d"]), dtype=torch.bfloat16, device=dev)
-    dws = torch.empty(mars.mars_decode_workspace_bytes(c["S"], c["B"], c["Hq"], c["Hkv"], c["d"],
-                                                       c["page"], bt.shape[1]),
-                      dtype=torch.uint8, device=dev)
-    lws = torch.empty(mars.mars_lmhead_workspace_bytes(N, LM["V"]), dtype=torch.uint8, device=dev)
-    top = torch.empty(N, dtype=torch.int32, device=dev)
-    pm = torch.empty(N, dtype=torch.float32, device=dev)
-    n_acc = torch.empty(c["S"], dtype=torch.int32, device=dev)
-    acc_ids = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
-    cpos = torch.empty((c["S"], c["B"]), dtype=torch.int32, device=dev)
-    total_ms = 0.0
-    accepted = []
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    for s in range(c["steps"]):
-        if s == c["switch"]:
-            tau.fill_(0.6)  # live threshold change: same buffers, no re-initialisation
-        q, kn, vn = synth.decode_step_tensors(1005, s, c["S"], c["B"], c["Hq"], c["Hkv"], c["d"])
-        Q, KN, VN = to_dev(q, dev), to_dev(kn, dev), to_dev(vn, dev)
-        ids, peak, _ = pool.peaks(s)
-        logits.copy_(pool_dev)
-        logits[rows, torch.from_numpy(ids).to(dev)] = torch.from_numpy(peak).to(dev)
-        a, b = ev(), ev()
-        a.record()
-        mars.mars_attn_block_decode(Q, KN, VN, kc, vc, bt, cl, o=o, workspace=dws, status=status)
-        mars.mars_lmhead_confidence(None, None, logits, top_id=top, p_max=pm, workspace=lws,
-                                    status=status)
-        mars.mars_accept_commit(pm.view(c["S"], c["B"]), top.view(c["S"], c["B"]), tau, KN, VN,
-                                kc, vc, bt, cl, n_accepted=n_acc, accepted_ids=acc_ids,
-                                commit_pos=cpos, status=status)
-        b.record()
-        torch.cuda.synchronize()
-        total_ms += a.elapsed_time(b)
-        accepted.append(int(n_acc.sum().item()))
-    acc = np.array(accepted, dtype=np.float64)
-    sw = c["switch"]
-    return {
-        "config": {k: c[k] for k in ("S", "B", "Hq", "Hkv", "d", "page", "steps")},
-        "accepted_tokens_per_s": round(acc.sum() / (total_ms * 1e-3), 1),
-        "ms_per_step": round(total_ms / c["steps"], 4),
-        "mean_accepted_per_seq_tau_0.9": round(acc[:sw].mean() / c["S"], 4),
-        "mean_accepted_per_seq_tau_0.6": round(acc[sw:].mean() / c["S"], 4),
-        "note": "per step: decode attention + confidence over 2048 x 152064 fp32 logits + "
-                "accept/commit; the synthetic logits are written outside the timed events",
-    }
+    di = loop.host
+    kc, vc, lens = di.k_cache.f32, di.v_cache.f32, di.cache_len.copy()
+    sample = [0, 77, 128, 255]
+    t_att = t_rest = 0.0
+    steps = accepted = 0
+    with _blas_limit(n):
+        while steps < c["switch"] and t_att * c["S"] / len(sample) + t_rest < budget_s:
+            q, kn, vn = synth.decode_step_tensors(1005, steps, c["S"], c["B"], c["Hq"],
+                                                  c["Hkv"], c["d"])
+            lg = loop.pool.logits(steps)
+            t0 = time.perf_counter()
+            oracle.attn_block_decode(q.f32, kn.f32, vn.f32, kc, vc, di.block_table, lens,
+                                     c["page"], seqs=sample)
+            t1 = time.perf_counter()
+            ids, p = oracle.confidence(lg)
+            tau = np.full(c["S"], c["tau0"], dtype=np.float32)
+            nacc, _ = oracle.accept(p.astype(np.float32).reshape(c["S"], c["B"]),
+                                    ids.reshape(c["S"], c["B"]), tau)
+            kc, vc, lens, _ = oracle.commit(kc, vc, di.block_table, lens, kn.f32, vn.f32, nacc,
+                                            c["page"])
+            t2 = time.perf_counter()
+            t_att += t1 - t0
+            t_rest += t2 - t1
+            accepted += int(nacc.sum())
+            steps += 1
+    est = t_att * c["S"] / len(sample) + t_rest
+    return {"value": round(accepted / est, 3), "unit": "accepted tokens/s", "cores": n,
+            "affinity_cpus": aff, "kind": "oracle",
+            "sample": f"the first {steps} steps of the S=256 B=8 loop (tau 0.9): confidence, "
+                      f"acceptance and commit on all 2048 rows per step ({t_rest:.1f} s), "
+                      f"decode attention on 4 of 256 sequences ({t_att:.1f} s, scaled by 64 "
+                      f"to the whole batch: a linear extrapolation)"}
 
 
 if __name__ == "__main__":

@@ -252,7 +252,10 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
 // Workgroup = nw waves, each owning one (query head, 32-row tile): gh heads of
 // one GQA group x rt row tiles, so every K/V tile staged through LDS feeds
 // 32 * nw query rows. The launcher uses gh = 1, rt = 4 at both head sizes.
-template <int D>
+// MODE is the mask: 0 the MARS two-stream mask, 1 plain causal over all 2L
+// positions (a separate instance, so that the two modes are told apart in
+// kernel traces and each folds its own interval arithmetic).
+template <int D, int MODE>
 __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p) {
   using C = Cfg<D>;
   // two K/V stages (K tile then V tile), separate objects so that reads of
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   const int h = kvh * p.group + hc * p.gh + w % p.gh;
   const int bm = 32 * p.rt;
   int qt;
-  if (p.mask_mode == 0 && (p.L % bm) == 0) {
+  if (MODE == 0 && (p.L % bm) == 0) {
     const int nqs = p.L / bm;  // tiles per stream; clean tile i and mask tile i cost alike
     qt = (rank & 1) * nqs + (nqs - 1 - (rank >> 1));
   } else {
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
 
   // key ranges of the whole workgroup (what gets staged) and of this wave
   int r1_hi, r2_lo, r2_hi, full_below;
-  rows_key_ranges(a0, a_last, p.L, p.B, p.mask_mode, r1_hi, r2_lo, r2_hi, full_below);
+  rows_key_ranges(a0, a_last, p.L, p.B, MODE, r1_hi, r2_lo, r2_hi, full_below);
   const int n1 = (r1_hi + C::BN - 1) / C::BN;
   const int n2 = r2_hi > r2_lo ? (r2_hi - r2_lo + C::BN - 1) / C::BN : 0;
   const int ntiles = n1 + n2;
@@ -310,12 +313,12 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
   const bool wave_live = wa0 < p.twoL;
   const int wa_last = wave_live ? min(wa0 + 31, p.twoL - 1) : wa0;
   int w1_hi, w2_lo, w2_hi, w_full;
-  rows_key_ranges(wa0, wa_last, p.L, p.B, p.mask_mode, w1_hi, w2_lo, w2_hi, w_full);
+  rows_key_ranges(wa0, wa_last, p.L, p.B, MODE, w1_hi, w2_lo, w2_hi, w_full);
 
   // ---- this lane's query row and its visible key intervals ---------------
   const int a = wa0 + j;
   int hi1, lo2, hi2;
-  row_intervals(a, p.L, p.B, p.mask_mode, hi1, lo2, hi2);
+  row_intervals(a, p.L, p.B, MODE, hi1, lo2, hi2);
 
   // buffer views: reads past the end of this (batch, head) slice return 0
   const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
@@ -466,8 +469,12 @@ int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   a.nqt = (a.twoL + 32 * a.rt - 1) / (32 * a.rt);
   const double nblocks = (double)a.batch * a.Hkv * a.nhc * a.nqt;
   if (nblocks >= 2147483647.0) return MARS_ERR_SHAPE;
-  hipLaunchKernelGGL(two_stream_bf16_kernel<D>, dim3((unsigned)nblocks), dim3(64 * a.nw),
-                     0, st, a);
+  if (a.mask_mode == 0)
+    hipLaunchKernelGGL((two_stream_bf16_kernel<D, 0>), dim3((unsigned)nblocks),
+                       dim3(64 * a.nw), 0, st, a);
+  else
+    hipLaunchKernelGGL((two_stream_bf16_kernel<D, 1>), dim3((unsigned)nblocks),
+                       dim3(64 * a.nw), 0, st, a);
   return mars_launch_status();
 }
 

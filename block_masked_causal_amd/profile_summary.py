@@ -3,16 +3,22 @@
     python -m block_masked_causal_amd.profile_summary stats KERNEL_STATS_CSV \
         --title T --cmd "rocprofv3 ..." --out profiles/NAME.md
     python -m block_masked_causal_amd.profile_summary traffic \
-        --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --copy-bytes N \
+        --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --plan PLAN_JSON \
         --cmd-fetch "..." --cmd-write "..." --out profiles/hbm_traffic.json
+    python -m block_masked_causal_amd.profile_summary counters COUNTER_CSV \
+        --plan PLAN_JSON --cmd "..." --out profiles/NAME.md
 
-`stats` turns the --kernel-trace --stats table into markdown. `traffic` reads
-two --pmc runs of `bench.py --profile-pass` (FETCH_SIZE, then WRITE_SIZE, in
-KiB per dispatch). That pass first copies a buffer of known size, so each
-counter is scaled by (known bytes) / (what the counter read for the copy). It
-then launches every hot-path kernel once. The result records the HBM bytes
-per launch of each hot-path call, together with a hash of the sources that
-built it: bench.py reports the figure only while those sources are unchanged.
+`stats` turns the --kernel-trace --stats table into markdown. `traffic` and
+`counters` read --pmc runs of `bench.py --profile-pass PLAN_JSON`. That pass
+first copies a buffer of known size, then launches every hot-path call once,
+each right after a one-element int64 fill (the marker); PLAN_JSON lists the
+calls in launch order. The dispatches between one marker and the next belong
+to that call. `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+by (known bytes) / (what the counter read for the copy) and records the HBM
+bytes per launch of each call with a hash of the sources that built it:
+bench.py reports the figure only while those sources are unchanged.
+`counters` tabulates the COUNTERS below per call, with MFMA busy =
+SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs).
 """
 
 from __future__ import annotations
@@ -28,27 +34,33 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# hot-path call -> (source files that build it, kernel-name substrings of its dispatches)
-CALLS = {
-    "two_stream_attention": (["attn_two_stream.hip", "attn_common.hpp", "mars_common.hpp"],
-                             ["two_stream_bf16_kernel"]),
-    "block_decode_attention": (["attn_decode.hip", "mars_common.hpp"],
-                               ["decode_split_kernel", "decode_merge_kernel"]),
-    "lmhead_confidence_fused": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                ["lmhead_gemm_kernel<true, 320>",
-                                 "lmhead_gemm_kernel<true, 64>", "conf_merge_wide_kernel"]),
-    "lmhead_gemm_plus_confidence": (["lmhead_confidence.hip", "mars_common.hpp"],
-                                    ["lmhead_gemm_kernel<false, 320>",
-                                     "lmhead_gemm_kernel<false, 64>", "conf_partial_kernel",
-                                     r"conf_merge_kernel\("]),
-    "accept_commit": (["accept_commit.hip", "mars_common.hpp"], ["accept_commit_kernel"]),
-    "kv_append": (["accept_commit.hip", "mars_common.hpp"],
-                  ["kv_append_kernel", "kv_append_len_kernel"]),
-    "two_stream_backward": (["attn_two_stream_bwd.hip", "attn_common.hpp", "mars_common.hpp"],
-                            ["bwd_dsum_kernel", "bwd_dq_kernel", r"bwd_dkv_kernel<",
-                             "bwd_dkv_reduce_kernel"]),
+_TS = ["attn_two_stream.hip", "attn_common.hpp", "mars_common.hpp"]
+_DEC = ["attn_decode.hip", "mars_common.hpp"]
+_LM = ["lmhead_confidence.hip", "mars_common.hpp"]
+_AC = ["accept_commit.hip", "mars_common.hpp"]
+_BWD = ["attn_two_stream_bwd.hip", "attn_common.hpp", "mars_common.hpp"]
+
+# hot-path call of the profile pass -> the source files that build its kernels
+SOURCES = {
+    "two_stream_attention": _TS,
+    "two_stream_causal_2L": _TS,
+    "two_stream_attention_0.5b": _TS,
+    "block_decode_attention": _DEC,
+    "lmhead_confidence_fused": _LM,
+    "accept_commit": _AC,
+    "lmhead_gemm_plus_confidence": _LM,
+    "confidence_only": _LM,
+    "loop_decode_attention": _DEC,
+    "loop_confidence": _LM,
+    "loop_accept_commit": _AC,
+    "two_stream_backward_0.5b": _BWD,
+    "two_stream_backward_7b": _BWD,
+    "kv_append": _AC,
+    "kv_commit_layers": _AC,
 }
 COPY_KERNEL = "copyBuffer"
+MARKER = "FillFunctor<long>"
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
 
 
 def sources_sha256(files) -> str:
@@ -82,78 +94,131 @@ def stats(args) -> None:
         f.write("\n".join(lines) + "\n")
 
 
-def _per_dispatch(path: str, counter: str):
-    """kernel name -> list of per-dispatch counter values (summed over dimensions)."""
-    acc = collections.defaultdict(float)
+def dispatches(path: str):
+    """[(dispatch id, kernel name, {counter: value summed over dimensions})] in order."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
     names = {}
     for r in csv.DictReader(open(path)):
-        if r["Counter_Name"] != counter:
-            continue
-        key = r["Dispatch_Id"]
-        acc[key] += float(r["Counter_Value"])
+        key = int(r["Dispatch_Id"])
+        acc[key][r["Counter_Name"]] += float(r["Counter_Value"])
         names[key] = r["Kernel_Name"]
-    out = collections.defaultdict(list)
-    for key, v in sorted(acc.items(), key=lambda kv: int(kv[0])):
-        out[names[key]].append(v)
+    return [(k, names[k], dict(acc[k])) for k in sorted(acc)]
+
+
+def segments(rows, plan):
+    """call name -> its dispatches (those after the call's marker, before the next)."""
+    out = collections.OrderedDict()
+    cur = -1
+    for k, name, vals in rows:
+        if MARKER in name:
+            cur += 1
+            if cur >= len(plan):
+                raise SystemExit(f"more markers than calls in the plan ({len(plan)})")
+            out[plan[cur]] = []
+            continue
+        if cur >= 0:
+            out[plan[cur]].append((k, name, vals))
+    if cur != len(plan) - 1:
+        raise SystemExit(f"found {cur + 1} markers for {len(plan)} calls")
     return out
 
 
+def _copy_value(rows, counter):
+    vals = [v[counter] for _, n, v in rows if COPY_KERNEL in n and counter in v]
+    if not vals:
+        raise SystemExit("no calibration copy dispatch found")
+    return max(vals)  # the large calibration copy, not small incidental copies
+
+
 def traffic(args) -> None:
-    fetch = _per_dispatch(args.fetch, "FETCH_SIZE")
-    write = _per_dispatch(args.write, "WRITE_SIZE")
-
-    def copy_value(table):
-        vals = [v for n, vs in table.items() if COPY_KERNEL in n for v in vs]
-        if not vals:
-            raise SystemExit("no calibration copy dispatch found")
-        return max(vals)  # the large calibration copy, not small incidental copies
-
-    f_copy, w_copy = copy_value(fetch), copy_value(write)
-    f_fac = args.copy_bytes / (f_copy * 1024.0)
-    w_fac = args.copy_bytes / (w_copy * 1024.0)
+    plan = json.load(open(args.plan))
+    fetch = dispatches(args.fetch)
+    write = dispatches(args.write)
+    f_copy, w_copy = _copy_value(fetch, "FETCH_SIZE"), _copy_value(write, "WRITE_SIZE")
+    copy_bytes = plan["copy_bytes"]
+    f_fac = copy_bytes / (f_copy * 1024.0)
+    w_fac = copy_bytes / (w_copy * 1024.0)
+    fs, ws = segments(fetch, plan["calls"]), segments(write, plan["calls"])
     out = {
-        "calibration": {"copy_bytes": args.copy_bytes, "fetch_kib": f_copy, "write_kib": w_copy,
+        "calibration": {"copy_bytes": copy_bytes, "fetch_kib": f_copy, "write_kib": w_copy,
                         "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
         "command_fetch": args.cmd_fetch, "command_write": args.cmd_write, "calls": {}}
-    for call, (files, pats) in CALLS.items():
-        fk = wk = 0.0
-        seen = []
-        for pat in pats:
-            fv = [v for n, vs in fetch.items() if re.search(pat, n) for v in vs]
-            wv = [v for n, vs in write.items() if re.search(pat, n) for v in vs]
-            if not fv or not wv:
-                continue
-            # one hot-path call launches each of its kernels once in the pass
-            fk += sum(fv) / len(fv)
-            wk += sum(wv) / len(wv)
-            seen.append(pat)
-        if not seen:
-            continue
+    for call in plan["calls"]:
+        fk = sum(v.get("FETCH_SIZE", 0.0) for _, _, v in fs[call])
+        wk = sum(v.get("WRITE_SIZE", 0.0) for _, _, v in ws[call])
+        kernels = sorted({_short(n) for _, n, _ in fs[call]})
+        files = SOURCES[call]
         out["calls"][call] = {
-            "kernels": seen, "sources": files, "sha256": sources_sha256(files),
-            "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+            "kernels": kernels, "dispatches": len(fs[call]), "sources": files,
+            "sha256": sources_sha256(files), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
             "bytes": round(fk * 1024.0 * f_fac + wk * 1024.0 * w_fac)}
     with open(args.out, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    md = [f"# HBM traffic per launch of each hot-path call (bench.py --profile-pass)", "",
+    md = ["# HBM traffic per launch of each hot-path call (bench.py --profile-pass)", "",
           "Commands (on one MI355X; $REPO is the repository root):", "", "```",
           args.cmd_fetch, args.cmd_write, "```", "",
-          f"Calibration: a plain {args.copy_bytes} B device copy reads FETCH_SIZE = "
+          f"Calibration: a plain {copy_bytes} B device copy reads FETCH_SIZE = "
           f"{f_copy:.1f} KiB and WRITE_SIZE = {w_copy:.1f} KiB, so FETCH_SIZE is scaled by "
           f"{f_fac:.4f} and WRITE_SIZE by {w_fac:.4f}.", "",
-          "| call | kernels | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch |",
-          "|---|---|---|---|---|"]
+          "| call | kernels | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch |",
+          "|---|---|---|---|---|---|"]
     for call, e in out["calls"].items():
-        md.append(f"| {call} | {', '.join(e['kernels'])} | {e['fetch_kib']:.1f} | "
-                  f"{e['write_kib']:.1f} | {e['bytes']} |")
+        md.append(f"| {call} | {'<br>'.join('`%s`' % k for k in e['kernels'])} | "
+                  f"{e['dispatches']} | {e['fetch_kib']:.1f} | {e['write_kib']:.1f} | "
+                  f"{e['bytes']} |")
     md += ["", f"Machine-readable copy with source hashes: {os.path.basename(args.out)} "
            "(bench.py reports a figure only while the hashed sources are unchanged).",
            "Summary written by: python -m block_masked_causal_amd.profile_summary traffic "
-           "--fetch <fetch csv> --write <write csv> --copy-bytes "
-           f"{args.copy_bytes} --cmd-fetch ... --cmd-write ... --out {args.out}"]
+           "--fetch <fetch csv> --write <write csv> --plan <plan json> --cmd-fetch ... "
+           f"--cmd-write ... --out {args.out}"]
     with open(os.path.splitext(args.out)[0] + ".md", "w") as f:
         f.write("\n".join(md) + "\n")
+
+
+COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+            "SQ_LDS_BANK_CONFLICT"]
+
+
+def counters(args) -> None:
+    plan = json.load(open(args.plan))
+    segs = segments(dispatches(args.csv), plan["calls"])
+    lines = [f"# {args.title}", "", "Command (on one MI355X; $REPO is the repository root):", "",
+             "```", args.cmd, "```", "",
+             "One row per kernel dispatch of `bench.py --profile-pass` (one launch of every "
+             "hot-path call). GRBM_GUI_ACTIVE is the dispatch's GPU-busy cycles; the SQ "
+             "counters are summed over the chip. Derived columns:", "",
+             f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMDS} SIMDs) x "
+             "100 (rocprofv3's MfmaUtil): the share of SIMD cycles the matrix core was busy;",
+             "- MFMA GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 1e9 (the counter counts "
+             "bf16 MFMA flops in units of 512), i.e. the flops the kernel computed, masked "
+             "or not;",
+             "- VALU / MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA (instructions issued);",
+             "- VALU busy % = SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE x "
+             f"{SIMDS}) x 100 (the counter is in quad-cycles);",
+             "- LDS bank-conflict cycles, summed over the chip.", "",
+             "| call | kernel | GRBM_GUI_ACTIVE | MFMA busy % | MFMA GFLOP | VALU / MFMA | "
+             "VALU busy % | LDS bank-conflict cycles |",
+             "|---|---|---|---|---|---|---|---|"]
+    for call, disp in segs.items():
+        for _, name, v in disp:
+            gui = v.get("GRBM_GUI_ACTIVE", 0.0)
+            busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+            nmfma = v.get("SQ_INSTS_MFMA", 0.0)
+            nvalu = v.get("SQ_INSTS_VALU", 0.0)
+            avalu = v.get("SQ_ACTIVE_INST_VALU", 0.0)
+            pct = 100.0 * busy / (gui * SIMDS) if gui else 0.0
+            vpct = 100.0 * 4.0 * avalu / (gui * SIMDS) if gui else 0.0
+            ratio = f"{nvalu / nmfma:.2f}" if nmfma else "-"
+            lines.append(f"| {call} | `{_short(name)}` | {gui:.0f} | {pct:.1f} | "
+                         f"{mops * 512 / 1e9:.1f} | {ratio} | {vpct:.1f} | "
+                         f"{v.get('SQ_LDS_BANK_CONFLICT', 0.0):.4g} |")
+    if args.note:
+        lines += ["", args.note]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def load_traffic(path: str):
@@ -183,12 +248,19 @@ def main() -> None:
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--plan", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--plan", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--note", default="")
+    c.add_argument("--out", required=True)
     args = ap.parse_args()
-    (stats if args.cmd_name == "stats" else traffic)(args)
+    {"stats": stats, "traffic": traffic, "counters": counters}[args.cmd_name](args)
 
 
 if __name__ == "__main__":

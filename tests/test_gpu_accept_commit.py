@@ -164,7 +164,7 @@ def run_loop(seed, S, B, Hq, Hkv, D, V, lo, hi, page, steps, switch, sample=None
     ov = d.v_cache.f32[pages]
     olen = d.cache_len[sample].copy()
     worst = 0.0
-    accepted_total = 0
+    accepted = [0, 0]   # accepted tokens over all sequences before / after the tau switch
     for step in range(steps):
         if step == switch:
             tau.copy_(to_dev(synth.tau_schedule(S, step, switch)))  # live change, no rebuild
@@ -197,7 +197,7 @@ def run_loop(seed, S, B, Hq, Hkv, D, V, lo, hi, page, steps, switch, sample=None
         assert np.array_equal(pos.cpu().numpy()[sample], rpos), step
         assert np.array_equal(cl.cpu().numpy()[sample], olen2), step
         olen = olen2
-        accepted_total += int(n.sum().item())
+        accepted[step >= switch] += int(n.sum().item())
         if step % say_every == 0:
             say(f"  step {step}: mean accepted {float(n.float().mean()):.3f}, attn err {worst:.2e}")
     assert int(status.item()) == 0
@@ -205,21 +205,37 @@ def run_loop(seed, S, B, Hq, Hkv, D, V, lo, hi, page, steps, switch, sample=None
     vbits = cache_bits(vc)[pages]
     assert np.array_equal(kbits, synth.bf16_round(ok).view(np.int16))
     assert np.array_equal(vbits, synth.bf16_round(ov).view(np.int16))
-    return worst, accepted_total
+    return worst, accepted
+
+
+def accepted_count_law(tau, B, a=5.0):
+    """Mean and variance of n = max(1, leading run of p_r >= tau) for i.i.d. p_r ~ Beta(a, 1):
+    P(p >= tau) = q = 1 - tau^a, the run is k < B with probability q^k (1 - q), B with q^B."""
+    q = 1.0 - tau ** a
+    pmf = np.array([q ** k * (1 - q) for k in range(B)] + [q ** B])
+    n = np.maximum(np.arange(B + 1), 1)
+    mean = float((pmf * n).sum())
+    return mean, float((pmf * n * n).sum()) - mean * mean
 
 
 def test_decode_loop_small_all_sequences():
     say("[loop] S=12 B=8 V=4096, 64 steps, tau 0.9 -> 0.6 at step 32")
-    worst, total = run_loop(4200, 12, 8, 28, 4, 128, 4096, 20, 200, 16, 64, 32)
+    worst, _ = run_loop(4200, 12, 8, 28, 4, 128, 4096, 20, 200, 16, 64, 32)
     assert worst <= 2e-2
 
 
 def test_full_size_decode_loop_sampled_sequences():
     """256 sequences, B = 8, prompt lengths U[128, 2048], V = 152064, 64 steps."""
     say("[loop] full size: S=256 B=8 V=152064, 64 steps, 4 sampled sequences")
-    worst, total = run_loop(1005, 256, 8, 28, 4, 128, 152064, 128, 2048, 16, 64, 32,
-                            sample=[0, 77, 128, 255])
+    worst, accepted = run_loop(1005, 256, 8, 28, 4, 128, 152064, 128, 2048, 16, 64, 32,
+                               sample=[0, 77, 128, 255])
     assert worst <= 2e-2
-    # the Beta(5,1) construction predicts about 1.28 (tau 0.9) and 5.73 (tau 0.6) per sequence
-    mean = total / (256 * 64)
-    assert 2.5 < mean < 4.5, mean
+    # Each phase's mean accepted count per sequence against its closed form (about 1.2835
+    # at tau 0.9 and 5.7314 at tau 0.6 with B = 8): 32 steps x 256 sequences = 8192 draws
+    # per phase, within five standard errors of the law's variance.
+    for phase, tau in enumerate((0.9, 0.6)):
+        mean, var = accepted_count_law(tau, 8)
+        got = accepted[phase] / (256 * 32)
+        say(f"  tau {tau}: mean accepted {got:.4f}, closed form {mean:.4f}")
+        assert abs(got - mean) <= 5 * np.sqrt(var / (256 * 32)), (tau, got, mean)
+
