@@ -1,11 +1,13 @@
 """GPU parity: two-stream attention backward (dq, dk, dv) against the fp64 oracle.
 
 Inputs q, k, v, dO ~ N(0, 1) in bf16; o and lse come from the device forward.
-Tolerance: max |gpu - oracle| <= 2e-2 * max(1, max |oracle|) per tensor. The
-device rounds P and dS to bf16 before the P^T dO, dS^T Q and dS K products
-(relative 2^-9 each), uses the bf16 forward output in rowsum(dO * O), and
-rounds dq, dk, dv to bf16 (relative 2^-9 of values up to ~10 at these sizes).
+Tolerance: absolute, per tensor, 4 bfloat16 half-ulps at the tensor's largest
+magnitude (see check()). The device rounds P and dS to bf16 before the P^T dO,
+dS^T Q and dS K products (relative 2^-9 each), uses the bf16 forward output in
+rowsum(dO * O), and rounds dq, dk, dv to bf16.
 """
+
+import math
 
 import numpy as np
 import pytest
@@ -54,29 +56,37 @@ def run(seed, b, L, B, Hq, Hkv, d, mode=0, groups=None):
     return errs, refs
 
 
-def check(errs, refs, bounds):
-    """Absolute per-tensor bounds; the oracle's gradient scale they were set for must
-    not have moved (a bound is only meaningful for the magnitudes it was derived from)."""
-    for name, e, r, (bound, ref_max) in zip(("dq", "dk", "dv"), errs, refs, bounds):
-        assert abs(r - ref_max) <= 0.01 * ref_max, (name, r, ref_max)
-        assert e <= bound, (name, e, bound)
+def bf16_half_ulp(x):
+    """Half a unit in the last place of bfloat16 (8 significant bits) at magnitude x."""
+    return 2.0 ** (math.floor(math.log2(x)) - 8)
 
 
-# (b, L, B, Hq, Hkv, d, mode) -> per tensor (dq, dk, dv): (absolute bound, the oracle's
-# max |gradient| for these seeded inputs). Each bound is 1/50 of that magnitude.
+def check(errs, refs, ref_max):
+    """Absolute per-tensor bounds: 4 bf16 half-ulps at the tensor's largest magnitude
+    (the oracle's, recorded below for these seeded inputs; it must not have moved, since
+    the bound was derived for it). The device's bf16 output rounding costs up to one half
+    ulp; the bf16 rounding of P and dS before the products and the bf16 forward output
+    inside rowsum(dO * O) add the rest (measured at 0.6 to 1.4 half-ulps)."""
+    for name, e, r, rm in zip(("dq", "dk", "dv"), errs, refs, ref_max):
+        assert abs(r - rm) <= 0.01 * rm, (name, r, rm)
+        assert e <= 4 * bf16_half_ulp(rm), (name, e, 4 * bf16_half_ulp(rm))
+
+
+# (b, L, B, Hq, Hkv, d, mode) -> the oracle's max |dq|, max |dk|, max |dv| for the
+# seeded inputs of run(6000 + L, ...)
 CASES = {
-    (1, 256, 4, 4, 2, 64, 0): ((0.043, 2.146), (0.069, 3.463), (0.135, 6.766)),
-    (1, 200, 7, 2, 2, 64, 0): ((0.034, 1.702), (0.060, 2.984), (0.089, 4.474)),
-    (1, 130, 1, 2, 1, 128, 0): ((0.065, 3.243), (0.084, 4.182), (0.145, 7.246)),
-    (1, 96, 96, 2, 2, 64, 0): ((0.043, 2.175), (0.059, 2.930), (0.089, 4.473)),
-    (1, 5, 2, 1, 1, 64, 0): ((0.042, 2.103), (0.030, 1.487), (0.070, 3.488)),
-    (1, 200, 4, 4, 2, 128, 1): ((0.044, 2.204), (0.077, 3.871), (0.108, 5.399)),
-    (2, 320, 8, 6, 3, 64, 1): ((0.057, 2.858), (0.076, 3.793), (0.115, 5.733)),
-    (1, 256, 16, 8, 2, 128, 0): ((0.073, 3.629), (0.087, 4.355), (0.163, 8.166)),
-    (1, 160, 16, 7, 1, 128, 0): ((0.084, 4.215), (0.126, 6.280), (0.212, 10.619)),
+    (1, 256, 4, 4, 2, 64, 0): (2.146, 3.463, 6.766),
+    (1, 200, 7, 2, 2, 64, 0): (1.702, 2.984, 4.474),
+    (1, 130, 1, 2, 1, 128, 0): (3.243, 4.182, 7.246),
+    (1, 96, 96, 2, 2, 64, 0): (2.175, 2.930, 4.473),
+    (1, 5, 2, 1, 1, 64, 0): (2.103, 1.487, 3.488),
+    (1, 200, 4, 4, 2, 128, 1): (2.204, 3.871, 5.399),
+    (2, 320, 8, 6, 3, 64, 1): (2.858, 3.793, 5.733),
+    (1, 256, 16, 8, 2, 128, 0): (3.629, 4.355, 8.166),
+    (1, 160, 16, 7, 1, 128, 0): (4.215, 6.280, 10.619),
 }
-FULL_05B = ((0.061, 3.0405), (0.145, 7.2636), (0.251, 12.5279))
-FULL_7B = ((0.073, 3.6721), (0.146, 7.2799), (0.267, 13.3539))
+FULL_05B = (3.0405, 7.2636, 12.5279)
+FULL_7B = (3.6721, 7.2799, 13.3539)
 CASE_NOTES = ["several 128-row / 128-key blocks, GQA 2",
               "L not a multiple of 32: blocks straddle the streams", "B = 1", "B = L",
               "a single partial block", "causal over 2L", "batch 2, GQA 3", "GQA 4, d = 128",
