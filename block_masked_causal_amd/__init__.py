@@ -28,6 +28,7 @@ from .api import (  # noqa: F401
     mars_block_sync_accept,
     mars_block_freeze,
     mars_lmhead_confidence,
+    mars_lmhead_confidence_noalloc,
     mars_lmhead_pack,
     PackedLMHead,
     mars_lmhead_workspace_bytes,

@@ -23,6 +23,8 @@ MARS_ERR_LAUNCH = -7
 MARS_F32 = 0
 MARS_BF16 = 1
 
+NOALLOC_SCRATCH_BYTES = 16 << 20  # MARS_NOALLOC_SCRATCH_BYTES
+
 STATUS_CACHE_OVERFLOW = 1
 STATUS_BAD_PAGE = 2
 STATUS_NONFINITE = 4
@@ -57,6 +59,8 @@ SIGNATURES = {
     "mars_lmhead_confidence": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _sz,
                                               _p, _p]),
     "mars_lmhead_workspace_bytes": (_sz, [_i32, _i32]),
+    "mars_lmhead_confidence_noalloc": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p,
+                                                      _p]),
     "mars_lmhead_packed_bytes": (_sz, [_i32, _i32]),
     "mars_lmhead_pack": (ctypes.c_int, [_p, _p, _i32, _i32, _p]),
     "mars_lmhead_confidence_packed": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _p, _p, _p,

@@ -453,3 +453,48 @@ def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block
         _ptr(status), _stream(stream))
     check("mars_accept_commit", code)
     return n_accepted, accepted_ids, commit_pos
+
+
+def mars_lmhead_confidence_noalloc(hidden, w_lm, logits=None, *, top_id=None, p_max=None,
+                                   status=None, stream=None, fused=False):
+    """As mars_lmhead_confidence (row-major w_lm [V, D], or hidden None with `logits`
+    as the input), with no workspace: the library keeps the partials in its own
+    fixed device array (for callers that cannot allocate device memory). Pass
+    top_id and p_max to allocate nothing here either. Returns (logits, top_id, p_max)."""
+    if isinstance(w_lm, PackedLMHead):
+        raise ValueError("the no-workspace call takes row-major weights [V, D]")
+    if hidden is not None:
+        _need(hidden, "hidden", torch.bfloat16, 2)
+        N, D = hidden.shape
+        _need(w_lm, "w_lm", torch.bfloat16, 2)
+        V = w_lm.shape[0]
+        if w_lm.shape[1] != D:
+            raise ValueError(f"w_lm must be [V, {D}] (got {tuple(w_lm.shape)})")
+        if fused:
+            if logits is not None:
+                raise ValueError("fused=True writes no logits; pass logits=None")
+        else:
+            _opt(logits, "logits", torch.float32, 2, (N, V))
+    else:
+        if logits is None or fused:
+            raise ValueError("logits are required (and fused is off) when hidden is None")
+        _need(logits, "logits", torch.float32, 2)
+        N, V = logits.shape
+        D = 0
+    _opt(top_id, "top_id", torch.int32, 1, (N,))
+    _opt(p_max, "p_max", torch.float32, 1, (N,))
+    _status(status)
+    _on_gpu(hidden=hidden, w_lm=w_lm if hidden is not None else None, logits=logits,
+            top_id=top_id, p_max=p_max, status=status)
+    dev = hidden.device if hidden is not None else logits.device
+    if logits is None and not fused:
+        logits = torch.empty((N, V), dtype=torch.float32, device=dev)
+    if top_id is None:
+        top_id = torch.empty(N, dtype=torch.int32, device=dev)
+    if p_max is None:
+        p_max = torch.empty(N, dtype=torch.float32, device=dev)
+    code = _lib.lib().mars_lmhead_confidence_noalloc(
+        _ptr(hidden), _ptr(w_lm) if hidden is not None else None, _ptr(logits), N, D, V,
+        _ptr(top_id), _ptr(p_max), _ptr(status), _stream(stream))
+    check("mars_lmhead_confidence_noalloc", code)
+    return logits, top_id, p_max

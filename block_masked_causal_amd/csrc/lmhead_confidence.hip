@@ -19,6 +19,7 @@
 //  * conf_merge_kernel: combines the chunks of a row in a fixed order:
 //    top_id = lowest index attaining the maximum, p_max = 1 / sum exp(l - m).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "mars_common.hpp"
@@ -489,17 +490,25 @@ int cu_count() {
   return n;
 }
 
-template <bool FUSED>
-int launch_gemm(GemmArgs g, int row_tiles, hipStream_t st) {
-  const int full = (g.V + GN - 1) / GN;
+// The GEMM's vocabulary tiling: main_tiles of GN entries, then tail_tiles of
+// GN_TAIL. Their sum is the number of confidence partials per row.
+void gemm_tiles(int V, int row_tiles, int* main_tiles, int* tail_tiles) {
+  const int full = (V + GN - 1) / GN;
   const int ncu = cu_count();
-  int main_tiles = full;
+  int m = full;
   if (row_tiles == 1 && ncu > 0 && full > ncu) {
     const int r = full % ncu;
-    if (r > 0 && (GN / GN_TAIL) * r <= ncu) main_tiles = full - r;
+    if (r > 0 && (GN / GN_TAIL) * r <= ncu) m = full - r;
   }
-  const int tail_v = g.V - main_tiles * GN;  // entries left to the narrow tiles
-  const int tail_tiles = tail_v > 0 ? (tail_v + GN_TAIL - 1) / GN_TAIL : 0;
+  const int tail_v = V - m * GN;  // entries left to the narrow tiles
+  *main_tiles = m;
+  *tail_tiles = tail_v > 0 ? (tail_v + GN_TAIL - 1) / GN_TAIL : 0;
+}
+
+template <bool FUSED>
+int launch_gemm(GemmArgs g, int row_tiles, hipStream_t st) {
+  int main_tiles, tail_tiles;
+  gemm_tiles(g.V, row_tiles, &main_tiles, &tail_tiles);
   g.nvt = main_tiles + tail_tiles;
   g.v_base = 0;
   g.tile0 = 0;
@@ -526,9 +535,9 @@ extern "C" size_t mars_lmhead_workspace_bytes(int32_t N, int32_t V) {
 }
 
 namespace {
-int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, int32_t N,
-               int32_t D, int32_t V, int32_t* top_id, float* p_max, void* workspace,
-               size_t workspace_bytes, int32_t* status, void* stream) {
+// Argument checks shared by every LM-head entry point (not the workspace).
+int check_lmhead(const void* hidden, const void* w_lm, const float* logits, int32_t N, int32_t D,
+                 int32_t V, const int32_t* top_id, const float* p_max) {
   MARS_REQUIRE(top_id && p_max, MARS_ERR_NULL);
   MARS_REQUIRE(!hidden || w_lm, MARS_ERR_NULL);
   MARS_REQUIRE(hidden || logits, MARS_ERR_NULL);  // logits may be omitted only when fused
@@ -541,18 +550,35 @@ int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, 
     MARS_REQUIRE((double)GN * D * 2 < 4294967295.0, MARS_ERR_SHAPE);
   }
   MARS_REQUIRE(mars_aligned16(hidden) && mars_aligned16(w_lm) && mars_aligned16(logits) &&
-                   mars_aligned16(top_id) && mars_aligned16(p_max) &&
-                   mars_aligned16(workspace),
+                   mars_aligned16(top_id) && mars_aligned16(p_max),
                MARS_ERR_ALIGN);
-  const size_t need = mars_lmhead_workspace_bytes(N, V);
-  MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
-  hipStream_t st = (hipStream_t)stream;
+  return MARS_OK;
+}
 
+// Bytes of partials the call actually uses: one per (row, vocabulary tile) on
+// the fused path, one per (row, chunk) when the confidence reads logits.
+size_t lmhead_need_bytes(bool fused, int32_t N, int32_t V) {
+  int nparts;
+  if (fused) {
+    int main_tiles, tail_tiles;
+    gemm_tiles(V, (N + GM - 1) / GM, &main_tiles, &tail_tiles);
+    nparts = main_tiles + tail_tiles;
+  } else {
+    int chunk;
+    conf_layout(N, V, &nparts, &chunk);
+  }
+  return (size_t)N * nparts * sizeof(ConfPart);
+}
+
+// Enqueues the call with `part` (16-byte aligned, large enough) as the partials.
+int launch_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, int32_t N,
+                  int32_t D, int32_t V, int32_t* top_id, float* p_max, ConfPart* part,
+                  int32_t* status, hipStream_t st) {
   ConfArgs c;
   c.logits = logits;
   c.top_id = top_id;
   c.p_max = p_max;
-  c.part = (ConfPart*)workspace;
+  c.part = part;
   c.status = status;
   c.N = N;
   c.V = V;
@@ -562,7 +588,7 @@ int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, 
     g.w = (const bf16_t*)w_lm;
     g.packed = packed;
     g.logits = logits;
-    g.part = (ConfPart*)workspace;
+    g.part = part;
     g.status = status;
     g.N = N;
     g.D = D;
@@ -583,6 +609,18 @@ int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, 
   hipLaunchKernelGGL(conf_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, c);
   return mars_launch_status();
 }
+
+int run_lmhead(const void* hidden, const void* w_lm, int packed, float* logits, int32_t N,
+               int32_t D, int32_t V, int32_t* top_id, float* p_max, void* workspace,
+               size_t workspace_bytes, int32_t* status, void* stream) {
+  const int err = check_lmhead(hidden, w_lm, logits, N, D, V, top_id, p_max);
+  if (err != MARS_OK) return err;
+  MARS_REQUIRE(mars_aligned16(workspace), MARS_ERR_ALIGN);
+  const size_t need = mars_lmhead_workspace_bytes(N, V);
+  MARS_REQUIRE(workspace && workspace_bytes >= need, MARS_ERR_WORKSPACE);
+  return launch_lmhead(hidden, w_lm, packed, logits, N, D, V, top_id, p_max,
+                       (ConfPart*)workspace, status, (hipStream_t)stream);
+}
 }  // namespace
 
 extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits,
@@ -591,6 +629,47 @@ extern "C" int mars_lmhead_confidence(const void* hidden, const void* w_lm, floa
                                       int32_t* status, void* stream) {
   return run_lmhead(hidden, w_lm, 0, logits, N, D, V, top_id, p_max, workspace,
                     workspace_bytes, status, stream);
+}
+
+// ---- the same call without a workspace argument -----------------------------
+// The confidence partials live in `scratch`, a library-owned device array. In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device with hipGetSymbolAddress (with
+// that device current) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MARS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`, or NULL on a HIP error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int mars_lmhead_confidence_noalloc(const void* hidden, const void* w_lm,
+                                              float* logits, int32_t N, int32_t D, int32_t V,
+                                              int32_t* top_id, float* p_max, int32_t* status,
+                                              void* stream) {
+  const int err = check_lmhead(hidden, w_lm, logits, N, D, V, top_id, p_max);
+  if (err != MARS_OK) return err;
+  const bool fused = hidden != nullptr && logits == nullptr;
+  MARS_REQUIRE(lmhead_need_bytes(fused, N, V) <= (size_t)MARS_NOALLOC_SCRATCH_BYTES,
+               MARS_ERR_WORKSPACE);
+  void* part = scratch_address();
+  MARS_REQUIRE(part != nullptr, MARS_ERR_LAUNCH);
+  return launch_lmhead(hidden, w_lm, 0, logits, N, D, V, top_id, p_max, (ConfPart*)part,
+                       status, (hipStream_t)stream);
 }
 
 extern "C" size_t mars_lmhead_packed_bytes(int32_t D, int32_t V) {

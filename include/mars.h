@@ -16,6 +16,7 @@
  *   mars_attn_block_decode_rows  the same with a per-sequence row count
  *   mars_lmhead_confidence  LM-head GEMM + per-position argmax / max-softmax
  *   mars_lmhead_confidence_packed  the same on weights packed by mars_lmhead_pack
+ *   mars_lmhead_confidence_noalloc the same with no workspace argument
  *   mars_accept_commit      left-to-right acceptance + KV commit of the prefix
  *   mars_kv_append          paged KV append of a prompt
  *   mars_block_sync_accept  acceptance under the batch-synchronous block cache
@@ -26,7 +27,8 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller. The library
  *    allocates no device memory and keeps no state between calls; scratch
  *    space, where needed, is a caller-provided `workspace` whose size the
- *    matching *_workspace_bytes() helper returns.
+ *    matching *_workspace_bytes() helper returns (mars_lmhead_confidence_noalloc
+ *    alone uses a fixed library-owned array instead; see there).
  *  - Tensors are dense, row-major (C order), in the layouts stated per call.
  *    Every tensor pointer must be 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -335,6 +337,31 @@ int mars_lmhead_confidence_packed(const void* hidden, const void* w_packed, floa
                                   int32_t N, int32_t D, int32_t V, int32_t* top_id,
                                   float* p_max, void* workspace, size_t workspace_bytes,
                                   int32_t* status, void* stream);
+
+/*
+ * mars_lmhead_confidence without a workspace argument: the entry point for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, layouts, results and errors as mars_lmhead_confidence (row-major
+ * w_lm; hidden may be NULL for the confidence alone). The confidence partials
+ * live in a library-owned device array of MARS_NOALLOC_SCRATCH_BYTES per GPU,
+ * created with the library's code object on each GPU and held until the
+ * process ends; the call allocates nothing. It needs N * P * 16 bytes of that
+ * array, where P is the number of vocabulary tiles of the GEMM (about V / 320)
+ * when the confidence is fused into the LM head (hidden != NULL, logits ==
+ * NULL), else the number of row chunks of the confidence pass (at most 32);
+ * beyond MARS_NOALLOC_SCRATCH_BYTES it returns MARS_ERR_WORKSPACE and enqueues
+ * nothing. At V = 152064 the fused form takes up to 2202 rows.
+ * Every call on one GPU shares that GPU's array and leaves its partials there:
+ * calls that may overlap on one GPU (other streams, no ordering between them)
+ * race on it and must not be made. No part of the array needs to start at
+ * zero (each partial is written before it is read).
+ */
+#define MARS_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mars_lmhead_confidence_noalloc(const void* hidden, const void* w_lm, float* logits,
+                                   int32_t N, int32_t D, int32_t V, int32_t* top_id,
+                                   float* p_max, int32_t* status, void* stream);
 
 /*
  * Left-to-right acceptance + KV commit of the accepted prefix.
