@@ -86,14 +86,18 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 
 // As lds_load16, but issued as inline assembly so that the compiler inserts
 // no waits of its own for it: the caller waits with wait_vm_upto before the
-// barrier that publishes the data. M0 is declared clobbered, so the compiler
-// keeps none of its own values in it across the call.
+// barrier that publishes the data.
+// The asm writes M0. The compiler treats M0 as a reserved register: it keeps
+// no value of its own there across statements (it sets M0 right before each
+// instruction that reads it) and refuses M0 in a clobber list. The one case in
+// which it may reuse an M0 value it set is a run of its own direct-load
+// builtins, so a kernel uses either this or lds_load16, never both.
 __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, void* lds_block, uint32_t byte_off) {
   const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_block;
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(la), "v"(byte_off), "s"(rsrc)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Wait until at most N vector-memory loads of this wave are in flight (loads
