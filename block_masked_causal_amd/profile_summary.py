@@ -61,6 +61,7 @@ SOURCES = {
 COPY_KERNEL = "copyBuffer"
 MARKER = "FillFunctor<long>"
 SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCCS = 8      # MI355X: 8 XCDs; each counts GRBM_GUI_ACTIVE, and the CSV holds their sum
 
 
 def sources_sha256(files) -> str:
@@ -95,7 +96,8 @@ def stats(args) -> None:
 
 
 def dispatches(path: str):
-    """[(dispatch id, kernel name, {counter: value summed over dimensions})] in order."""
+    """[(dispatch id, kernel name, {counter: value})] in order (values summed over any
+    dimension rows; rocprofv3's CSV already holds one chip-wide sum per counter)."""
     acc = collections.defaultdict(lambda: collections.defaultdict(float))
     names = {}
     for r in csv.DictReader(open(path)):
@@ -105,18 +107,33 @@ def dispatches(path: str):
     return [(k, names[k], dict(acc[k])) for k in sorted(acc)]
 
 
+def calibration_index(rows):
+    """Index of the calibration copy: the first copy after the first marker (the pass
+    creates the marker tensor, then copies the buffer of known size, then launches
+    the calls, each after a marker fill)."""
+    first = next((i for i, (_, n, _) in enumerate(rows) if MARKER in n), None)
+    if first is None:
+        raise SystemExit("no marker dispatch found")
+    for i in range(first + 1, len(rows)):
+        if COPY_KERNEL in rows[i][1]:
+            return i
+    raise SystemExit("no calibration copy dispatch found after the first marker")
+
+
 def segments(rows, plan):
-    """call name -> its dispatches (those after the call's marker, before the next)."""
+    """call name -> its dispatches (those after the call's marker, before the next),
+    counting markers from the calibration copy on. Runtime copies (the host reading a
+    status word after the last call) are not the library's and are left out."""
     out = collections.OrderedDict()
     cur = -1
-    for k, name, vals in rows:
+    for k, name, vals in rows[calibration_index(rows) + 1:]:
         if MARKER in name:
             cur += 1
             if cur >= len(plan):
                 raise SystemExit(f"more markers than calls in the plan ({len(plan)})")
             out[plan[cur]] = []
             continue
-        if cur >= 0:
+        if cur >= 0 and COPY_KERNEL not in name:
             out[plan[cur]].append((k, name, vals))
     if cur != len(plan) - 1:
         raise SystemExit(f"found {cur + 1} markers for {len(plan)} calls")
@@ -124,10 +141,7 @@ def segments(rows, plan):
 
 
 def _copy_value(rows, counter):
-    vals = [v[counter] for _, n, v in rows if COPY_KERNEL in n and counter in v]
-    if not vals:
-        raise SystemExit("no calibration copy dispatch found")
-    return max(vals)  # the large calibration copy, not small incidental copies
+    return rows[calibration_index(rows)][2][counter]
 
 
 def traffic(args) -> None:
@@ -187,23 +201,24 @@ def counters(args) -> None:
     lines = [f"# {args.title}", "", "Command (on one MI355X; $REPO is the repository root):", "",
              "```", args.cmd, "```", "",
              "One row per kernel dispatch of `bench.py --profile-pass` (one launch of every "
-             "hot-path call). GRBM_GUI_ACTIVE is the dispatch's GPU-busy cycles; the SQ "
-             "counters are summed over the chip. Derived columns:", "",
-             f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMDS} SIMDs) x "
-             "100 (rocprofv3's MfmaUtil): the share of SIMD cycles the matrix core was busy;",
+             "hot-path call). Every counter is the chip-wide sum rocprofv3 writes; each of "
+             f"the {XCCS} XCCs counts GRBM_GUI_ACTIVE, so the dispatch's busy cycles are "
+             f"GRBM_GUI_ACTIVE / {XCCS} (the cycles column). Derived columns:", "",
+             f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {SIMDS} SIMDs) x 100 "
+             "(rocprofv3's MfmaUtil): the share of SIMD cycles the matrix core was busy;",
              "- MFMA GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 1e9 (the counter counts "
              "bf16 MFMA flops in units of 512), i.e. the flops the kernel computed, masked "
              "or not;",
              "- VALU / MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA (instructions issued);",
-             "- VALU busy % = SQ_ACTIVE_INST_VALU x 4 / (GRBM_GUI_ACTIVE x "
-             f"{SIMDS}) x 100 (the counter is in quad-cycles);",
+             f"- VALU busy % = SQ_ACTIVE_INST_VALU x 4 / (cycles x {SIMDS}) x 100 (the "
+             "counter is in quad-cycles);",
              "- LDS bank-conflict cycles, summed over the chip.", "",
-             "| call | kernel | GRBM_GUI_ACTIVE | MFMA busy % | MFMA GFLOP | VALU / MFMA | "
+             "| call | kernel | cycles | MFMA busy % | MFMA GFLOP | VALU / MFMA | "
              "VALU busy % | LDS bank-conflict cycles |",
              "|---|---|---|---|---|---|---|---|"]
     for call, disp in segs.items():
         for _, name, v in disp:
-            gui = v.get("GRBM_GUI_ACTIVE", 0.0)
+            gui = v.get("GRBM_GUI_ACTIVE", 0.0) / XCCS
             busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
             mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
             nmfma = v.get("SQ_INSTS_MFMA", 0.0)

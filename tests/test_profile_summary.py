@@ -34,8 +34,9 @@ def test_traffic_scales_by_copy_and_splits_calls_at_markers(tmp_path):
     # FETCH_SIZE reads half of the copy, WRITE_SIZE all of it; the same kernels serve
     # two calls, told apart only by the marker dispatch before each
     _csv(tmp_path / "f.csv", "FETCH_SIZE", [
-        (1, "__amd_rocclr_copyBuffer", [256.0, 256.0]),
-        (2, "__amd_rocclr_copyBuffer", [1.0]),                # small incidental copy
+        (0, "__amd_rocclr_copyBuffer", [900.0]),              # a setup copy before the pass
+        (1, MARK, [0.0]),                                     # the marker tensor is created
+        (2, "__amd_rocclr_copyBuffer", [256.0, 256.0]),       # the calibration copy
         (3, MARK, [0.0]),
         (4, "void decode_split_kernel<128, 16>(DecodeArgs)", [100.0]),
         (5, "void decode_merge_kernel<128>(DecodeArgs)", [10.0]),
@@ -43,8 +44,9 @@ def test_traffic_scales_by_copy_and_splits_calls_at_markers(tmp_path):
         (7, "void decode_split_kernel<128, 16>(DecodeArgs)", [300.0]),
     ])
     _csv(tmp_path / "w.csv", "WRITE_SIZE", [
-        (1, "__amd_rocclr_copyBuffer", [1024.0]),
-        (2, "__amd_rocclr_copyBuffer", [2.0]),
+        (0, "__amd_rocclr_copyBuffer", [1800.0]),
+        (1, MARK, [0.0]),
+        (2, "__amd_rocclr_copyBuffer", [1024.0]),
         (3, MARK, [0.0]),
         (4, "void decode_split_kernel<128, 16>(DecodeArgs)", [40.0]),
         (5, "void decode_merge_kernel<128>(DecodeArgs)", [4.0]),
@@ -72,11 +74,14 @@ def test_traffic_scales_by_copy_and_splits_calls_at_markers(tmp_path):
 
 def test_segments_reject_a_plan_that_does_not_match_the_markers(tmp_path):
     import pytest
-    rows = [(1, MARK, {}), (2, "k", {"X": 1.0})]
+    rows = [(0, MARK, {}), (1, "__amd_rocclr_copyBuffer", {}), (2, MARK, {}),
+            (3, "k", {"X": 1.0})]
     with pytest.raises(SystemExit):
         ps.segments(rows, ["a", "b"])
     with pytest.raises(SystemExit):
-        ps.segments(rows + [(3, MARK, {}), (4, MARK, {})], ["a", "b"])
+        ps.segments(rows + [(4, MARK, {}), (5, MARK, {})], ["a", "b"])
+    with pytest.raises(SystemExit):
+        ps.segments(rows[2:], ["a"])          # no calibration copy after a marker
     assert list(ps.segments(rows, ["a"])) == ["a"]
 
 
@@ -87,11 +92,13 @@ def test_counter_table_derives_mfma_busy(tmp_path):
     with open(path, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(HEAD)
-        rows = [(1, MARK, "GRBM_GUI_ACTIVE", 5.0),
-                (2, "K", "GRBM_GUI_ACTIVE", 1000.0),
-                (2, "K", "SQ_VALU_MFMA_BUSY_CYCLES", 256000.0),
-                (2, "K", "SQ_INSTS_MFMA", 10.0),
-                (2, "K", "SQ_INSTS_VALU", 135.0)]
+        rows = [(0, MARK, "GRBM_GUI_ACTIVE", 5.0),
+                (1, "__amd_rocclr_copyBuffer", "GRBM_GUI_ACTIVE", 50.0),
+                (2, MARK, "GRBM_GUI_ACTIVE", 5.0),
+                (3, "K", "GRBM_GUI_ACTIVE", 8000.0),
+                (3, "K", "SQ_VALU_MFMA_BUSY_CYCLES", 256000.0),
+                (3, "K", "SQ_INSTS_MFMA", 10.0),
+                (3, "K", "SQ_INSTS_VALU", 135.0)]
         for disp, name, ctr, val in rows:
             w.writerow([disp, disp, "Agent 1", 1, 1, 1, 64, 1, name, 64, 0, 0, 8, 0, 8,
                         ctr, val, 0, 1])
