@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     mars_accept_commit,
+    mars_accept_commit_layers,
     mars_attn_block_decode,
     mars_attn_causal,
     mars_attn_two_stream,

@@ -67,6 +67,9 @@ SIGNATURES = {
                                                      _sz, _p, _p]),
     "mars_accept_commit": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32,
                                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
+    "mars_accept_commit_layers": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, _p, _p]),
     "mars_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "mars_version": (ctypes.c_int, []),
 }

@@ -410,22 +410,32 @@ def mars_lmhead_confidence(hidden, w_lm, logits=None, *, top_id=None, p_max=None
     return logits, top_id, p_max
 
 
-def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
-                       cache_len, *, n_accepted=None, accepted_ids=None, commit_pos=None,
-                       status=None, stream=None):
-    """Acceptance + KV commit. p_max [S,B] fp32, top_id [S,B] int32, tau [S] fp32,
-    k_new/v_new [S,B,Hkv,d]; caches as for decode; cache_len updated in place.
-    Returns (n_accepted [S], accepted_ids [S,B], commit_pos [S,B])."""
+def _commit_args(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table, cache_len,
+                 n_accepted, accepted_ids, commit_pos, status, layered):
+    """Shape checks of the commit calls; returns (S, B, Hkv, d, page, num_pages, layers)."""
     _need(p_max, "p_max", torch.float32, 2)
     S, B = p_max.shape
     _need(top_id, "top_id", torch.int32, 2, (S, B))
     _need(tau, "tau", torch.float32, 1, (S,))
     dt = k_new.dtype
-    _need(k_new, "k_new", dt, 4)
-    Hkv, d = k_new.shape[2], k_new.shape[3]
-    _need(k_new, "k_new", dt, 4, (S, B, Hkv, d))
-    _need(v_new, "v_new", dt, 4, (S, B, Hkv, d))
-    num_pages, page = _paged_cache(k_cache, v_cache, dt, Hkv, d)
+    if layered:
+        _need(k_new, "k_new", dt, 5)
+        layers, Hkv, d = k_new.shape[0], k_new.shape[3], k_new.shape[4]
+        rows = (layers, S, B, Hkv, d)
+        _need(k_cache, "k_cache", dt, 5)
+        if k_cache.shape[0] != layers:
+            raise ValueError(f"k_cache must hold {layers} layers (got {k_cache.shape[0]})")
+        _need(v_cache, "v_cache", dt, 5)
+        if v_cache.shape[0] != layers:
+            raise ValueError(f"v_cache must hold {layers} layers (got {v_cache.shape[0]})")
+        num_pages, page = _paged_cache(k_cache[0], v_cache[0], dt, Hkv, d)
+    else:
+        _need(k_new, "k_new", dt, 4)
+        layers, Hkv, d = 1, k_new.shape[2], k_new.shape[3]
+        rows = (S, B, Hkv, d)
+        num_pages, page = _paged_cache(k_cache, v_cache, dt, Hkv, d)
+    _need(k_new, "k_new", dt, len(rows), rows)
+    _need(v_new, "v_new", dt, len(rows), rows)
     _need(block_table, "block_table", torch.int32, 2)
     if block_table.shape[0] != S:
         raise ValueError(f"block_table must have {S} rows (got {block_table.shape[0]})")
@@ -438,7 +448,11 @@ def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block
             v_cache=v_cache, block_table=block_table, cache_len=cache_len,
             n_accepted=n_accepted, accepted_ids=accepted_ids, commit_pos=commit_pos,
             status=status)
-    max_pages = block_table.shape[1]
+    return S, B, Hkv, d, page, num_pages, layers
+
+
+def _commit_outputs(p_max, n_accepted, accepted_ids, commit_pos):
+    S, B = p_max.shape
     dev = p_max.device
     if n_accepted is None:
         n_accepted = torch.empty(S, dtype=torch.int32, device=dev)
@@ -446,12 +460,47 @@ def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block
         accepted_ids = torch.empty((S, B), dtype=torch.int32, device=dev)
     if commit_pos is None:
         commit_pos = torch.empty((S, B), dtype=torch.int32, device=dev)
+    return n_accepted, accepted_ids, commit_pos
+
+
+def mars_accept_commit(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
+                       cache_len, *, n_accepted=None, accepted_ids=None, commit_pos=None,
+                       status=None, stream=None):
+    """Acceptance + KV commit. p_max [S,B] fp32, top_id [S,B] int32, tau [S] fp32,
+    k_new/v_new [S,B,Hkv,d]; caches as for decode; cache_len updated in place.
+    Returns (n_accepted [S], accepted_ids [S,B], commit_pos [S,B])."""
+    S, B, Hkv, d, page, num_pages, _ = _commit_args(
+        p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_accepted,
+        accepted_ids, commit_pos, status, layered=False)
+    n_accepted, accepted_ids, commit_pos = _commit_outputs(p_max, n_accepted, accepted_ids,
+                                                           commit_pos)
     code = _lib.lib().mars_accept_commit(
         _ptr(p_max), _ptr(top_id), _ptr(tau), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_table), _ptr(cache_len), _ptr(n_accepted), _ptr(accepted_ids),
-        _ptr(commit_pos), S, B, Hkv, d, page, max_pages, num_pages, _DT.get(dt, -1),
-        _ptr(status), _stream(stream))
+        _ptr(commit_pos), S, B, Hkv, d, page, block_table.shape[1], num_pages,
+        _DT.get(k_new.dtype, -1), _ptr(status), _stream(stream))
     check("mars_accept_commit", code)
+    return n_accepted, accepted_ids, commit_pos
+
+
+def mars_accept_commit_layers(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
+                              cache_len, *, n_accepted=None, accepted_ids=None, commit_pos=None,
+                              status=None, stream=None):
+    """As mars_accept_commit, committing into every layer: k_new/v_new
+    [layers,S,B,Hkv,d], k_cache [layers,pages,Hkv,page,d], v_cache
+    [layers,pages,Hkv,d,page]; one block table and cache_len for all layers.
+    Returns (n_accepted [S], accepted_ids [S,B], commit_pos [S,B])."""
+    S, B, Hkv, d, page, num_pages, layers = _commit_args(
+        p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table, cache_len, n_accepted,
+        accepted_ids, commit_pos, status, layered=True)
+    n_accepted, accepted_ids, commit_pos = _commit_outputs(p_max, n_accepted, accepted_ids,
+                                                           commit_pos)
+    code = _lib.lib().mars_accept_commit_layers(
+        _ptr(p_max), _ptr(top_id), _ptr(tau), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), _ptr(cache_len), _ptr(n_accepted), _ptr(accepted_ids),
+        _ptr(commit_pos), layers, S, B, Hkv, d, page, block_table.shape[1], num_pages,
+        _DT.get(k_new.dtype, -1), _ptr(status), _stream(stream))
+    check("mars_accept_commit_layers", code)
     return n_accepted, accepted_ids, commit_pos
 
 

@@ -37,6 +37,7 @@ struct CommitArgs {
   int32_t* commit_pos;
   int32_t* status;
   int S, B, Hkv, D, page_size, max_pages, num_pages;
+  int layers;  // caches and new rows hold this many layers, back to back
 };
 
 // Accepted count of one row of B max-probabilities: the leading run of
@@ -47,104 +48,110 @@ __device__ __forceinline__ int accepted_count(const float* pr, int B, float tau)
   return n < 1 ? 1 : n;
 }
 
-constexpr int kCommitStageBytes = 16384;  // LDS staging of V rows in the commit
-
-template <int ES>  // element size in bytes (2 = bf16, 4 = fp32)
-__global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
-  __shared__ int sh_page[kMaxB];
-  __shared__ int sh_len, sh_nc;
-  __shared__ __attribute__((aligned(16))) char vst[kCommitStageBytes];
-  const int s = blockIdx.x, tid = threadIdx.x;
-  if (tid < 64) {
-    // Wave 0, lane r = position r: the accepted count is the run of set bits
-    // at the bottom of the ballot of p >= tau (a NaN compares false), at
-    // least 1; then each accepted row resolves its page in parallel and the
-    // commit keeps the rows before the first one that cannot be placed.
-    const int r = tid;
-    const bool pass = r < p.B && p.p_max[(size_t)s * p.B + r] >= p.tau[s];
-    const uint64_t pm = __ballot(pass);
-    const int n = max(pm == ~0ull ? 64 : __builtin_ctzll(~pm), 1);
-    const int len = p.cache_len[s];
-    const long long cap = (long long)p.max_pages * p.page_size;
-    int pg = -1;
-    int32_t flag = 0;
-    if (r < n) {
-      const long long pos = (long long)len + r;
-      if (len < 0 || pos >= cap) {
-        flag = MARS_STATUS_CACHE_OVERFLOW;
-      } else {
-        pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
-        if (pg < 0 || pg >= p.num_pages) flag = MARS_STATUS_BAD_PAGE;
-      }
-    }
-    const uint64_t gm = __ballot(r < n && flag == 0);
-    const int nc = gm == ~0ull ? 64 : __builtin_ctzll(~gm);  // rows placed
-    if (r == nc && r < n) status_or(p.status, flag);          // the first failure
-    if (r < nc) sh_page[r] = pg;
-    if (r < p.B) {
-      p.accepted_ids[(size_t)s * p.B + r] = r < n ? p.top_id[(size_t)s * p.B + r] : -1;
-      p.commit_pos[(size_t)s * p.B + r] = r < nc ? len + r : -1;
-    }
-    if (r == 0) {
-      p.n_accepted[s] = n;
-      sh_len = len;
-      sh_nc = nc;
+// The decision of sequence s, taken by one whole wave with lane r = position
+// r: the accepted count is the run of set bits at the bottom of the ballot of
+// p >= tau (a NaN compares false), at least 1; each accepted row resolves its
+// page in parallel and the commit keeps the rows before the first one that
+// cannot be placed. Writes n_accepted, accepted_ids, commit_pos and the first
+// failure's status flag; returns the rows placed (nc) and the old length, and
+// the page of row r in *pg (rows r < nc).
+__device__ __forceinline__ int decide(const CommitArgs& p, int s, int r, int* len_out, int* pg_out) {
+  const bool pass = r < p.B && p.p_max[(size_t)s * p.B + r] >= p.tau[s];
+  const uint64_t pm = __ballot(pass);
+  const int n = max(pm == ~0ull ? 64 : __builtin_ctzll(~pm), 1);
+  const int len = p.cache_len[s];
+  const long long cap = (long long)p.max_pages * p.page_size;
+  int pg = -1;
+  int32_t flag = 0;
+  if (r < n) {
+    const long long pos = (long long)len + r;
+    if (len < 0 || pos >= cap) {
+      flag = MARS_STATUS_CACHE_OVERFLOW;
+    } else {
+      pg = p.block_table[(size_t)s * p.max_pages + (int)(pos / p.page_size)];
+      if (pg < 0 || pg >= p.num_pages) flag = MARS_STATUS_BAD_PAGE;
     }
   }
-  __syncthreads();
-  const int len = sh_len, nc = sh_nc;
-  const int rowbytes = p.D * ES;   // one head's row
-  const int chunks = rowbytes / 16;
+  const uint64_t gm = __ballot(r < n && flag == 0);
+  const int nc = gm == ~0ull ? 64 : __builtin_ctzll(~gm);  // rows placed
+  if (r == nc && r < n) status_or(p.status, flag);          // the first failure
+  if (r < p.B) {
+    p.accepted_ids[(size_t)s * p.B + r] = r < n ? p.top_id[(size_t)s * p.B + r] : -1;
+    p.commit_pos[(size_t)s * p.B + r] = r < nc ? len + r : -1;
+  }
+  if (r == 0) p.n_accepted[s] = n;
+  *len_out = len;
+  *pg_out = pg;
+  return nc;
+}
 
-  // K: [page][head][slot][d], 16-byte chunks
+constexpr int kCommitStageBytes = 16384;  // LDS staging of V rows in the commit
+
+// Copies rows 0 .. nc-1 of sequence s of one layer (the rows' pages in
+// page[r], positions len + r) into that layer's caches; every thread of the
+// 256-thread workgroup takes part. K rows go as 16-byte vectors into the
+// [page][head][slot][d] pages, head-major so that the rows of one head land
+// on consecutive slots. V rows: the (head, row) pairs are staged in LDS
+// (head-major, with 16-byte loads: a row is contiguous in v_new), then
+// written to the transposed [page][head][d][slot] pages one element per
+// thread, row fastest, so that neighbouring lanes store neighbouring slots.
+// Rows too long for the staging buffer take the element path directly.
+template <int ES>  // element size in bytes (2 = bf16, 4 = fp32)
+__device__ __forceinline__ void copy_rows(const CommitArgs& p, int layer, int s, int len, int nc,
+                                          const int* page, char* vst) {
+  const int tid = threadIdx.x;
+  const int rowbytes = p.D * ES;  // one head's row
+  const int chunks = rowbytes / 16;
+  const size_t new_off = (size_t)layer * p.S * p.B * p.Hkv * rowbytes;
+  const size_t cache_off = (size_t)layer * p.num_pages * p.Hkv * p.page_size * rowbytes;
+  const char* k_new = p.k_new + new_off;
+  const char* v_new = p.v_new + new_off;
+  char* k_cache = p.k_cache + cache_off;
+  char* v_cache = p.v_cache + cache_off;
+
   for (int idx = tid; idx < nc * p.Hkv * chunks; idx += 256) {
     const int ch = idx % chunks;
-    const int kvh = (idx / chunks) % p.Hkv;
-    const int r = idx / (chunks * p.Hkv);
+    const int r = (idx / chunks) % nc;
+    const int kvh = idx / (chunks * nc);
     const int pos = len + r;
     const size_t src = (((size_t)s * p.B + r) * p.Hkv + kvh) * rowbytes + ch * 16;
     const size_t dst =
-        (((size_t)sh_page[r] * p.Hkv + kvh) * p.page_size + pos % p.page_size) * rowbytes +
-        ch * 16;
-    *(u32x4*)(p.k_cache + dst) = *(const u32x4*)(p.k_new + src);
+        (((size_t)page[r] * p.Hkv + kvh) * p.page_size + pos % p.page_size) * rowbytes + ch * 16;
+    *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_new + src);
   }
-  // V: [page][head][d][slot]. With several rows, the accepted rows of one head
-  // are staged in LDS with 16-byte loads (a row is contiguous in v_new), then
-  // written one element per thread, slot fastest, so that neighbouring lanes
-  // store neighbouring slots. A single row (its loads already contiguous
-  // across lanes) and rows too long for the staging buffer take the element
-  // path directly.
   const int vrs = rowbytes + 4;  // padded LDS row stride
+  const int rows = nc * p.Hkv;   // staged (head, row) pairs, j = head * nc + row
   if (nc > 1 && vrs <= kCommitStageBytes) {
-    const int G = kCommitStageBytes / vrs;  // rows per pass
-    for (int kvh = 0; kvh < p.Hkv; ++kvh) {
-      for (int r0 = 0; r0 < nc; r0 += G) {
-        const int g = min(G, nc - r0);
-        for (int idx = tid; idx < g * chunks; idx += 256) {
-          const int ch = idx % chunks;
-          const int r = idx / chunks;
-          const u32x4 x = *(const u32x4*)(p.v_new + (((size_t)s * p.B + r0 + r) * p.Hkv + kvh) *
-                                                        rowbytes + ch * 16);
-          uint32_t* d4 = (uint32_t*)(vst + r * vrs + ch * 16);
-          d4[0] = x[0];
-          d4[1] = x[1];
-          d4[2] = x[2];
-          d4[3] = x[3];
-        }
-        __syncthreads();
-        for (int idx = tid; idx < g * p.D; idx += 256) {
-          const int r = idx % g;
-          const int d = idx / g;
-          const int pos = len + r0 + r;
-          const size_t dst = ((((size_t)sh_page[r0 + r] * p.Hkv + kvh) * p.D + d) * p.page_size +
-                              pos % p.page_size) * ES;
-          if (ES == 2)
-            *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(vst + r * vrs + d * 2);
-          else
-            *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(vst + r * vrs + d * 4);
-        }
-        __syncthreads();
+    const int G = kCommitStageBytes / vrs;  // pairs per pass
+    for (int j0 = 0; j0 < rows; j0 += G) {
+      const int g = min(G, rows - j0);
+      for (int idx = tid; idx < g * chunks; idx += 256) {
+        const int ch = idx % chunks;
+        const int j = j0 + idx / chunks;
+        const int r = j % nc, kvh = j / nc;
+        const u32x4 x =
+            *(const u32x4*)(v_new + (((size_t)s * p.B + r) * p.Hkv + kvh) * rowbytes + ch * 16);
+        uint32_t* d4 = (uint32_t*)(vst + (j - j0) * vrs + ch * 16);
+        d4[0] = x[0];
+        d4[1] = x[1];
+        d4[2] = x[2];
+        d4[3] = x[3];
       }
+      __syncthreads();
+      for (int idx = tid; idx < g * p.D; idx += 256) {
+        const int jj = idx % g;
+        const int d = idx / g;
+        const int j = j0 + jj;
+        const int r = j % nc, kvh = j / nc;
+        const int pos = len + r;
+        const size_t dst =
+            ((((size_t)page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
+        if (ES == 2)
+          *(uint16_t*)(v_cache + dst) = *(const uint16_t*)(vst + jj * vrs + d * 2);
+        else
+          *(uint32_t*)(v_cache + dst) = *(const uint32_t*)(vst + jj * vrs + d * 4);
+      }
+      __syncthreads();
     }
   } else {
     for (int idx = tid; idx < nc * p.Hkv * p.D; idx += 256) {
@@ -154,15 +161,86 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
       const int pos = len + r;
       const size_t src = ((((size_t)s * p.B + r) * p.Hkv + kvh) * p.D + d) * ES;
       const size_t dst =
-          ((((size_t)sh_page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
+          ((((size_t)page[r] * p.Hkv + kvh) * p.D + d) * p.page_size + pos % p.page_size) * ES;
       if (ES == 2)
-        *(uint16_t*)(p.v_cache + dst) = *(const uint16_t*)(p.v_new + src);
+        *(uint16_t*)(v_cache + dst) = *(const uint16_t*)(v_new + src);
       else
-        *(uint32_t*)(p.v_cache + dst) = *(const uint32_t*)(p.v_new + src);
+        *(uint32_t*)(v_cache + dst) = *(const uint32_t*)(v_new + src);
     }
     __syncthreads();
   }
+}
+
+// One layer: one workgroup per sequence. Wave 0 decides (see decide), then
+// the whole workgroup copies the accepted rows and thread 0 advances
+// cache_len.
+template <int ES>
+__global__ __launch_bounds__(256) void accept_commit_kernel(CommitArgs p) {
+  __shared__ int sh_page[kMaxB];
+  __shared__ int sh_len, sh_nc;
+  __shared__ __attribute__((aligned(16))) char vst[kCommitStageBytes];
+  const int s = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    int len, pg;
+    const int nc = decide(p, s, tid, &len, &pg);
+    if (tid < nc) sh_page[tid] = pg;
+    if (tid == 0) {
+      sh_len = len;
+      sh_nc = nc;
+    }
+  }
+  __syncthreads();
+  const int len = sh_len, nc = sh_nc;
+  copy_rows<ES>(p, 0, s, len, nc, sh_page, vst);
   if (tid == 0) p.cache_len[s] = len + nc;
+}
+
+// Several layers, first launch: the decision of 4 sequences per workgroup,
+// one wave each; each wave also advances its sequence's cache_len (the copy
+// that follows reads the positions from commit_pos, not from cache_len).
+__global__ __launch_bounds__(256) void accept_decide_kernel(CommitArgs p) {
+  const int s = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int r = threadIdx.x & 63;
+  if (s >= p.S) return;  // wave-uniform
+  int len, pg;
+  const int nc = decide(p, s, r, &len, &pg);
+  if (r == 0) p.cache_len[s] = len + nc;
+}
+
+// Several layers, second launch: workgroup (s, layer) copies the committed
+// rows of sequence s of that layer. The rows are the leading run of
+// commit_pos[s, r] == commit_pos[s, 0] + r; each row's page is looked up
+// again (and a row whose page is out of range ends the run, which the
+// decision already excluded).
+template <int ES>
+__global__ __launch_bounds__(256) void commit_layers_kernel(CommitArgs p) {
+  __shared__ int sh_page[kMaxB];
+  __shared__ int sh_len, sh_nc;
+  __shared__ __attribute__((aligned(16))) char vst[kCommitStageBytes];
+  const int s = blockIdx.x, layer = blockIdx.y, tid = threadIdx.x;
+  if (tid < 64) {
+    const int r = tid;
+    const int len = p.commit_pos[(size_t)s * p.B];
+    const long long cap = (long long)p.max_pages * p.page_size;
+    bool ok = false;
+    int pg = -1;
+    if (r < p.B && len >= 0) {
+      const int pos = p.commit_pos[(size_t)s * p.B + r];
+      if (pos == len + r && (long long)pos < cap) {
+        pg = p.block_table[(size_t)s * p.max_pages + pos / p.page_size];
+        ok = pg >= 0 && pg < p.num_pages;
+      }
+    }
+    const uint64_t m = __ballot(ok);
+    const int nc = m == ~0ull ? 64 : __builtin_ctzll(~m);
+    if (r < nc) sh_page[r] = pg;
+    if (r == 0) {
+      sh_len = len;
+      sh_nc = nc;
+    }
+  }
+  __syncthreads();
+  copy_rows<ES>(p, layer, s, sh_len, sh_nc, sh_page, vst);
 }
 
 // ---------------------------------------------------------------- append ----
@@ -329,19 +407,21 @@ __global__ __launch_bounds__(256) void kv_append_len_kernel(AppendArgs p) {
 
 }  // namespace
 
-extern "C" int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* tau,
-                                  const void* k_new, const void* v_new, void* k_cache,
-                                  void* v_cache, const int32_t* block_table, int32_t* cache_len,
-                                  int32_t* n_accepted, int32_t* accepted_ids,
-                                  int32_t* commit_pos, int32_t S, int32_t B, int32_t n_kv_heads,
-                                  int32_t head_dim, int32_t page_size, int32_t max_pages,
-                                  int32_t num_pages, int32_t dtype, int32_t* status,
-                                  void* stream) {
+namespace {
+// Checks shared by the one-layer and the layered commit, then the kernel
+// arguments.
+int commit_args(const float* p_max, const int32_t* top_id, const float* tau, const void* k_new,
+                const void* v_new, void* k_cache, void* v_cache, const int32_t* block_table,
+                int32_t* cache_len, int32_t* n_accepted, int32_t* accepted_ids,
+                int32_t* commit_pos, int32_t layers, int32_t S, int32_t B, int32_t n_kv_heads,
+                int32_t head_dim, int32_t page_size, int32_t max_pages, int32_t num_pages,
+                int32_t dtype, int32_t* status, CommitArgs* a) {
   MARS_REQUIRE(p_max && top_id && tau && k_new && v_new && k_cache && v_cache && block_table &&
                    cache_len && n_accepted && accepted_ids && commit_pos,
                MARS_ERR_NULL);
   MARS_REQUIRE(dtype == MARS_F32 || dtype == MARS_BF16, MARS_ERR_DTYPE);
   MARS_REQUIRE(S >= 1 && S <= (1 << 30) && B >= 1 && B <= kMaxB, MARS_ERR_SHAPE);
+  MARS_REQUIRE(layers >= 1 && layers <= 65535, MARS_ERR_SHAPE);
   MARS_REQUIRE(n_kv_heads >= 1 && head_dim >= 8 && head_dim % 8 == 0, MARS_ERR_SHAPE);
   MARS_REQUIRE(page_size >= 1 && max_pages >= 1 && num_pages >= 1, MARS_ERR_SHAPE);
   MARS_REQUIRE((long long)max_pages * page_size <= (1LL << 30), MARS_ERR_SHAPE);
@@ -351,32 +431,76 @@ extern "C" int mars_accept_commit(const float* p_max, const int32_t* top_id, con
                    mars_aligned16(cache_len) && mars_aligned16(n_accepted) &&
                    mars_aligned16(accepted_ids) && mars_aligned16(commit_pos),
                MARS_ERR_ALIGN);
+  a->p_max = p_max;
+  a->top_id = top_id;
+  a->tau = tau;
+  a->k_new = (const char*)k_new;
+  a->v_new = (const char*)v_new;
+  a->k_cache = (char*)k_cache;
+  a->v_cache = (char*)v_cache;
+  a->block_table = block_table;
+  a->cache_len = cache_len;
+  a->n_accepted = n_accepted;
+  a->accepted_ids = accepted_ids;
+  a->commit_pos = commit_pos;
+  a->status = status;
+  a->S = S;
+  a->B = B;
+  a->Hkv = n_kv_heads;
+  a->D = head_dim;
+  a->page_size = page_size;
+  a->max_pages = max_pages;
+  a->num_pages = num_pages;
+  a->layers = layers;
+  return MARS_OK;
+}
+}  // namespace
+
+extern "C" int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* tau,
+                                  const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const int32_t* block_table, int32_t* cache_len,
+                                  int32_t* n_accepted, int32_t* accepted_ids,
+                                  int32_t* commit_pos, int32_t S, int32_t B, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t page_size, int32_t max_pages,
+                                  int32_t num_pages, int32_t dtype, int32_t* status,
+                                  void* stream) {
   CommitArgs a;
-  a.p_max = p_max;
-  a.top_id = top_id;
-  a.tau = tau;
-  a.k_new = (const char*)k_new;
-  a.v_new = (const char*)v_new;
-  a.k_cache = (char*)k_cache;
-  a.v_cache = (char*)v_cache;
-  a.block_table = block_table;
-  a.cache_len = cache_len;
-  a.n_accepted = n_accepted;
-  a.accepted_ids = accepted_ids;
-  a.commit_pos = commit_pos;
-  a.status = status;
-  a.S = S;
-  a.B = B;
-  a.Hkv = n_kv_heads;
-  a.D = head_dim;
-  a.page_size = page_size;
-  a.max_pages = max_pages;
-  a.num_pages = num_pages;
+  const int rc = commit_args(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
+                             cache_len, n_accepted, accepted_ids, commit_pos, 1, S, B,
+                             n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype, status,
+                             &a);
+  if (rc != MARS_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == MARS_BF16)
     hipLaunchKernelGGL(accept_commit_kernel<2>, dim3(S), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(accept_commit_kernel<4>, dim3(S), dim3(256), 0, st, a);
+  return mars_launch_status();
+}
+
+extern "C" int mars_accept_commit_layers(const float* p_max, const int32_t* top_id,
+                                         const float* tau, const void* k_new, const void* v_new,
+                                         void* k_cache, void* v_cache,
+                                         const int32_t* block_table, int32_t* cache_len,
+                                         int32_t* n_accepted, int32_t* accepted_ids,
+                                         int32_t* commit_pos, int32_t n_layers, int32_t S,
+                                         int32_t B, int32_t n_kv_heads, int32_t head_dim,
+                                         int32_t page_size, int32_t max_pages,
+                                         int32_t num_pages, int32_t dtype, int32_t* status,
+                                         void* stream) {
+  CommitArgs a;
+  const int rc = commit_args(p_max, top_id, tau, k_new, v_new, k_cache, v_cache, block_table,
+                             cache_len, n_accepted, accepted_ids, commit_pos, n_layers, S, B,
+                             n_kv_heads, head_dim, page_size, max_pages, num_pages, dtype, status,
+                             &a);
+  if (rc != MARS_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(accept_decide_kernel, dim3((S + 3) / 4), dim3(256), 0, st, a);
+  const dim3 grid(S, n_layers);
+  if (dtype == MARS_BF16)
+    hipLaunchKernelGGL(commit_layers_kernel<2>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(commit_layers_kernel<4>, grid, dim3(256), 0, st, a);
   return mars_launch_status();
 }
 

@@ -56,7 +56,7 @@ SOURCES = {
     "two_stream_backward_0.5b": _BWD,
     "two_stream_backward_7b": _BWD,
     "kv_append": _AC,
-    "kv_commit_layers": _AC,
+    "commit_layers": _AC,
 }
 COPY_KERNEL = "copyBuffer"
 MARKER = "FillFunctor<long>"

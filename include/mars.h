@@ -18,6 +18,7 @@
  *   mars_lmhead_confidence_packed  the same on weights packed by mars_lmhead_pack
  *   mars_lmhead_confidence_noalloc the same with no workspace argument
  *   mars_accept_commit      left-to-right acceptance + KV commit of the prefix
+ *   mars_accept_commit_layers  the same, committing into every layer's cache
  *   mars_kv_append          paged KV append of a prompt
  *   mars_block_sync_accept  acceptance under the batch-synchronous block cache
  *   mars_block_freeze       freezes a full block into the paged cache
@@ -397,6 +398,30 @@ int mars_accept_commit(const float* p_max, const int32_t* top_id, const float* t
                        int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
                        int32_t max_pages, int32_t num_pages, int32_t dtype, int32_t* status,
                        void* stream);
+
+/*
+ * The same acceptance, then the commit into every layer's cache at once (the
+ * accepted tokens join each layer's prefix cache: notes, key design 4
+ * (关键设计 4); a model keeps one KV cache per decoder layer).
+ *
+ * The decision, n_accepted, accepted_ids, commit_pos, cache_len and status are
+ * exactly those of mars_accept_commit (taken once; one block table and one
+ * length per sequence serve every layer). k_new, v_new
+ * [n_layers, S, B, n_kv_heads, head_dim]; k_cache [n_layers, pages, Hkv, page,
+ * d], v_cache [n_layers, pages, Hkv, d, page]: layer l of each is laid out as
+ * in mars_accept_commit, and rows r < n of layer l of k_new/v_new go to layer
+ * l of the caches. Two launches on `stream`: the decision (which advances
+ * cache_len and writes commit_pos), then one workgroup per (sequence, layer)
+ * that copies the rows commit_pos names. Limits as mars_accept_commit, and
+ * 1 <= n_layers <= 65535.
+ */
+int mars_accept_commit_layers(const float* p_max, const int32_t* top_id, const float* tau,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_table, int32_t* cache_len,
+                              int32_t* n_accepted, int32_t* accepted_ids, int32_t* commit_pos,
+                              int32_t n_layers, int32_t S, int32_t B, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t max_pages,
+                              int32_t num_pages, int32_t dtype, int32_t* status, void* stream);
 
 /* Human-readable text for a MARS_* return code. */
 const char* mars_strerror(int code);

@@ -18,6 +18,8 @@ from .generators import (  # noqa: F401
     two_stream_qkv,
     sequence_qkv,
     decode_inputs,
+    layered_commit_inputs,
+    LayeredCommitInputs,
     lmhead_inputs,
     normal_logits,
     PeakedLogitsPool,

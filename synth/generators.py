@@ -11,7 +11,8 @@ Layouts (row-major, C order):
   two-stream K, V   [batch, 2L, n_kv_heads, head_dim]
   decode q          [S, B, n_q_heads, head_dim]
   decode k_new/v_new[S, B, n_kv_heads, head_dim]
-  K cache pages     [num_pages, n_kv_heads, page_size, head_dim]
+  K cache pages     [num_pages, n_kv_heads, page_size, head_dim] (one more
+                    leading layers dim in layered_commit_inputs)
   V cache pages     [num_pages, n_kv_heads, head_dim, page_size]  (V is stored
                     transposed inside each page)
   block_table       [S, max_pages] int32, page ids of each sequence's pages
@@ -139,6 +140,43 @@ def decode_inputs(seed: int, S: int, B: int, n_q_heads: int, n_kv_heads: int,
     q, kn, vn = decode_step_tensors(seed, 0, S, B, n_q_heads, n_kv_heads, head_dim, dtype)
     return DecodeInputs(q, kn, vn, k_cache, v_cache, block_table, cache_len,
                         page_size, max_pages, num_pages)
+
+
+@dataclass
+class LayeredCommitInputs:
+    k_new: Tensor        # [layers, S, B, n_kv_heads, head_dim]
+    v_new: Tensor
+    k_cache: Tensor      # [layers, num_pages, n_kv_heads, page_size, head_dim]
+    v_cache: Tensor      # [layers, num_pages, n_kv_heads, head_dim, page_size]
+    block_table: np.ndarray
+    cache_len: np.ndarray
+    page_size: int
+    max_pages: int
+    num_pages: int
+
+
+def layered_commit_inputs(seed: int, layers: int, S: int, B: int, n_kv_heads: int,
+                          head_dim: int, len_lo: int, len_hi: int, page_size: int,
+                          extra_capacity: int = 0, dtype: str = "bf16") -> LayeredCommitInputs:
+    """One paged KV cache per layer sharing one block table and one length per sequence.
+
+    Lengths ~ U{len_lo..len_hi}; each sequence owns ceil((len_hi + extra_capacity)
+    / page_size) pages whose ids are a seeded permutation; cache slots and the new
+    rows of every layer hold N(0, 1) values.
+    """
+    rng = np.random.default_rng([seed, 104729])
+    cache_len = rng.integers(len_lo, len_hi + 1, size=S).astype(np.int32)
+    max_pages = max(1, -(-(len_hi + extra_capacity) // page_size))
+    num_pages = S * max_pages
+    block_table = rng.permutation(num_pages).astype(np.int32).reshape(S, max_pages)
+    shape = (layers, num_pages, n_kv_heads, page_size, head_dim)
+    k_cache = _make(_normal(rng, shape), dtype)
+    v_cache = _make(np.ascontiguousarray(_normal(rng, shape).transpose(0, 1, 2, 4, 3)), dtype)
+    rows = (layers, S, B, n_kv_heads, head_dim)
+    k_new = _make(_normal(rng, rows), dtype)
+    v_new = _make(_normal(rng, rows), dtype)
+    return LayeredCommitInputs(k_new, v_new, k_cache, v_cache, block_table, cache_len,
+                               page_size, max_pages, num_pages)
 
 
 def lmhead_inputs(seed: int, N: int, D: int, V: int, w_std: float = 0.02):

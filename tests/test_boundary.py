@@ -223,6 +223,20 @@ def test_accept_commit_argument_checks():
     assert ac(kc=MIS) == _lib.MARS_ERR_ALIGN
 
 
+def acl(layers=2, S=4, B=4, kc=FAKE):
+    return mars.lib().mars_accept_commit_layers(FAKE, FAKE, FAKE, FAKE, FAKE, kc, FAKE, FAKE,
+                                                FAKE, FAKE, FAKE, FAKE, layers, S, B, 2, 32, 16,
+                                                4, 16, 1, None, None)
+
+
+def test_layered_commit_argument_checks():
+    assert acl(layers=0) == _lib.MARS_ERR_SHAPE
+    assert acl(layers=65536) == _lib.MARS_ERR_SHAPE
+    assert acl(B=65) == _lib.MARS_ERR_SHAPE
+    assert acl(kc=MIS) == _lib.MARS_ERR_ALIGN
+    assert acl(kc=None) == _lib.MARS_ERR_NULL
+
+
 def test_binding_rejects_cpu_tensors_before_calling():
     import torch
     q = torch.zeros(1, 8, 2, 32)
@@ -393,3 +407,32 @@ def test_oracle_is_not_imported_by_the_package():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg_dir, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_binding_checks_every_shape_of_the_layered_commit():
+    import torch
+    S, B, Hkv, d, L = 2, 4, 2, 64, 3
+    base = dict(p_max=_cpu((S, B), torch.float32), top_id=_cpu((S, B), torch.int32),
+                tau=_cpu((S,), torch.float32), k_new=_cpu((L, S, B, Hkv, d)),
+                v_new=_cpu((L, S, B, Hkv, d)), k_cache=_cpu((L, 6, Hkv, 16, d)),
+                v_cache=_cpu((L, 6, Hkv, d, 16)), block_table=_cpu((S, 3), torch.int32),
+                cache_len=_cpu((S,), torch.int32))
+    names = list(base)
+
+    def call(**kw):
+        args = {**base, **kw}
+        outs = {k: v for k, v in kw.items() if k in ("n_accepted", "accepted_ids",
+                                                      "commit_pos", "status")}
+        return mars.mars_accept_commit_layers(*[args[n] for n in names], **outs)
+
+    _gpu_error(call)
+    _shape_error(call, match="k_new must have 5 dims", k_new=_cpu((S, B, Hkv, d)))
+    _shape_error(call, match="v_new must have shape", v_new=_cpu((L - 1, S, B, Hkv, d)))
+    _shape_error(call, match="k_cache must hold 3 layers", k_cache=_cpu((2, 6, Hkv, 16, d)))
+    _shape_error(call, match="v_cache must hold 3 layers", v_cache=_cpu((2, 6, Hkv, d, 16)))
+    _shape_error(call, match="v_cache must have shape", v_cache=_cpu((L, 6, Hkv, 16, d)))
+    _shape_error(call, match="k_cache must be", k_cache=_cpu((L, 6, 1, 16, d)))
+    _shape_error(call, match="block_table must have 2 rows",
+                 block_table=_cpu((1, 3), torch.int32))
+    _shape_error(call, match="commit_pos must have shape",
+                 commit_pos=_cpu((S, 1), torch.int32))

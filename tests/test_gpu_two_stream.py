@@ -68,6 +68,15 @@ def test_fp32_matches_oracle(b, L, B, Hq, Hkv, d):
     # both ragged (2L not a multiple of the 128-row workgroup tile)
     (2, 84, 4, 28, 4, 128, 0),
     (1, 100, 4, 7, 1, 128, 0),
+    # d = 128 workgroups that pair clean tile i with mask tile i (L a multiple of
+    # 128): blocks larger than a tile, blocks that do not divide 128, a single
+    # pair, B = L (mask rows see no clean key); causal over 2L with few tiles
+    (1, 512, 200, 2, 1, 128, 0),
+    (1, 384, 24, 4, 2, 128, 0),
+    (1, 128, 4, 7, 1, 128, 0),
+    (1, 128, 128, 2, 1, 128, 0),
+    (1, 3, 2, 2, 1, 128, 1),
+    (2, 300, 4, 4, 2, 128, 1),
 ])
 def test_bf16_matches_oracle(b, L, B, Hq, Hkv, d, mode):
     eo, el, _ = run_case(2000 + L, b, L, B, Hq, Hkv, d, "bf16", mode=mode)
