@@ -15,32 +15,33 @@
 //   * O^T = V^T P^T: the V pages are stored transposed ([d][slot]), so the A
 //     operand of lane (dim, hf) is one 16-byte read of 8 consecutive slots
 //     (the probabilities are regrouped between the wave halves to match).
-// The cache of one sequence is cut into 512-key chunks (split-K). Each
-// workgroup handles one (chunk, KV head, sequence) and writes an unnormalised
-// partial (O, running max, running sum); a merge kernel combines the chunks. A sequence that fits in one chunk is written out directly.
-// Chunk 0 also handles the new rows (causal among themselves). Their number
-// may differ per sequence (at most 64): under the batch-synchronous block
-// cache (notes, key design 4) a sequence's new rows are its tokens accepted
-// since the last frozen block followed by the B masks. Packed rows beyond
-// kMaxQT query tiles go to further workgroups of the same (chunk, KV head,
-// sequence), which read the same K/V.
+// The cache of one sequence is cut into chunks (split-K). Each workgroup
+// handles one (chunk, KV head, sequence); when the packed rows fill fewer than
+// 4 query tiles, the spare waves of the workgroup split the chunk's keys (4
+// waves per tile with one tile, 2 with two), each streaming 256 keys, and
+// combine their (max, sum, O) through LDS in a fixed order. The workgroup
+// writes an unnormalised partial (O, running max, running sum) per chunk; a
+// merge kernel combines the chunks, and a sequence that fits in one chunk is
+// written out directly.
+// Chunk 0 also handles the new rows (causal among themselves); the workgroup
+// stages their V rows transposed in LDS. Their number may differ per sequence
+// (at most 64): under the batch-synchronous block cache (notes, key design 4)
+// a sequence's new rows are its tokens accepted since the last frozen block
+// followed by the B masks. Packed rows beyond kMaxQT query tiles go to further
+// workgroups of the same (chunk, KV head, sequence), which read the same K/V.
 #include "mars_common.hpp"
 
 using namespace mars;
 
 namespace {
 
-// Split-K chunk (cache keys per workgroup). 512 keys measured fastest both for
-// 64 sequences x 4 KV heads (where 256-key chunks give more workgroups but twice
-// the partials to write and merge) and for 256 x 4; a chunk's page ids must fit
-// one per lane (<= 64 pages of >= 16 keys).
-inline int decode_chunk(int S, int Hkv, int nqt) {
-  (void)S;
-  (void)Hkv;
-  (void)nqt;
-  return 512;
-}
 constexpr int kMaxQT = 4;    // query tiles of 32 packed rows per workgroup
+// Waves that share one query tile and split its chunk's keys: a workgroup has
+// at most 4 waves, so 1 tile -> 4 key parts, 2 tiles -> 2, 3 or 4 tiles -> 1.
+inline int key_split(int nqt) {
+  const int t = nqt < kMaxQT ? nqt : kMaxQT;
+  return t == 1 ? 4 : t == 2 ? 2 : 1;
+}
 constexpr int kMaxRows = 64; // new rows per sequence
 
 struct DecodeArgs {
@@ -144,30 +145,58 @@ __device__ __forceinline__ void dec_step(const bf16x8 (&ka)[D / 16], const bf16x
   dec_pv<D>(va, pb, o);
 }
 
-// Keeps the first n (0..8) bf16 values of an 8-key V group, zeroes the rest.
+// Keeps the first n (0..8) bf16 values of an 8-key V group, zeroes the rest
+// (word masks: element 2w + 1 is the high half of word w).
 __device__ __forceinline__ bf16x8 keep_first(bf16x8 v, int n) {
+  u32x4 w = __builtin_bit_cast(u32x4, v);
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (e >= n) v[e] = (bf16_t)0.f;
-  return v;
+  for (int k = 0; k < 4; ++k)
+    w[k] &= n >= 2 * k + 2 ? 0xFFFFFFFFu : n == 2 * k + 1 ? 0x0000FFFFu : 0u;
+  return __builtin_bit_cast(bf16x8, w);
 }
 
-// PS = the page size when it is a compile-time constant (16 or 32, the block
-// granularities the method uses), or 0 for any other multiple of 16.
 __device__ __forceinline__ int rows_of(const DecodeArgs& p, int s) {
   return p.n_rows ? min(max(p.n_rows[s], 0), p.B) : p.B;
 }
 
-template <int D, int PS>
+// Keys of the cache one wave streams; a chunk is kKeysPerWave x KS keys.
+constexpr int kKeysPerWave = 256;
+// V rows of the new keys (at most kMaxRows) staged transposed in LDS:
+// [head_dim][kNewStride] bf16; a row of 144 bytes keeps 16-byte reads aligned.
+constexpr int kNewStride = 72;
+
+// Bytes of dynamic LDS of one split workgroup: per wave its query tile (D x 64
+// bytes), and the staged V^T of the new rows; the combine of the KS waves of a
+// tile reuses that space once the waves are done with it.
+__host__ __device__ constexpr size_t split_lds_bytes(int D, int tiles, int KS) {
+  const size_t qv = (size_t)tiles * KS * D * 64 + (size_t)D * kNewStride * 2;
+  const size_t comb = (size_t)(KS == 4 ? 2 : KS == 2 ? 1 : 0) * tiles * (D / 32 * 16 + 2) * 64 * 4;
+  return qv > comb ? qv : comb;
+}
+
+// Split-K chunk (cache keys per workgroup): each of the key_split(nqt) waves
+// of a query tile streams kKeysPerWave keys of it. The chunk's page ids are
+// held one per lane (<= 64 pages of >= 16 keys: chunks of at most 1024 keys).
+inline int decode_chunk(int nqt) { return kKeysPerWave * key_split(nqt); }
+
+// PS = the page size when it is a compile-time constant (16 or 32, the block
+// granularities the method uses), or 0 for any other multiple of 16.
+// KS = waves that share one query tile and split its chunk's keys between
+// them (1, 2 or 4); a workgroup holds `tiles` query tiles x KS waves.
+template <int D, int PS, int KS>
 __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs p) {
   const int split = blockIdx.x, s = blockIdx.z;
   const int kvh = blockIdx.y / p.qgroups, qg = blockIdx.y % p.qgroups;
-  const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tiles = (int)blockDim.x / (64 * KS);
+  const int wq = w % tiles, kp = w / tiles;  // query tile, key part
   const int j = lane & 31, hf = lane >> 5;
   const int rs = rows_of(p, s);  // new rows of this sequence
   const int nrows = p.group * rs;
   const int tq = qg * kMaxQT + wq;  // this wave's query tile
-  if (tq * 32 >= nrows) return;  // wave-uniform: no barriers in this kernel
+  // a tile without rows (a sequence with fewer new rows) skips the work but
+  // still takes part in the workgroup's barriers
+  const bool tile_live = tq * 32 < nrows;
 
   int len = p.cache_len[s];
   const int cap = p.max_pages * p.page_size;
@@ -177,143 +206,211 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   }
   if (len < 0) len = 0;
   const int k_lo = split * p.chunk;
-  if (split > 0 && k_lo >= len) return;
+  if (split > 0 && k_lo >= len) return;  // workgroup-uniform
   const int k_hi = min(len, k_lo + p.chunk);
   const bool single = len <= p.chunk;  // the only chunk: write the final output
+  // this wave's share of the chunk
+  const int w_lo = min(k_lo + kp * kKeysPerWave, k_hi);
+  const int w_hi = min(w_lo + kKeysPerWave, k_hi);
 
   // Packed query row of this lane: j' = r * g + head_in_group.
   const int qi = tq * 32 + j;
   const bool qvalid = qi < nrows;
   const int qr = qvalid ? qi / p.group : 0;
   const int qh = kvh * p.group + (qvalid ? qi % p.group : 0);
-  extern __shared__ bf16x8 qsh[];  // [waves][D / 16][64]
-  bf16x8* qlds = qsh + (size_t)wq * (D / 16) * 64 + lane;
-  {
-    const bf16_t* qrow = p.q + (((size_t)s * p.B + qr) * p.Hq + qh) * D + 8 * hf;
+  extern __shared__ bf16x8 qsh[];  // [waves][D / 16][64], then V^T of the new rows
+  bf16x8* qlds = qsh + (size_t)w * (D / 16) * 64 + lane;
+  bf16_t* vnew = (bf16_t*)(qsh + (size_t)tiles * KS * (D / 16) * 64);
+  if (split == 0) {
+    // Chunk 0 also attends to the new rows: the workgroup stages their V rows
+    // transposed ([d][key], keys rounded up to a multiple of 32, zero past
+    // rs), so that the V^T operand of 8 consecutive keys is one 16-byte read.
+    const int keys = (rs + 31) & ~31;
+    for (int idx = threadIdx.x; idx < keys * (D / 8); idx += blockDim.x) {
+      const int t = idx / (D / 8), c = idx % (D / 8);
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (t < rs)
+        x = *(const u32x4*)(p.v_new + (((size_t)s * p.B + t) * p.Hkv + kvh) * D + 8 * c);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qlds[64 * c] = qvalid ? *(const bf16x8*)(qrow + 16 * c) : bf16x8{};
+      for (int e = 0; e < 8; ++e)
+        *(uint16_t*)(vnew + (size_t)(8 * c + e) * kNewStride + t) =
+            (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();  // workgroup-uniform (split == 0)
   }
-
-  // Page ids of this chunk, one per lane (lane t: page k_lo / ps + t); -1 = bad.
-  const int ps = PS > 0 ? PS : p.page_size;
-  const int pg0 = k_lo / ps;
-  const int npg = k_hi > k_lo ? (k_hi - 1) / ps - pg0 + 1 : 0;
-  int mypage = 0;
-  if (lane < npg) {
-    const int raw = p.block_table[(size_t)s * p.max_pages + pg0 + lane];
-    mypage = (raw >= 0 && raw < p.num_pages) ? raw : -1;
-  }
-  const bool chunk_bad = __ballot(mypage < 0) != 0;
-  if (chunk_bad && lane == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
-
-  const size_t kpage = (size_t)p.Hkv * ps * D;  // elements per page (all heads)
-  const bf16_t* kbase = p.k_cache + (size_t)kvh * ps * D;
-  const bf16_t* vbase = p.v_cache + (size_t)kvh * D * ps;
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // The step loop is rotated so that a wave always has loads in flight: the K
-  // rows of step s+1 are requested as soon as the score MFMAs of step s have
-  // consumed the K registers, and the V rows of step s+1 as soon as the PV
-  // MFMAs of step s have consumed the V registers.
-  bf16x8 ka[D / 16];
-  bf16x8 va[D / 32][2];
-  auto load_k = [&](int c0) {
-    const int pos = c0 + j;
-    const int pk = __shfl(mypage, pos / ps - pg0);
-    const bf16_t* kr = kbase + (size_t)max(pk, 0) * kpage + (size_t)(pos % ps) * D + 8 * hf;
+  if (tile_live) {
+    {
+      const bf16_t* qrow = p.q + (((size_t)s * p.B + qr) * p.Hq + qh) * D + 8 * hf;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
-  };
-  // V group of 8 keys starting at step offset 16kc + 8hf (one page: pages
-  // hold a multiple of 16 slots)
-  auto v_page = [&](int c0, int kc) {
-    return __shfl(mypage, (c0 + 16 * kc + 8 * hf) / ps - pg0);
-  };
-  auto load_v = [&](int c0) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int k0 = c0 + 16 * kc + 8 * hf;
-      const bf16_t* v0 = vbase + (size_t)max(v_page(c0, kc), 0) * kpage + (k0 % ps);
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-        va[i][kc] = *(const bf16x8*)(v0 + (size_t)(32 * i + j) * ps);
+      for (int c = 0; c < D / 16; ++c)
+        qlds[64 * c] = qvalid ? *(const bf16x8*)(qrow + 16 * c) : bf16x8{};
     }
-  };
-  // past the chunk end or on a bad page: zero V (stale slots may hold anything)
-  auto zero_v_tail = [&](int c0) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int k0 = c0 + 16 * kc + 8 * hf;
-      const int n0 = v_page(c0, kc) < 0 ? 0 : k_hi - k0;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) va[i][kc] = keep_first(va[i][kc], n0);
-    }
-  };
 
-  if (k_lo < k_hi) {
-    load_k(k_lo);
-    load_v(k_lo);
-  }
-  for (int c0 = k_lo; c0 < k_hi; c0 += 32) {
-    const bool full = c0 + 32 <= k_hi && !chunk_bad;
-    const bool more = c0 + 32 < k_hi;
-    f32x16 sc = dec_scores<D>(ka, qlds);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) load_k(c0 + 32);
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 pb[2];
-    if (full) {
-      dec_softmax<D, false>(sc, pb, o, m, l, p.scale_log2, 0u, hf);
-    } else {
+    // Page ids of this chunk, one per lane (lane t: page k_lo / ps + t); -1 = bad.
+    const int ps = PS > 0 ? PS : p.page_size;
+    const int pg0 = k_lo / ps;
+    const int npg = k_hi > k_lo ? (k_hi - 1) / ps - pg0 + 1 : 0;
+    int mypage = 0;
+    if (lane < npg) {
+      const int raw = p.block_table[(size_t)s * p.max_pages + pg0 + lane];
+      mypage = (raw >= 0 && raw < p.num_pages) ? raw : -1;
+    }
+    const bool chunk_bad = __ballot(mypage < 0) != 0;
+    if (chunk_bad && lane == 0 && kp == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
+
+    const size_t kpage = (size_t)p.Hkv * ps * D;  // elements per page (all heads)
+    const bf16_t* kbase = p.k_cache + (size_t)kvh * ps * D;
+    const bf16_t* vbase = p.v_cache + (size_t)kvh * D * ps;
+
+    // The step loop is rotated so that a wave always has loads in flight: the K
+    // rows of step s+1 are requested as soon as the score MFMAs of step s have
+    // consumed the K registers, and the V rows of step s+1 as soon as the PV
+    // MFMAs of step s have consumed the V registers.
+    bf16x8 ka[D / 16];
+    bf16x8 va[D / 32][2];
+    auto load_k = [&](int c0) {
+      const int pos = c0 + j;
+      const int pk = __shfl(mypage, pos / ps - pg0);
+      const bf16_t* kr = kbase + (size_t)max(pk, 0) * kpage + (size_t)(pos % ps) * D + 8 * hf;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) ka[c] = *(const bf16x8*)(kr + 16 * c);
+    };
+    // V group of 8 keys starting at step offset 16kc + 8hf (one page: pages
+    // hold a multiple of 16 slots)
+    auto v_page = [&](int c0, int kc) {
+      return __shfl(mypage, (c0 + 16 * kc + 8 * hf) / ps - pg0);
+    };
+    auto load_v = [&](int c0) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int k0 = c0 + 16 * kc + 8 * hf;
+        const bf16_t* v0 = vbase + (size_t)max(v_page(c0, kc), 0) * kpage + (k0 % ps);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+          va[i][kc] = *(const bf16x8*)(v0 + (size_t)(32 * i + j) * ps);
+      }
+    };
+    // A step that masks keys past the wave's end or on a bad page (their V
+    // slots are zeroed too: stale slots may hold anything); K and V loaded.
+    auto masked_step = [&](int c0) {
+      f32x16 sc = dec_scores<D>(ka, qlds);
       const int pos = c0 + j;
       const uint32_t live =
-          (uint32_t)__ballot(pos < k_hi && __shfl(mypage, pos / ps - pg0) >= 0);
+          (uint32_t)__ballot(pos < w_hi && __shfl(mypage, pos / ps - pg0) >= 0);
+      bf16x8 pb[2];
       dec_softmax<D, true>(sc, pb, o, m, l, p.scale_log2, live, hf);
-      zero_v_tail(c0);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int k0 = c0 + 16 * kc + 8 * hf;
+        const int n0 = v_page(c0, kc) < 0 ? 0 : w_hi - k0;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) va[i][kc] = keep_first(va[i][kc], n0);
+      }
+      dec_pv<D>(va, pb, o);
+    };
+    if (!chunk_bad) {
+      // whole 32-key steps, then at most one partial step: keeping the masked
+      // code out of the loop keeps its registers out of the loop's live set
+      const int w_full = w_lo + ((w_hi - w_lo) & ~31);
+      if (w_lo < w_hi) {
+        load_k(w_lo);
+        load_v(w_lo);
+      }
+      for (int c0 = w_lo; c0 < w_full; c0 += 32) {
+        const bool more = c0 + 32 < w_hi;
+        f32x16 sc = dec_scores<D>(ka, qlds);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_k(c0 + 32);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 pb[2];
+        dec_softmax<D, false>(sc, pb, o, m, l, p.scale_log2, 0u, hf);
+        dec_pv<D>(va, pb, o);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_v(c0 + 32);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (w_full < w_hi) masked_step(w_full);
+    } else {
+      for (int c0 = w_lo; c0 < w_hi; c0 += 32) {
+        load_k(c0);
+        load_v(c0);
+        masked_step(c0);
+      }
     }
-    dec_pv<D>(va, pb, o);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) load_v(c0 + 32);
-    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the new rows, causal among themselves (chunk 0, last key part) ----
+    if (split == 0 && kp == KS - 1) {
+      for (int n0 = 0; n0 < rs; n0 += 32) {
+        {
+          const bool kv = n0 + j < rs;
+          const bf16_t* kr =
+              p.k_new + (((size_t)s * p.B + (kv ? n0 + j : 0)) * p.Hkv + kvh) * D + 8 * hf;
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) ka[c] = kv ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
+        }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+            va[i][kc] = *(const bf16x8*)(vnew + (size_t)(32 * i + j) * kNewStride + n0 +
+                                         16 * kc + 8 * hf);
+        // new row n0 + t is visible to packed row j' iff n0 + t <= r(j'): a per-lane mask
+        const int vis = qr - n0 + 1;  // visible keys of this step
+        const uint32_t live = vis <= 0 ? 0u : vis >= 32 ? 0xFFFFFFFFu : ((1u << vis) - 1u);
+        dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
+      }
+    }
   }
 
-  // ---- the new rows, causal among themselves (chunk 0 only) ----------------
-  if (split == 0) {
-    for (int n0 = 0; n0 < rs; n0 += 32) {
-      bf16x8 ka[D / 16];
-      {
-        const bool kv = n0 + j < rs;
-        const bf16_t* kr =
-            p.k_new + (((size_t)s * p.B + (kv ? n0 + j : 0)) * p.Hkv + kvh) * D + 8 * hf;
+  // ---- the KS waves of a tile combine, in a fixed order -------------------
+  if constexpr (KS > 1) {
+    constexpr int kOF = D / 32 * 16 * 64;  // floats of one wave's O
+    float* cbuf = (float*)qsh;             // reuses the query and staging space
+    auto slot = [&](int k) { return cbuf + (size_t)(k * tiles + wq) * (kOF + 128); };
+    auto put = [&](float* b) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) ka[c] = kv ? *(const bf16x8*)(kr + 16 * c) : bf16x8{};
-      }
-      bf16x8 va[D / 32][2];
+      for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const int d = 32 * i + j;
+        for (int r = 0; r < 16; ++r) b[(i * 16 + r) * 64 + lane] = o[i][r];
+      b[kOF + lane] = m;
+      b[kOF + 64 + lane] = l;
+    };
+    // (m, l, O) of this wave and of the wave that wrote b, in that order
+    auto take = [&](const float* b) {
+      const float mb = b[kOF + lane], lb = b[kOF + 64 + lane];
+      const float M = fmaxf(m, mb);
+      const float sa = m == M ? 1.f : fast_exp2(m - M);
+      const float sb = mb == M ? 1.f : fast_exp2(mb - M);
+      l = l * sa + lb * sb;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+      for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = n0 + 16 * kc + 8 * hf + e;
-            va[i][kc][e] = key < rs
-                               ? p.v_new[(((size_t)s * p.B + key) * p.Hkv + kvh) * D + d]
-                               : (bf16_t)0.f;
-          }
-        }
-      }
-      // new row n0 + t is visible to packed row j' iff n0 + t <= r(j'): a per-lane mask
-      const int vis = qr - n0 + 1;  // visible keys of this step
-      const uint32_t live = vis <= 0 ? 0u : vis >= 32 ? 0xFFFFFFFFu : ((1u << vis) - 1u);
-      dec_step<D, true>(ka, va, qlds, o, m, l, p.scale_log2, live, hf);
+        for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * sa + b[(i * 16 + r) * 64 + lane] * sb;
+      m = M;
+    };
+    __syncthreads();  // every wave is done with the query and staging space
+    if (KS == 4) {    // ((0 + 1) + (2 + 3))
+      if (kp & 1) put(slot(kp >> 1));
+      __syncthreads();
+      if (!(kp & 1)) take(slot(kp >> 1));
+      __syncthreads();
+      if (kp == 2) put(slot(0));
+      __syncthreads();
+      if (kp == 0) take(slot(0));
+    } else {  // (0 + 1)
+      if (kp == 1) put(slot(0));
+      __syncthreads();
+      if (kp == 0) take(slot(0));
     }
+    if (kp != 0) return;
   }
+  if (!tile_live) return;
 
   // ---- partial result for this chunk ---------------------------------------
   const float lt = l + __shfl_xor(l, 32);
@@ -417,7 +514,7 @@ size_t decode_ws_bytes(int S, int B, int Hq, int Hkv, int D, int page_size, int 
   const long long cap = (long long)max_pages * page_size;
   const int nrows = (Hq / Hkv) * B;
   const int nrows_pad = ((nrows + 31) / 32) * 32;
-  const int chunk = decode_chunk(S, Hkv, nrows_pad / 32);
+  const int chunk = decode_chunk(nrows_pad / 32);
   const int nsplit = (int)std::max<long long>(1, (cap + chunk - 1) / chunk);
   if (nsplit_out) *nsplit_out = nsplit;
   if (nrows_pad_out) *nrows_pad_out = nrows_pad;
@@ -501,7 +598,7 @@ int run_decode(const void* q, const void* k_new, const void* v_new, const void* 
   a.num_pages = num_pages;
   a.nsplit = nsplit;
   a.nrows_pad = nrows_pad;
-  a.chunk = decode_chunk(S, n_kv_heads, nrows_pad / 32);
+  a.chunk = decode_chunk(nrows_pad / 32);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
   a.scale_log2 = scale * kLog2e;
 
@@ -512,10 +609,18 @@ int run_decode(const void* q, const void* k_new, const void* v_new, const void* 
   const long long merge_waves = (long long)S * n_kv_heads * a.group * B;
   MARS_REQUIRE(merge_waves < (1LL << 31), MARS_ERR_SHAPE);
   dim3 grid(nsplit, n_kv_heads * a.qgroups, S);
-  const size_t qlds = (size_t)wg_tiles * (head_dim / 16) * 64 * 16;
-  const dim3 blk(64 * wg_tiles);
-#define MARS_DECODE_LAUNCH(D_, PS_) \
-  hipLaunchKernelGGL((decode_split_kernel<D_, PS_>), grid, blk, qlds, st, a)
+  const int ks = key_split(nqt);
+  const size_t lds = split_lds_bytes(head_dim, wg_tiles, ks);
+  const dim3 blk(64 * wg_tiles * ks);
+#define MARS_DECODE_LAUNCH(D_, PS_)                                                           \
+  do {                                                                                        \
+    if (ks == 4)                                                                              \
+      hipLaunchKernelGGL((decode_split_kernel<D_, PS_, 4>), grid, blk, lds, st, a);           \
+    else if (ks == 2)                                                                         \
+      hipLaunchKernelGGL((decode_split_kernel<D_, PS_, 2>), grid, blk, lds, st, a);           \
+    else                                                                                      \
+      hipLaunchKernelGGL((decode_split_kernel<D_, PS_, 1>), grid, blk, lds, st, a);           \
+  } while (0)
   if (head_dim == 128) {
     if (page_size == 16) MARS_DECODE_LAUNCH(128, 16);
     else if (page_size == 32) MARS_DECODE_LAUNCH(128, 32);

@@ -54,22 +54,24 @@ def test_decode_lengths_on_chunk_and_page_edges():
 
 
 def test_decode_more_than_eight_chunks():
-    """Caches longer than eight 512-key chunks: the merge takes the chunk partials
-    eight at a time and rescales across batches when a later batch raises a row's
-    maximum (4096 keys = exactly eight chunks, then 9, 9, 10 and 18)."""
-    lens = [4096, 4097, 4608, 5120, 9000]
-    err, st = run(3400, len(lens), 4, 8, 2, 128, 0, 9000, 16, lens=lens)
+    """Caches longer than eight chunks (one query tile: 4 waves x 256 keys = 1024-key
+    chunks): the merge takes the chunk partials eight at a time and rescales across
+    batches when a later batch raises a row's maximum (8192 keys = exactly eight
+    chunks, then 9, 9, 10 and 18)."""
+    lens = [8192, 8193, 9216, 10240, 18000]
+    err, st = run(3400, len(lens), 4, 8, 2, 128, 0, 18000, 16, lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
-def test_decode_large_batch_uses_512_key_chunks_on_edges():
-    """130 sequences x 8 KV heads, 512-key chunks;
-    lengths sit on both sides of the chunk and single-chunk boundaries."""
+def test_decode_large_batch_on_chunk_and_wave_edges():
+    """130 sequences x 8 KV heads, one packed row per KV head (1024-key chunks split
+    over 4 waves of 256 keys); lengths sit on both sides of the wave, chunk and
+    single-chunk boundaries."""
     rng = np.random.default_rng(3150)
-    lens = rng.integers(0, 1100, size=130)
-    lens[:10] = [0, 1, 511, 512, 513, 1023, 1024, 1025, 31, 32]
-    seqs = list(range(0, 130, 9))
-    err, st = run(3150, 130, 1, 8, 8, 64, 0, 1100, 16, seqs=seqs, lens=lens)
+    lens = rng.integers(0, 2200, size=130)
+    lens[:16] = [0, 1, 255, 256, 257, 511, 512, 513, 767, 768, 1023, 1024, 1025, 2048, 31, 32]
+    seqs = list(range(0, 130, 9)) + [1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15]
+    err, st = run(3150, 130, 1, 8, 8, 64, 0, 2200, 16, seqs=sorted(set(seqs)), lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
