@@ -29,7 +29,8 @@ Extras (skippable with --no-extras): the 7B two-stream shape in causal-2L
 mode (the tile-skipping benefit), the 0.5B two-stream shape, per-kernel times
 of the decode loop, the two-pass LM head and the confidence alone, the
 attention backward at both training shapes, the causal prefill and the paged
-KV append, the commit sweep, the batch-synchronous block cache beside
+KV append, the commit at full acceptance (one layer per call, and 28 layers'
+caches in one call), the batch-synchronous block cache beside
 per-token commit and one-token AR, and the CPU oracle timed on bounded
 samples of the 7B two-stream shape, the decode step and the decode loop.
 Prints one JSON line on stdout; progress goes to stderr.

@@ -53,6 +53,15 @@ def test_decode_lengths_on_chunk_and_page_edges():
     assert err <= TOL and st == 0, (err, st)
 
 
+def test_decode_two_query_tiles_on_chunk_and_wave_edges():
+    """B = 8 with 7 query heads per KV head: 56 packed rows in two query tiles, whose
+    workgroup splits each 512-key chunk between two waves of 256 keys; lengths on
+    both sides of the wave and chunk boundaries."""
+    lens = [0, 1, 255, 256, 257, 511, 512, 513, 767, 768, 1023, 1024, 1025, 2600]
+    err, st = run(3120, len(lens), 8, 28, 4, 128, 0, 2600, 16, lens=lens)
+    assert err <= TOL and st == 0, (err, st)
+
+
 def test_decode_more_than_eight_chunks():
     """Caches longer than eight chunks (one query tile: 4 waves x 256 keys = 1024-key
     chunks): the merge takes the chunk partials eight at a time and rescales across
