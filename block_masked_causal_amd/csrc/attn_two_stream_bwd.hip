@@ -14,12 +14,13 @@
 //  * bwd_dq_kernel: the forward's structure (one wave per 32 query rows, the
 //    visible K/V tiles staged in LDS); P is recomputed from lse, dP^T = V dO^T
 //    and dQ^T += K^T dS^T with dS^T fed from registers.
-//  * bwd_dkv_kernel: one wave per 32 keys and one query head; it walks only
-//    the query blocks that can see its keys (each key's visible rows are at
-//    most two intervals), accumulating dK^T and dV^T in registers. With a GQA
-//    group of one head it writes dK, dV directly; otherwise it writes fp32
-//    partials per query head and bwd_dkv_reduce_kernel sums the group's heads
-//    in a fixed order (no atomics: the result is deterministic).
+//  * bwd_dkv_kernel: one wave per 32 keys (64 at d = 128) and one query
+//    head; it walks only the query blocks that can see its keys (each key's
+//    visible rows are at most two intervals), accumulating dK^T and dV^T in
+//    registers. With a GQA group of one head it writes dK, dV directly;
+//    otherwise it writes fp32 partials per query head and
+//    bwd_dkv_reduce_kernel sums the group's heads in a fixed order (no
+//    atomics: the result is deterministic).
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -312,76 +313,96 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ dK, dV --
-// Workgroup: 4 waves, 128 consecutive keys of one (batch, query head); wave w
-// owns keys k0 + 32 w + j. K rows sit in registers as B fragments, V rows in
-// LDS. The workgroup walks 32-row query blocks through double-buffered LDS
-// stages holding Q, dO, lse and D.
+// Workgroup: 4 waves over consecutive keys of one (batch, query head); wave w
+// owns KG groups of 32 keys, keys k0 + 32 (KG w + g) + j. The K rows of a
+// wave's keys sit in registers as B fragments, the workgroup's V rows in LDS.
+// The workgroup walks the 64-row query blocks that can see its keys through
+// double-buffered LDS stages holding Q, dO, lse and D. At d = 128 a wave owns
+// two key groups: every Q / dO fragment it reads from LDS (rows for S and dP,
+// transposed for dK and dV) then feeds both, halving the LDS bytes per MFMA
+// (with one group the kernel was bound by those reads).
 template <int D>
 struct DkvCfg {
+  static constexpr int KG = D == 128 ? 2 : 1;   // 32-key groups per wave
   static constexpr int QB = 64;                 // query rows per staged block (2 x 32)
   static constexpr int CPR = D / 8;
   static constexpr int QSZ = QB * D;            // Q (or dO) block, elements
   static constexpr int NBLK = QSZ / 512;        // 1 KiB blocks per Q (or dO) block
-  static constexpr int KB = 128;                // keys per workgroup
+  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int KB = 32 * KG * NW;       // keys per workgroup
   static constexpr int VSZ = KB * D;
 };
 
-template <int D, int MASK>
+// Bits [lo, hi) of a 32-bit mask, the range clamped to [0, 32).
+__device__ __forceinline__ uint32_t row_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 32);
+  if (hi <= lo) return 0u;
+  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u;
+  return upto_hi & ~((1u << lo) - 1u);
+}
+
+// One 32-row query sub-block for one wave's KG key groups. MASKED keeps the
+// scores of the rows whose bit is set in vm[g]: bit t is the row t past the
+// lane's first row (row offsets 8 (r / 4) + r % 4 of accumulator r).
+template <int D, int KG, bool MASKED>
 __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
                                           const bf16_t* __restrict__ Ds,
                                           const float* __restrict__ Ls,
                                           const float* __restrict__ Dl,
                                           const bf16_t* __restrict__ Vs,
-                                          const bf16x8 (&kf)[D / 16], f32x16 (&dk)[D / 32],
-                                          f32x16 (&dv)[D / 32], float cs, int lo1, int w1,
-                                          int lo2, int w2, const int (&qad)[D / 16],
-                                          const int (&qtr)[2][D / 32], const int (&vad)[D / 16],
-                                          int hf) {
-  // S = Q K^T and dP = dO V^T: lane (j, hf) holds key j and query rows
-  // 8 (r / 4) + 4 hf + r % 4 of the block
-  f32x16 s = f32x16{}, dp = f32x16{};
+                                          const bf16x8 (&kf)[KG][D / 16],
+                                          f32x16 (&dk)[KG][D / 32], f32x16 (&dv)[KG][D / 32],
+                                          float cs, const uint32_t (&vm)[KG],
+                                          const int (&qad)[D / 16], const int (&qtr)[2][D / 32],
+                                          const int (&vad)[KG][D / 16], int hf) {
+  // S = Q K^T and dP = dO V^T: lane (j, hf) holds key 32 g + j and query rows
+  // 8 (r / 4) + 4 hf + r % 4 of the sub-block
+  f32x16 s[KG], dp[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) s[g] = dp[g] = f32x16{};
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     const bf16x8 qa = *(const bf16x8*)(Qs + qad[c]);
-    s = mfma32(qa, kf[c], s);
+#pragma unroll
+    for (int g = 0; g < KG; ++g) s[g] = mfma32(qa, kf[g][c], s[g]);
   }
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     const bf16x8 da = *(const bf16x8*)(Ds + qad[c]);
-    const bf16x8 vb = *(const bf16x8*)(Vs + vad[c]);
-    dp = mfma32(da, vb, dp);
-  }
-  if constexpr (MASK != kMaskNone) {
-    int l1 = lo1, x1 = w1, l2 = lo2, x2 = w2;
-    asm volatile("" : "+v"(l1), "+v"(x1), "+v"(l2), "+v"(x2) : "v"(s));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 8 * (r >> 2) + (r & 3);
-      bool vis;
-      if constexpr (MASK == kMaskRange) {
-        vis = (uint32_t)(off - l1) < (uint32_t)x1;
-      } else {
-        vis = ((uint32_t)(off - l1) < (uint32_t)x1) | ((uint32_t)(off - l2) < (uint32_t)x2);
+    for (int g = 0; g < KG; ++g) dp[g] = mfma32(da, *(const bf16x8*)(Vs + vad[g][c]), dp[g]);
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s[g][r] = (vm[g] >> off) & 1u ? s[g][r] : -INFINITY;
       }
-      s[r] = vis ? s[r] : -INFINITY;
     }
   }
   // lse2 and D of the lane's 16 rows: 4 runs of 4 consecutive rows
-  bf16x8 pp[2], ps[2];
+  bf16x8 pp[KG][2], ps[KG][2];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 l4 = *(const f32x4*)(Ls + 8 * g + 4 * hf);
-    const f32x4 d4 = *(const f32x4*)(Dl + 8 * g + 4 * hf);
+  for (int gg = 0; gg < 4; ++gg) {
+    const f32x4 l4 = *(const f32x4*)(Ls + 8 * gg + 4 * hf);
+    const f32x4 d4 = *(const f32x4*)(Dl + 8 * gg + 4 * hf);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e;
-      const float pr = fast_exp2(fmaf(s[r], cs, -l4[e]));
-      pp[r >> 3][r & 7] = (bf16_t)pr;
-      ps[r >> 3][r & 7] = (bf16_t)(pr * (dp[r] - d4[e]));
+      const int r = 4 * gg + e;
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        const float pr = fast_exp2(fmaf(s[g][r], cs, -l4[e]));
+        pp[g][r >> 3][r & 7] = (bf16_t)pr;
+        ps[g][r >> 3][r & 7] = (bf16_t)(pr * (dp[g][r] - d4[e]));
+      }
     }
   }
   // dV^T += dO^T P and dK^T += Q^T dS: A from transposing reads of the dO / Q
-  // block (rows = query slots of the 16-row chunk kc), B from registers
+  // block (rows = query slots of the 16-row chunk kc), shared by the key
+  // groups; B from registers
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
 #pragma unroll
@@ -389,21 +410,24 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
       const bf16x4 dlo = lds_read_tr(Ds + qtr[0][i] + 16 * kc * D);
       const bf16x4 dhi = lds_read_tr(Ds + qtr[1][i] + 16 * kc * D);
       const bf16x8 da = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-      dv[i] = mfma32(da, pp[kc], dv[i]);
+#pragma unroll
+      for (int g = 0; g < KG; ++g) dv[g][i] = mfma32(da, pp[g][kc], dv[g][i]);
       const bf16x4 qlo = lds_read_tr(Qs + qtr[0][i] + 16 * kc * D);
       const bf16x4 qhi = lds_read_tr(Qs + qtr[1][i] + 16 * kc * D);
       const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-      dk[i] = mfma32(qa, ps[kc], dk[i]);
+#pragma unroll
+      for (int g = 0; g < KG; ++g) dk[g][i] = mfma32(qa, ps[g][kc], dk[g][i]);
     }
   }
 }
 
-// d = 128 runs one wave per SIMD: the dK^T / dV^T accumulators (128 registers)
-// then live in accumulation registers instead of spilling (2x faster measured).
+// d = 64: two waves per SIMD. d = 128: one, so that the 2 x 2 x 4 accumulator
+// tiles (256 registers) live in accumulation registers beside the K fragments.
 template <int D>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p) {
+__global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p) {
   using C = DkvCfg<D>;
-  // per stage: Q block, dO block, then lse2[32] and D[32]
+  constexpr int KG = C::KG, NW = C::NW;
+  // per stage: Q block, dO block, then lse2[QB] and D[QB]
   constexpr int STG_EL = 2 * C::QSZ + 4 * C::QB;  // elements (bf16 units); 2 QB floats
   __shared__ __attribute__((aligned(16))) bf16_t stage0[STG_EL];
   __shared__ __attribute__((aligned(16))) bf16_t stage1[STG_EL];
@@ -422,16 +446,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   const int hq = bh % p.Hq;
   const int kvh = hq / p.group;
   const int k0 = kbi * C::KB;
-  const int kw0 = k0 + 32 * w;
-  const int key = kw0 + j;
-  const bool key_ok = key < p.twoL;
-
-  // the lane's key and the query rows that see it
-  int lo1, hi1, lo2, hi2;
-  key_rows(min(key, p.twoL - 1), p.L, p.B, p.mask_mode, lo1, hi1, lo2, hi2);
-  if (!key_ok) {
-    hi1 = lo1;
-    hi2 = lo2;
+  int key[KG];
+  bool key_ok[KG];
+  int lo1[KG], hi1[KG], lo2[KG], hi2[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    key[g] = k0 + 32 * (KG * w + g) + j;
+    key_ok[g] = key[g] < p.twoL;
+    // the lane's key and the query rows that see it
+    key_rows(min(key[g], p.twoL - 1), p.L, p.B, p.mask_mode, lo1[g], hi1[g], lo2[g], hi2[g]);
+    if (!key_ok[g]) {
+      hi1[g] = lo1[g];
+      hi2[g] = lo2[g];
+    }
   }
   // the workgroup's query rows: the union over its keys, as up to two ranges
   const int klast = min(k0 + C::KB, p.twoL) - 1;
@@ -455,8 +482,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   if (fb2 <= lb1) fb2 = lb1 + 1;  // never the same query block twice
   const int nb1 = lb1 - fb1 + 1;
   const int nb2 = lb2 >= fb2 ? lb2 - fb2 + 1 : 0;
-  const int nblocks = nb1 + nb2;
-  const int niter = nblocks;
+  const int niter = nb1 + nb2;
 
   const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
   const uint32_t q_bytes = (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t));
@@ -466,17 +492,20 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   const rsrc_t rk = make_rsrc(p.k + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
   const rsrc_t rv = make_rsrc(p.v + (size_t)b * p.twoL * rs + (size_t)kvh * D, kv_bytes);
 
-  // K rows of the lane's key as B fragments; V rows of the workgroup's keys into LDS
-  bf16x8 kf[D / 16];
+  // K rows of the lane's keys as B fragments (rows past the end read as
+  // zeros); V rows of the workgroup's keys into LDS
+  bf16x8 kf[KG][D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    kf[c] = __builtin_bit_cast(
-        bf16x8, buf_load16(rk, (uint32_t)((key * rs + 16 * c + 8 * hf) * sizeof(bf16_t))));
+  for (int g = 0; g < KG; ++g)
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      kf[g][c] = __builtin_bit_cast(
+          bf16x8, buf_load16(rk, (uint32_t)((key[g] * rs + 16 * c + 8 * hf) * sizeof(bf16_t))));
   {
     constexpr int VB = C::VSZ / 512;  // 1 KiB blocks of the V tile
 #pragma unroll
-    for (int i = 0; i < (VB + 3) / 4; ++i) {
-      const int blk = w + 4 * i;
+    for (int i = 0; i < (VB + NW - 1) / NW; ++i) {
+      const int blk = w + NW * i;
       if (blk < VB) {
         const int u = blk * 64 + lane;
         const int row = u / C::CPR, slot = u % C::CPR;
@@ -494,8 +523,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   auto issue_block = [&](int it, bf16_t* st) {
     const int q0 = block_q0(it);
 #pragma unroll
-    for (int i = 0; i < (C::NBLK + 3) / 4; ++i) {
-      const int blk = w + 4 * i;
+    for (int i = 0; i < (C::NBLK + NW - 1) / NW; ++i) {
+      const int blk = w + NW * i;
       if (blk < C::NBLK) {
         const int u = blk * 64 + lane;
         const int row = u / C::CPR, slot = u % C::CPR;
@@ -525,14 +554,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
   };
 
   // read offsets. Row reads of the Q / dO block: row i = lane % 32, chunk 2c + hf.
-  // V row reads: key row 32 w + j. Transposing reads of Q / dO: 16-lane group
-  // g reads rows 4 (g / 2) + lane % 16 / 4 (+ 8 e, + 16 kc) at columns
+  // V row reads: key row 32 (KG w + g) + j. Transposing reads of Q / dO: 16-lane
+  // group g reads rows 4 (g / 2) + lane % 16 / 4 (+ 8 e, + 16 kc) at columns
   // 32 i + 16 (g % 2) + 4 (lane % 4).
-  int qad[D / 16], vad[D / 16], qtr[2][D / 32];
+  int qad[D / 16], qtr[2][D / 32], vad[KG][D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
     qad[c] = j * D + 8 * ((2 * c + hf) ^ swz_b<D>(j));
-    vad[c] = (32 * w + j) * D + 8 * ((2 * c + hf) ^ swz_b<D>(32 * w + j));
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      const int vr = 32 * (KG * w + g) + j;
+      vad[g][c] = vr * D + 8 * ((2 * c + hf) ^ swz_b<D>(vr));
+    }
   }
   {
     const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -545,12 +578,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
     }
   }
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 dk[KG][D / 32], dv[KG][D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
+  for (int g = 0; g < KG; ++g)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      dk[g][i] = f32x16{};
+      dv[g][i] = f32x16{};
+    }
 
   if (niter > 0) {
     issue_block(0, stage0);
@@ -558,7 +593,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
     store_ld(stage0);
   }
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(kf[c]));
+  for (int g = 0; g < KG; ++g)
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(kf[g][c]));
   __syncthreads();
 
   auto iteration = [&](int it, auto stage_tag) {
@@ -576,32 +613,34 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int q0 = block_q0(it) + 32 * sb;
-      // the lane's visible rows relative to its first row q0 + 4 hf
+      // each key group's visible rows as a bit mask over the rows past the
+      // lane's first row rb = q0 + 4 hf (bit t: row rb + t)
       const int rb = q0 + 4 * hf;
-      const int l1 = max(lo1, q0) - rb, x1 = max(min(hi1, q0 + 32) - max(lo1, q0), 0);
-      const int l2 = max(lo2, q0) - rb, x2 = max(min(hi2, q0 + 32) - max(lo2, q0), 0);
-      const bool any = __builtin_amdgcn_ballot_w64((x1 > 0) | (x2 > 0)) != 0;
-      if (any) {
+      uint32_t vm[KG];
+      bool see = false, all = true;
+#pragma unroll
+      for (int g = 0; g < KG; ++g) {
+        vm[g] = row_bits(lo1[g] - rb, hi1[g] - rb) | row_bits(lo2[g] - rb, hi2[g] - rb);
+        see = see | (min(hi1[g], q0 + 32) > max(lo1[g], q0)) |
+              (min(hi2[g], q0 + 32) > max(lo2[g], q0));
+        // every row of the sub-block visible to this key?
+        all = all & (((lo1[g] <= q0) & (hi1[g] >= q0 + 32)) |
+                     ((lo2[g] <= q0) & (hi2[g] >= q0 + 32)));
+      }
+      if (__builtin_amdgcn_ballot_w64(see) != 0) {
         const bf16_t* Qb = Qs + 32 * sb * D;
         const bf16_t* Db = Ds + 32 * sb * D;
         const float* Lb = Ls + 32 * sb;
         const float* Dlb = Ls + C::QB + 32 * sb;
-        // every row of the sub-block visible to every key of the wave?
-        const bool all1 = (lo1 <= q0) & (hi1 >= q0 + 32);
-        const bool all2 = (lo2 <= q0) & (hi2 >= q0 + 32);
-        const bool full = __builtin_amdgcn_ballot_w64(!(all1 | all2)) == 0;
-        const bool two = __builtin_amdgcn_ballot_w64((x1 > 0) & (x2 > 0)) != 0;
-        if (full) {
-          dkv_block<D, kMaskNone>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, 0, 0, 0, 0,
-                                  qad, qtr, vad, hf);
-        } else if (!two) {
-          const bool in1 = x1 > 0;
-          dkv_block<D, kMaskRange>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2,
-                                   in1 ? l1 : l2, in1 ? x1 : x2, 0, 0, qad, qtr, vad, hf);
-        } else {
-          dkv_block<D, kMaskBoth>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, l1, x1, l2,
-                                  x2, qad, qtr, vad, hf);
-        }
+        // With two key groups one code path serves every sub-block (a fully
+        // visible one has all bits set): an unmasked copy beside it in the
+        // same loop made the register allocation spill.
+        if (KG == 1 && __builtin_amdgcn_ballot_w64(!all) == 0)
+          dkv_block<D, KG, false>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr,
+                                  vad, hf);
+        else
+          dkv_block<D, KG, true>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr,
+                                 vad, hf);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -613,35 +652,39 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p
     if (it + 1 < niter) iteration(it + 1, std::integral_constant<int, 1>{});
   }
 
-  if (!key_ok) return;
   // lane (j, hf) holds dK^T / dV^T rows d = 32 i + 8 (r / 4) + 4 hf + r % 4 of its key
-  if (p.group > 1) {
-    float* dkr = p.dkp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
-    float* dvr = p.dvp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+  for (int g = 0; g < KG; ++g) {
+    if (!key_ok[g]) continue;
+    if (p.group > 1) {
+      float* dkr = p.dkp + (((size_t)b * p.twoL + key[g]) * p.Hq + hq) * D;
+      float* dvr = p.dvp + (((size_t)b * p.twoL + key[g]) * p.Hq + hq) * D;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          *(f32x4*)(dkr + 32 * i + 8 * gg + 4 * hf) =
+              f32x4{dk[g][i][4 * gg] * p.scale, dk[g][i][4 * gg + 1] * p.scale,
+                    dk[g][i][4 * gg + 2] * p.scale, dk[g][i][4 * gg + 3] * p.scale};
+          *(f32x4*)(dvr + 32 * i + 8 * gg + 4 * hf) =
+              f32x4{dv[g][i][4 * gg], dv[g][i][4 * gg + 1], dv[g][i][4 * gg + 2],
+                    dv[g][i][4 * gg + 3]};
+        }
+      continue;
+    }
+    bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key[g]) * p.Hkv + kvh) * D;
+    bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key[g]) * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        *(f32x4*)(dkr + 32 * i + 8 * gg + 4 * hf) =
-            f32x4{dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale,
-                  dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale};
-        *(f32x4*)(dvr + 32 * i + 8 * gg + 4 * hf) =
-            f32x4{dv[i][4 * gg], dv[i][4 * gg + 1], dv[i][4 * gg + 2], dv[i][4 * gg + 3]};
+        const u32x2 pk = {pack_bf16x2(dk[g][i][4 * gg] * p.scale, dk[g][i][4 * gg + 1] * p.scale),
+                          pack_bf16x2(dk[g][i][4 * gg + 2] * p.scale, dk[g][i][4 * gg + 3] * p.scale)};
+        *(u32x2*)(dkr + 32 * i + 8 * gg + 4 * hf) = pk;
+        const u32x2 pv = {pack_bf16x2(dv[g][i][4 * gg], dv[g][i][4 * gg + 1]),
+                          pack_bf16x2(dv[g][i][4 * gg + 2], dv[g][i][4 * gg + 3])};
+        *(u32x2*)(dvr + 32 * i + 8 * gg + 4 * hf) = pv;
       }
-    return;
-  }
-  bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
-  bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const u32x2 pk = {pack_bf16x2(dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale),
-                        pack_bf16x2(dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale)};
-      *(u32x2*)(dkr + 32 * i + 8 * gg + 4 * hf) = pk;
-      const u32x2 pv = {pack_bf16x2(dv[i][4 * gg], dv[i][4 * gg + 1]),
-                        pack_bf16x2(dv[i][4 * gg + 2], dv[i][4 * gg + 3])};
-      *(u32x2*)(dvr + 32 * i + 8 * gg + 4 * hf) = pv;
     }
   }
 }
@@ -695,7 +738,7 @@ int launch_bwd(BwdArgs a, hipStream_t st) {
   const double nk = (double)a.batch * a.Hq * nkb;
   if (nq >= 2147483647.0 || nk >= 2147483647.0) return MARS_ERR_SHAPE;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(64 * a.nw), 0, st, a);
-  hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)nk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)nk), dim3(64 * DkvCfg<D>::NW), 0, st, a);
   if (a.group > 1) {
     const size_t tot = (size_t)a.batch * a.twoL * a.Hkv * (D / 8);
     hipLaunchKernelGGL(bwd_dkv_reduce_kernel<D>, dim3((unsigned)((tot + 255) / 256)), dim3(256),
