@@ -32,6 +32,10 @@ def cache_bits(t):
     (3, 20, 14, 2, 64, 16, 0, 1200),     # 0.5B heads, several cache chunks
     (5, 64, 4, 2, 128, 32, 10, 90),      # the row limit
     (2, 9, 7, 1, 64, 16, 0, 0),          # empty caches
+    # 7 heads x 8 rows: two query tiles; sequences with at most 4 rows fill only the
+    # first
+    (6, 8, 28, 4, 128, 16, 0, 2500),
+    (4, 8, 14, 2, 64, 32, 0, 1500),
 ])
 def test_decode_rows_matches_oracle(S, R, Hq, Hkv, D, page, lo, hi):
     say(f"[block rows] S={S} R={R} Hq={Hq} Hkv={Hkv} D={D} page={page} len U[{lo},{hi}]")
@@ -60,9 +64,10 @@ def test_decode_rows_matches_oracle(S, R, Hq, Hkv, D, page, lo, hi):
     assert err <= 2e-2, err
 
 
-def test_decode_rows_full_equals_plain_decode_bitwise():
-    say("[block rows] n_rows = R everywhere vs the plain entry")
-    S, R, Hq, Hkv, D, page = 3, 12, 28, 4, 128, 16
+@pytest.mark.parametrize("R", [12, 8])  # 3 query tiles; 2
+def test_decode_rows_full_equals_plain_decode_bitwise(R):
+    say(f"[block rows] n_rows = R = {R} everywhere vs the plain entry")
+    S, Hq, Hkv, D, page = 3, 28, 4, 128, 16
     d = synth.decode_inputs(4200, S, R, Hq, Hkv, D, 100, 900, page)
     args = [to_dev(d.q), to_dev(d.k_new), to_dev(d.v_new), to_dev(d.k_cache), to_dev(d.v_cache),
             to_dev(d.block_table), to_dev(d.cache_len)]

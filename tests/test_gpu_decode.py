@@ -41,6 +41,7 @@ def run(seed, S, B, Hq, Hkv, D, lo, hi, page, seqs=None, lens=None):
     (3, 4, 4, 2, 64, 30, 300, 32),     # d = 64, page 32
     (2, 1, 2, 1, 128, 0, 40, 16),      # B = 1
     (2, 32, 4, 1, 64, 5, 90, 16),      # B = 32, 128 packed rows
+    (3, 8, 14, 2, 64, 0, 1500, 32),    # d = 64 with two query tiles (56 rows)
 ])
 def test_decode_matches_oracle(S, B, Hq, Hkv, D, lo, hi, page):
     err, st = run(3000 + S * 10 + B, S, B, Hq, Hkv, D, lo, hi, page)
