@@ -38,7 +38,9 @@ __device__ __forceinline__ bool in_rows(int c, int hi1, int lo2, int hi2) {
 
 // ---------------------------------------------------------------------------
 // float32 path: one wave per 64 query rows, K/V staged in LDS 32 keys at a
-// time, one query row per lane. Used for the small fp32 configuration.
+// time, one query row per lane with its q and o rows in registers (at
+// head_dim 128, 256 VGPRs + 135 accumulation registers: one wave per SIMD).
+// A full-precision check path for the small fp32 configuration, not a fast one.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void two_stream_f32_kernel(TwoStreamArgs p) {

@@ -99,6 +99,10 @@ extern "C" {
  * Query head h reads KV head h / (n_q_heads / n_kv_heads).
  * Supported: dtype MARS_BF16 with head_dim 64 or 128 (MFMA path);
  *            dtype MARS_F32  with head_dim 32, 64 or 128.
+ * The fp32 path is a full-precision check path, not a fast one: one lane per
+ * query row holds its q and o rows in registers (head_dim 128: 256 VGPRs + 135
+ * accumulation registers, one wave per SIMD; 64: 213 VGPRs; 32: 117) and K/V
+ * pass through LDS 32 keys at a time with scalar FMAs.
  * Limits: 1 <= B <= L, 2L <= 2^30, n_q_heads % n_kv_heads == 0.
  */
 int mars_attn_two_stream(const void* q, const void* k, const void* v, void* o, float* lse,
