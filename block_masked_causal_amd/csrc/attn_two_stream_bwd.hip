@@ -70,6 +70,15 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs p) {
   p.dsum[((size_t)b * p.Hq + h) * p.twoL + a] = acc;
 }
 
+// Bits [lo, hi) of a 32-bit mask, the range clamped to [0, 32).
+__device__ __forceinline__ uint32_t row_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 32);
+  if (hi <= lo) return 0u;
+  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u;
+  return upto_hi & ~((1u << lo) - 1u);
+}
+
 // ------------------------------------------------------------------ dQ ------
 template <int D>
 struct DqCfg {
@@ -85,13 +94,15 @@ struct DqCfg {
 // P^T = exp2(cs S^T - lse2_j), dS^T = P^T (dP^T - D_j), dQ^T += K^T dS^T with
 // dS^T as the B operand (K slot (hf, e) of a 16-key chunk is key 4 hf + e or
 // 8 + 4 hf + e - 4, the keys the lane holds) and K^T from transposing reads.
-template <int D, int MASK>
+// Only the keys whose bit is set in vm[n] count for the 32-key half n (bit t:
+// the key t past the lane's first key c0 + 32 n + 4 hf).
+template <int D>
 __device__ __forceinline__ void dq_tile(const bf16_t* __restrict__ Ks,
                                         const bf16_t* __restrict__ Vs,
                                         const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&dof)[D / 16], f32x16 (&dq)[D / 32],
-                                        float lse2, float dsum, float cs, int hi_a, int lo_b,
-                                        int wb, const int (&kad)[D / 16],
+                                        float lse2, float dsum, float cs, const uint32_t (&vm)[2],
+                                        const int (&kad)[D / 16],
                                         const int (&ktr)[2][D / 32]) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -106,22 +117,10 @@ __device__ __forceinline__ void dq_tile(const bf16_t* __restrict__ Ks,
       const bf16x8 va = *(const bf16x8*)(Vs + kad[c] + 32 * n * D);
       dp = mfma32(va, dof[c], dp);
     }
-    if constexpr (MASK != kMaskNone) {
-      int ha = hi_a, lb = lo_b, w = wb;
-      asm volatile("" : "+v"(ha), "+v"(lb), "+v"(w) : "v"(s));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * n + 8 * (r >> 2) + (r & 3);
-        bool vis;
-        if constexpr (MASK == kMaskUpper) {
-          vis = off < ha;
-        } else if constexpr (MASK == kMaskRange) {
-          vis = (uint32_t)(off - lb) < (uint32_t)w;
-        } else {
-          vis = (off < ha) | ((uint32_t)(off - lb) < (uint32_t)w);
-        }
-        s[r] = vis ? s[r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      s[r] = (vm[n] >> off) & 1u ? s[r] : -INFINITY;
     }
     bf16x8 ds[2];
 #pragma unroll
@@ -271,26 +270,18 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
     const int t_lo = max(c0, lim_lo), t_hi = min(c0 + C::BN, lim_hi);
     const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
     if (need) {
-      if (in_r1 && c0 + C::BN - 1 < w_full) {
-        dq_tile<D, kMaskNone>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, 0, 0, 0, kad, ktr);
-      } else {
-        const int kb = c0 + 4 * hf;
-        const int hi_a = min(hi1, lim_hi) - kb;
-        const int lo_b = max(lo2, lim_lo) - kb;
-        const int wb = max(min(hi2, lim_hi) - kb - lo_b, 0);
-        const bool any_a = __builtin_amdgcn_ballot_w64(hi_a > 0) != 0;
-        const bool any_b = __builtin_amdgcn_ballot_w64(wb > 0) != 0;
-        if (!any_b) {
-          dq_tile<D, kMaskUpper>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, hi_a, 0, 0, kad,
-                                 ktr);
-        } else if (!any_a) {
-          dq_tile<D, kMaskRange>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, 0, lo_b, wb,
-                                 kad, ktr);
-        } else {
-          dq_tile<D, kMaskBoth>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, hi_a, lo_b, wb,
-                                kad, ktr);
-        }
+      // the lane's visible keys of each 32-key half as a bit mask over the
+      // keys past kb = c0 + 32 n + 4 hf, within this tile's range
+      uint32_t vm[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int kb = c0 + 32 * n + 4 * hf;
+        vm[n] = row_bits(lim_lo - kb, min(hi1, lim_hi) - kb) |
+                row_bits(max(lo2, lim_lo) - kb, min(hi2, lim_hi) - kb);
       }
+      // one code path for every tile (a fully visible one has all bits set): the
+      // unmasked and interval-specific copies beside it made the registers spill
+      dq_tile<D>(Ks, Vs, qf, dof, dq, lse2, dsum, p.scale_log2, vm, kad, ktr);
     }
     __syncthreads();
   };
@@ -333,19 +324,10 @@ struct DkvCfg {
   static constexpr int VSZ = KB * D;
 };
 
-// Bits [lo, hi) of a 32-bit mask, the range clamped to [0, 32).
-__device__ __forceinline__ uint32_t row_bits(int lo, int hi) {
-  lo = max(lo, 0);
-  hi = min(hi, 32);
-  if (hi <= lo) return 0u;
-  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u;
-  return upto_hi & ~((1u << lo) - 1u);
-}
-
-// One 32-row query sub-block for one wave's KG key groups. MASKED keeps the
-// scores of the rows whose bit is set in vm[g]: bit t is the row t past the
-// lane's first row (row offsets 8 (r / 4) + r % 4 of accumulator r).
-template <int D, int KG, bool MASKED>
+// One 32-row query sub-block for one wave's KG key groups. Only the scores of
+// the rows whose bit is set in vm[g] count: bit t is the row t past the lane's
+// first row (row offsets 8 (r / 4) + r % 4 of accumulator r).
+template <int D, int KG>
 __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
                                           const bf16_t* __restrict__ Ds,
                                           const float* __restrict__ Ls,
@@ -373,14 +355,12 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
 #pragma unroll
     for (int g = 0; g < KG; ++g) dp[g] = mfma32(da, *(const bf16x8*)(Vs + vad[g][c]), dp[g]);
   }
-  if constexpr (MASKED) {
 #pragma unroll
-    for (int g = 0; g < KG; ++g) {
+  for (int g = 0; g < KG; ++g) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        s[g][r] = (vm[g] >> off) & 1u ? s[g][r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      s[g][r] = (vm[g] >> off) & 1u ? s[g][r] : -INFINITY;
     }
   }
   // lse2 and D of the lane's 16 rows: 4 runs of 4 consecutive rows
@@ -617,30 +597,23 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
       // lane's first row rb = q0 + 4 hf (bit t: row rb + t)
       const int rb = q0 + 4 * hf;
       uint32_t vm[KG];
-      bool see = false, all = true;
+      bool see = false;
 #pragma unroll
       for (int g = 0; g < KG; ++g) {
         vm[g] = row_bits(lo1[g] - rb, hi1[g] - rb) | row_bits(lo2[g] - rb, hi2[g] - rb);
         see = see | (min(hi1[g], q0 + 32) > max(lo1[g], q0)) |
               (min(hi2[g], q0 + 32) > max(lo2[g], q0));
-        // every row of the sub-block visible to this key?
-        all = all & (((lo1[g] <= q0) & (hi1[g] >= q0 + 32)) |
-                     ((lo2[g] <= q0) & (hi2[g] >= q0 + 32)));
       }
       if (__builtin_amdgcn_ballot_w64(see) != 0) {
         const bf16_t* Qb = Qs + 32 * sb * D;
         const bf16_t* Db = Ds + 32 * sb * D;
         const float* Lb = Ls + 32 * sb;
         const float* Dlb = Ls + C::QB + 32 * sb;
-        // With two key groups one code path serves every sub-block (a fully
-        // visible one has all bits set): an unmasked copy beside it in the
-        // same loop made the register allocation spill.
-        if (KG == 1 && __builtin_amdgcn_ballot_w64(!all) == 0)
-          dkv_block<D, KG, false>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr,
-                                  vad, hf);
-        else
-          dkv_block<D, KG, true>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr,
-                                 vad, hf);
+        // One code path serves every sub-block (a fully visible one has all
+        // bits set): an unmasked copy beside it in the same loop made the
+        // register allocation spill at d = 128 and ran slower at d = 64.
+        dkv_block<D, KG>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr, vad,
+                         hf);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
