@@ -18,8 +18,9 @@
 // The cache of one sequence is cut into chunks (split-K). Each workgroup
 // handles one (chunk, KV head, sequence); when the packed rows fill fewer than
 // 4 query tiles, the spare waves of the workgroup split the chunk's keys (4
-// waves per tile with one tile, 2 with two), each streaming 256 keys, and
-// combine their (max, sum, O) through LDS in a fixed order. The workgroup
+// waves per tile with one tile, 2 with two, each streaming 512 keys), and
+// combine their (max, sum, O) through LDS in a fixed order. Each wave fetches
+// the page ids of its own keys. The workgroup
 // writes an unnormalised partial (O, running max, running sum) per chunk; a
 // merge kernel combines the chunks, and a sequence that fits in one chunk is
 // written out directly.
@@ -159,8 +160,11 @@ __device__ __forceinline__ int rows_of(const DecodeArgs& p, int s) {
   return p.n_rows ? min(max(p.n_rows[s], 0), p.B) : p.B;
 }
 
-// Keys of the cache one wave streams; a chunk is kKeysPerWave x KS keys.
-constexpr int kKeysPerWave = 256;
+// Keys of the cache one wave streams: 512 when several waves share a query
+// tile (2048-key chunks with four, 1024 with two, so fewer chunk partials are
+// written and merged), else 256. A chunk is keys_per_wave x KS keys. A wave's
+// keys span at most 32 pages, one page id per lane.
+__host__ __device__ constexpr int keys_per_wave(int KS) { return KS == 1 ? 256 : 512; }
 // V rows of the new keys (at most kMaxRows) staged transposed in LDS:
 // [head_dim][kNewStride] bf16; a row of 144 bytes keeps 16-byte reads aligned.
 constexpr int kNewStride = 72;
@@ -175,9 +179,8 @@ __host__ __device__ constexpr size_t split_lds_bytes(int D, int tiles, int KS) {
 }
 
 // Split-K chunk (cache keys per workgroup): each of the key_split(nqt) waves
-// of a query tile streams kKeysPerWave keys of it. The chunk's page ids are
-// held one per lane (<= 64 pages of >= 16 keys: chunks of at most 1024 keys).
-inline int decode_chunk(int nqt) { return kKeysPerWave * key_split(nqt); }
+// of a query tile streams keys_per_wave of it.
+inline int decode_chunk(int nqt) { return keys_per_wave(key_split(nqt)) * key_split(nqt); }
 
 // PS = the page size when it is a compile-time constant (16 or 32, the block
 // granularities the method uses), or 0 for any other multiple of 16.
@@ -210,8 +213,8 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   const int k_hi = min(len, k_lo + p.chunk);
   const bool single = len <= p.chunk;  // the only chunk: write the final output
   // this wave's share of the chunk
-  const int w_lo = min(k_lo + kp * kKeysPerWave, k_hi);
-  const int w_hi = min(w_lo + kKeysPerWave, k_hi);
+  const int w_lo = min(k_lo + kp * keys_per_wave(KS), k_hi);
+  const int w_hi = min(w_lo + keys_per_wave(KS), k_hi);
 
   // Packed query row of this lane: j' = r * g + head_in_group.
   const int qi = tq * 32 + j;
@@ -252,17 +255,19 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
         qlds[64 * c] = qvalid ? *(const bf16x8*)(qrow + 16 * c) : bf16x8{};
     }
 
-    // Page ids of this chunk, one per lane (lane t: page k_lo / ps + t); -1 = bad.
+    // Page ids of this wave's keys, one per lane (lane t: page w_lo / ps + t;
+    // at most 32 pages of >= 16 keys); -1 = bad.
     const int ps = PS > 0 ? PS : p.page_size;
-    const int pg0 = k_lo / ps;
-    const int npg = k_hi > k_lo ? (k_hi - 1) / ps - pg0 + 1 : 0;
+    const int pg0 = w_lo / ps;
+    const int npg = w_hi > w_lo ? (w_hi - 1) / ps - pg0 + 1 : 0;
     int mypage = 0;
     if (lane < npg) {
       const int raw = p.block_table[(size_t)s * p.max_pages + pg0 + lane];
       mypage = (raw >= 0 && raw < p.num_pages) ? raw : -1;
     }
+    // a wave whose keys touch a bad page masks every step (the page's keys drop out)
     const bool chunk_bad = __ballot(mypage < 0) != 0;
-    if (chunk_bad && lane == 0 && kp == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
+    if (chunk_bad && lane == 0) status_or(p.status, MARS_STATUS_BAD_PAGE);
 
     const size_t kpage = (size_t)p.Hkv * ps * D;  // elements per page (all heads)
     const bf16_t* kbase = p.k_cache + (size_t)kvh * ps * D;

@@ -49,39 +49,43 @@ def test_decode_matches_oracle(S, B, Hq, Hkv, D, lo, hi, page):
 
 
 def test_decode_lengths_on_chunk_and_page_edges():
-    lens = [0, 1, 15, 16, 31, 32, 255, 256, 257, 511, 512, 513]
-    err, st = run(3100, len(lens), 4, 8, 2, 128, 0, 520, 16, lens=lens)
+    """One query tile: 2048-key chunks split over 4 waves of 512 keys; lengths on both
+    sides of page, wave and chunk boundaries."""
+    lens = [0, 1, 15, 16, 31, 32, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047,
+            2048, 2049]
+    err, st = run(3100, len(lens), 4, 8, 2, 128, 0, 2060, 16, lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
 def test_decode_two_query_tiles_on_chunk_and_wave_edges():
     """B = 8 with 7 query heads per KV head: 56 packed rows in two query tiles, whose
-    workgroup splits each 512-key chunk between two waves of 256 keys; lengths on
+    workgroup splits each 1024-key chunk between two waves of 512 keys; lengths on
     both sides of the wave and chunk boundaries."""
-    lens = [0, 1, 255, 256, 257, 511, 512, 513, 767, 768, 1023, 1024, 1025, 2600]
+    lens = [0, 1, 511, 512, 513, 1023, 1024, 1025, 1535, 1536, 2047, 2048, 2049, 2600]
     err, st = run(3120, len(lens), 8, 28, 4, 128, 0, 2600, 16, lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
 def test_decode_more_than_eight_chunks():
-    """Caches longer than eight chunks (one query tile: 4 waves x 256 keys = 1024-key
+    """Caches longer than eight chunks (one query tile: 4 waves x 512 keys = 2048-key
     chunks): the merge takes the chunk partials eight at a time and rescales across
-    batches when a later batch raises a row's maximum (8192 keys = exactly eight
+    batches when a later batch raises a row's maximum (16384 keys = exactly eight
     chunks, then 9, 9, 10 and 18)."""
-    lens = [8192, 8193, 9216, 10240, 18000]
-    err, st = run(3400, len(lens), 4, 8, 2, 128, 0, 18000, 16, lens=lens)
+    lens = [16384, 16385, 18432, 20480, 36000]
+    err, st = run(3400, len(lens), 4, 8, 2, 128, 0, 36000, 16, lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
 def test_decode_large_batch_on_chunk_and_wave_edges():
-    """130 sequences x 8 KV heads, one packed row per KV head (1024-key chunks split
-    over 4 waves of 256 keys); lengths sit on both sides of the wave, chunk and
+    """130 sequences x 8 KV heads, one packed row per KV head (2048-key chunks split
+    over 4 waves of 512 keys); lengths sit on both sides of the wave, chunk and
     single-chunk boundaries."""
     rng = np.random.default_rng(3150)
-    lens = rng.integers(0, 2200, size=130)
-    lens[:16] = [0, 1, 255, 256, 257, 511, 512, 513, 767, 768, 1023, 1024, 1025, 2048, 31, 32]
-    seqs = list(range(0, 130, 9)) + [1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15]
-    err, st = run(3150, 130, 1, 8, 8, 64, 0, 2200, 16, seqs=sorted(set(seqs)), lens=lens)
+    lens = rng.integers(0, 4400, size=130)
+    lens[:18] = [0, 1, 511, 512, 513, 1023, 1024, 1025, 1535, 1536, 2047, 2048, 2049, 4095,
+                 4096, 4097, 31, 32]
+    seqs = list(range(0, 130, 9)) + list(range(1, 18))
+    err, st = run(3150, 130, 1, 8, 8, 64, 0, 4400, 16, seqs=sorted(set(seqs)), lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
@@ -116,11 +120,16 @@ def test_decode_equals_two_stream_mask_rows_on_gpu():
     assert max_abs(from_dev(od), want) <= TOL
 
 
-def test_decode_flags_bad_page_and_overflow_without_faulting():
-    say("[decode] status flags for a bad page id and an over-long cache_len")
-    d = synth.decode_inputs(3300, 3, 4, 8, 2, 128, 20, 60, 16, extra_capacity=4)
+@pytest.mark.parametrize("bad_page", [0, 40, 100])
+def test_decode_flags_bad_page_and_overflow_without_faulting(bad_page):
+    """A bad page id in the first, second or fourth 512-key part of sequence 1's first
+    chunk (the wave holding it flags it and masks its keys), and a cache_len longer
+    than the pages sequence 2 owns."""
+    say(f"[decode] status flags for a bad page id (page {bad_page}) and an over-long cache_len")
+    d = synth.decode_inputs(3300, 3, 4, 8, 2, 128, 20, 1800, 16, extra_capacity=4)
+    d.cache_len[:2] = [45, 1700]
     q, kn, vn, kc, vc, bt, cl = dev_inputs(d)
-    bt[1, 0] = -5                 # bad page id in sequence 1
+    bt[1, bad_page] = -5          # bad page id in sequence 1
     cl[2] = bt.shape[1] * 16 + 7  # longer than the pages sequence 2 owns
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
     o = mars.mars_attn_block_decode(q, kn, vn, kc, vc, bt, cl, status=status)
