@@ -18,6 +18,8 @@
 //    the running max), and reduces them in the workgroup (sums in fp64).
 //  * conf_merge_kernel: combines the chunks of a row in a fixed order:
 //    top_id = lowest index attaining the maximum, p_max = 1 / sum exp(l - m).
+//  * conf_row_kernel: with at least 256 rows, one 1024-thread workgroup per
+//    row does both in one pass (no partials, no second launch).
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
@@ -396,6 +398,74 @@ __global__ __launch_bounds__(256) void conf_partial_kernel(ConfArgs p) {
   }
 }
 
+// Confidence of whole rows, one 1024-thread workgroup per row (used when
+// there are enough rows to fill the GPU, N >= kRowKernelMinRows): no partials
+// and no merge launch. Each thread keeps four 16-byte loads in flight and folds
+// its elements in index order; then a fixed butterfly over each wave and a
+// fixed order over the 16 waves, sums in fp64.
+constexpr int kRowThreads = 1024;
+constexpr int kRowKernelMinRows = 256;
+__global__ __launch_bounds__(kRowThreads) void conf_row_kernel(ConfArgs p) {
+  constexpr int U = 4;  // loads in flight per thread
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* L = p.logits + (size_t)row * p.V;
+  float m = -INFINITY;
+  int idx = 0x7FFFFFFF;
+  float s = 0.f;
+  bool bad = false;
+  auto fold = [&](const f32x4& x, int i) {
+    bad |= !(isfinite(x[0]) && isfinite(x[1]) && isfinite(x[2]) && isfinite(x[3]));
+    const float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (bm > m) {
+      s = m == -INFINITY ? 0.f : s * fast_exp2((m - bm) * kLog2e);
+      m = bm;
+      idx = x[0] == bm ? i : (x[1] == bm ? i + 1 : (x[2] == bm ? i + 2 : i + 3));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += fast_exp2((x[e] - m) * kLog2e);
+  };
+  constexpr int step = 4 * kRowThreads;
+  int i = 4 * tid;
+  for (; i + (U - 1) * step < p.V; i += U * step) {
+    f32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = *(const f32x4*)(L + i + u * step);
+#pragma unroll
+    for (int u = 0; u < U; ++u) fold(x[u], i + u * step);
+  }
+  for (; i < p.V; i += step) fold(*(const f32x4*)(L + i), i);
+  if (bad) status_or(p.status, MARS_STATUS_NONFINITE);
+
+  double sd = (double)s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const int i2 = __shfl_xor(idx, o);
+    const double s2 = __shfl_xor(sd, o);
+    conf_combine(m, idx, sd, m2, i2, s2);
+  }
+  constexpr int NWV = kRowThreads / 64;
+  __shared__ float sm[NWV];
+  __shared__ int si[NWV];
+  __shared__ double ss[NWV];
+  const int wv = tid >> 6;
+  if ((tid & 63) == 0) {
+    sm[wv] = m;
+    si[wv] = idx;
+    ss[wv] = sd;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = sm[0];
+    int I = si[0];
+    double S = ss[0];
+    for (int k = 1; k < NWV; ++k) conf_combine(M, I, S, sm[k], si[k], ss[k]);
+    p.top_id[row] = I == 0x7FFFFFFF ? 0 : I;
+    p.p_max[row] = (float)(1.0 / S);
+  }
+}
+
 __global__ __launch_bounds__(256) void conf_merge_kernel(ConfArgs p) {
   const int row = blockIdx.x * 256 + threadIdx.x;
   if (row >= p.N) return;
@@ -605,6 +675,10 @@ int launch_lmhead(const void* hidden, const void* w_lm, int packed, float* logit
     }
   }
   conf_layout(N, V, &c.nchunk, &c.chunk);
+  if (N >= kRowKernelMinRows) {
+    hipLaunchKernelGGL(conf_row_kernel, dim3(N), dim3(kRowThreads), 0, st, c);
+    return mars_launch_status();
+  }
   hipLaunchKernelGGL(conf_partial_kernel, dim3(c.nchunk, N), dim3(256), 0, st, c);
   hipLaunchKernelGGL(conf_merge_kernel, dim3((N + 255) / 256), dim3(256), 0, st, c);
   return mars_launch_status();

@@ -139,6 +139,15 @@ def test_decode_flags_bad_page_and_overflow_without_faulting(bad_page):
     ref = oracle.attn_block_decode(d.q.f32, d.k_new.f32, d.v_new.f32, d.k_cache.f32,
                                    d.v_cache.f32, d.block_table, d.cache_len, 16, seqs=[0])
     assert max_abs(from_dev(o)[0:1], ref) <= TOL  # untouched sequences stay exact
+    # sequence 1 equals the same sequence with the bad page's 16 keys left out
+    table = d.block_table.copy()
+    row = table[1]
+    table[1] = np.concatenate([np.delete(row, bad_page), row[bad_page:bad_page + 1]])
+    lens = d.cache_len.copy()
+    lens[1] -= 16
+    ref1 = oracle.attn_block_decode(d.q.f32, d.k_new.f32, d.v_new.f32, d.k_cache.f32,
+                                    d.v_cache.f32, table, lens, 16, seqs=[1])
+    assert max_abs(from_dev(o)[1:2], ref1) <= TOL
 
 
 def test_full_size_qwen7b_decode_sampled_sequences():
