@@ -448,70 +448,69 @@ __global__ __launch_bounds__(64 * kMaxQT, 2) void decode_split_kernel(DecodeArgs
   }
 }
 
-// One wave per (sequence, KV head, packed query row): combine the chunks.
+// One workgroup per (sequence, KV head): combine the chunks of each packed
+// query row. A thread owns 4 consecutive head-dimension elements of a row at a
+// time (D / 4 threads per row); a sequence whose cache fits in one chunk was
+// written directly by the split kernel and is skipped.
+constexpr int kMergeThreads = 512;
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs p) {
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int nrows = p.group * p.B;
-  const int total = p.S * p.Hkv * nrows;
-  if (wave >= total) return;
-  const int qi = wave % nrows;
-  const int kvh = (wave / nrows) % p.Hkv;
-  const int s = wave / (nrows * p.Hkv);
-  if (qi >= p.group * rows_of(p, s)) return;  // not a row of this sequence
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs p) {
+  const int kvh = blockIdx.x % p.Hkv;
+  const int s = blockIdx.x / p.Hkv;
   int len = p.cache_len[s];
   len = min(max(len, 0), p.max_pages * p.page_size);
   const int nsp = max(1, (len + p.chunk - 1) / p.chunk);
   if (nsp == 1) return;  // written directly by the split kernel
-
-  const size_t base = (((size_t)s * p.Hkv + kvh) * p.nsplit) * p.nrows_pad + qi;
+  const int nrows = p.group * rows_of(p, s);
+  constexpr int Q4 = D / 4;  // threads per row
   const size_t stride = p.nrows_pad;
-  constexpr int PER = D / 64;
+  const size_t base0 = ((size_t)s * p.Hkv + kvh) * p.nsplit * p.nrows_pad;
   // Chunks are taken kMergeBatch at a time with all their loads in flight
   // (one memory round trip per batch, not two per chunk), in chunk order. A
   // later batch that raises the maximum rescales what came before; with at
   // most kMergeBatch chunks the arithmetic is a single fixed-order pass.
   constexpr int kMergeBatch = 8;
-  float M = -INFINITY, lsum = 0.f;
-  float acc[PER];
+  for (int e = threadIdx.x; e < nrows * Q4; e += kMergeThreads) {
+    const int qi = e / Q4, d0 = 4 * (e % Q4);
+    const size_t base = base0 + qi;
+    float M = -INFINITY, lsum = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < nsp; sp0 += kMergeBatch) {
+      float mv[kMergeBatch], lv[kMergeBatch];
+      f32x4 ov[kMergeBatch];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int sp0 = 0; sp0 < nsp; sp0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch][PER];
+      for (int t = 0; t < kMergeBatch; ++t) {
+        const bool in = sp0 + t < nsp;
+        const size_t row = base + (size_t)(in ? sp0 + t : sp0) * stride;
+        mv[t] = in ? p.part_ml[row * 2] : -INFINITY;
+        lv[t] = in ? p.part_ml[row * 2 + 1] : 0.f;
+        ov[t] = in ? *(const f32x4*)(p.part_o + row * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float mt = M;
 #pragma unroll
-    for (int t = 0; t < kMergeBatch; ++t) {
-      const bool in = sp0 + t < nsp;
-      const size_t row = base + (size_t)(in ? sp0 + t : sp0) * stride;
-      mv[t] = in ? p.part_ml[row * 2] : -INFINITY;
-      lv[t] = in ? p.part_ml[row * 2 + 1] : 0.f;
+      for (int t = 0; t < kMergeBatch; ++t) mt = fmaxf(mt, mv[t]);
+      const float mb = mt == -INFINITY ? 0.f : mt;
+      if (M != -INFINITY && M != mt) {  // a later batch raised the maximum
+        const float sc = fast_exp2(M - mb);
+        lsum *= sc;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) ov[t][e] = in ? p.part_o[row * D + lane * PER + e] : 0.f;
+        for (int k = 0; k < 4; ++k) acc[k] *= sc;
+      }
+#pragma unroll
+      for (int t = 0; t < kMergeBatch; ++t) {
+        const float w = mv[t] == -INFINITY ? 0.f : fast_exp2(mv[t] - mb);
+        lsum += w * lv[t];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] += w * ov[t][k];
+      }
+      M = mt;
     }
-    float mt = M;
-#pragma unroll
-    for (int t = 0; t < kMergeBatch; ++t) mt = fmaxf(mt, mv[t]);
-    const float mb = mt == -INFINITY ? 0.f : mt;
-    if (M != -INFINITY && M != mt) {  // a later batch raised the maximum
-      const float sc = fast_exp2(M - mb);
-      lsum *= sc;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] *= sc;
-    }
-#pragma unroll
-    for (int t = 0; t < kMergeBatch; ++t) {
-      const float w = mv[t] == -INFINITY ? 0.f : fast_exp2(mv[t] - mb);
-      lsum += w * lv[t];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * ov[t][e];
-    }
-    M = mt;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int r = qi / p.group, h = kvh * p.group + qi % p.group;
+    bf16_t* orow = p.o + (((size_t)s * p.B + r) * p.Hq + h) * D + d0;
+    *(u32x2*)orow = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                          pack_bf16x2(acc[2] * inv, acc[3] * inv)};
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const int r = qi / p.group, h = kvh * p.group + qi % p.group;
-  bf16_t* orow = p.o + (((size_t)s * p.B + r) * p.Hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) orow[e] = (bf16_t)(acc[e] * inv);
 }
 
 size_t decode_ws_bytes(int S, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
@@ -611,8 +610,8 @@ int run_decode(const void* q, const void* k_new, const void* v_new, const void* 
   const int nqt = nrows_pad / 32;
   const int wg_tiles = nqt < kMaxQT ? nqt : kMaxQT;
   a.qgroups = (nqt + kMaxQT - 1) / kMaxQT;
-  const long long merge_waves = (long long)S * n_kv_heads * a.group * B;
-  MARS_REQUIRE(merge_waves < (1LL << 31), MARS_ERR_SHAPE);
+  const long long merge_blocks = (long long)S * n_kv_heads;
+  MARS_REQUIRE(merge_blocks < (1LL << 31), MARS_ERR_SHAPE);
   dim3 grid(nsplit, n_kv_heads * a.qgroups, S);
   const int ks = key_split(nqt);
   const size_t lds = split_lds_bytes(head_dim, wg_tiles, ks);
@@ -630,12 +629,12 @@ int run_decode(const void* q, const void* k_new, const void* v_new, const void* 
     if (page_size == 16) MARS_DECODE_LAUNCH(128, 16);
     else if (page_size == 32) MARS_DECODE_LAUNCH(128, 32);
     else MARS_DECODE_LAUNCH(128, 0);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)merge_blocks), dim3(kMergeThreads), 0, st, a);
   } else {
     if (page_size == 16) MARS_DECODE_LAUNCH(64, 16);
     else if (page_size == 32) MARS_DECODE_LAUNCH(64, 32);
     else MARS_DECODE_LAUNCH(64, 0);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((merge_waves + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)merge_blocks), dim3(kMergeThreads), 0, st, a);
   }
 #undef MARS_DECODE_LAUNCH
   return mars_launch_status();
