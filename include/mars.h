@@ -305,14 +305,14 @@ size_t mars_decode_workspace_bytes(int32_t S, int32_t B, int32_t n_q_heads, int3
  * logits  [N, V] float32: written (= hidden . w_lm^T, fp32 accumulation) when
  *         hidden != NULL, read otherwise. May be NULL when hidden != NULL:
  *         then the confidence is reduced inside the GEMM (per row and
- *         256-entry vocabulary tile: max, lowest argmax, sum of exp) and no
- *         logits are written. top_id is identical to the unfused call (same
+ *         vocabulary tile of 320 entries, or 64 in a tail launch: max, lowest
+ *         argmax, sum of exp) and no logits are written. top_id is identical to the unfused call (same
  *         fp32 values); p_max agrees to fp32 rounding of the sum order.
  * top_id  [N] int32, p_max [N] float32 (written).
  * workspace >= mars_lmhead_workspace_bytes(N, V) bytes (covers both forms).
  * status  optional: MARS_STATUS_NONFINITE if a row held NaN/Inf (that row's
  *         p_max is then NaN or 0). The fused form detects NaN and +Inf.
- * Limits: D % 32 == 0 when hidden != NULL; V % 4 == 0; N >= 1.
+ * Limits: D % 32 == 0 when hidden != NULL; V % 4 == 0; 1 <= N <= 65535.
  */
 int mars_lmhead_confidence(const void* hidden, const void* w_lm, float* logits, int32_t N,
                            int32_t D, int32_t V, int32_t* top_id, float* p_max,
