@@ -61,8 +61,9 @@ def test_decode_two_query_tiles_on_chunk_and_wave_edges():
     """B = 8 with 7 query heads per KV head: 56 packed rows in two query tiles, whose
     workgroup splits each 1024-key chunk between two waves of 512 keys; lengths on
     both sides of the wave and chunk boundaries."""
-    lens = [0, 1, 511, 512, 513, 1023, 1024, 1025, 1535, 1536, 2047, 2048, 2049, 2600]
-    err, st = run(3120, len(lens), 8, 28, 4, 128, 0, 2600, 16, lens=lens)
+    lens = [0, 1, 511, 512, 513, 1023, 1024, 1025, 1535, 1536, 2047, 2048, 2049, 2600,
+            8192, 9000, 12000]  # the last three: more than eight chunks
+    err, st = run(3120, len(lens), 8, 28, 4, 128, 0, 12000, 16, lens=lens)
     assert err <= TOL and st == 0, (err, st)
 
 
