@@ -102,15 +102,16 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 
 
-// How a tile's keys are tested against a lane's visible intervals (both given
-// relative to the lane's first key kb = c0 + 4 hf). The first interval always
-// starts at or before the tile, so only its upper end matters.
-enum : int {
-  kMaskNone = 0,   // every key visible to every row of the wave
-  kMaskUpper = 1,  // key < hi_a
-  kMaskRange = 2,  // lo_b <= key < lo_b + wb
-  kMaskBoth = 3,   // either
-};
+// Bits [lo, hi) of a 32-bit mask, the range clamped to [0, 32): a lane's
+// visible keys among the 32 keys of a tile half (bit t = key t past the
+// lane's first key).
+__device__ __forceinline__ uint32_t row_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 32);
+  if (hi <= lo) return 0u;
+  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u;
+  return upto_hi & ~((1u << lo) - 1u);
+}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;

@@ -131,6 +131,8 @@ constexpr float kLazyRescale = 8.0f;
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
 // O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
 // row. kad[c] / vad[i] are the lane's K and V^T read offsets inside a tile.
+// MASKED: only the keys whose bit is set in vm0 (half 0) or vm1 (half 1)
+// count (bit 8 (r / 4) + r % 4 of a half is the lane's score r).
 //
 // The tile is worked as two 32-key halves in a software pipeline, so that a
 // wave always has matrix work next to its vector work: the scores of half 1
@@ -138,12 +140,12 @@ constexpr float kLazyRescale = 8.0f;
 // P V products run while half 1's probabilities are formed. Each half keeps
 // the lazy running maximum; when half 1 raises it, the output is rescaled
 // after half 0's products (which were formed with the old maximum).
-template <int D, int MASK>
+template <int D, bool MASKED>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
                                           const bf16_t* __restrict__ Vs,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                          float& m, float& l, float cs, int hi_a, int lo_b,
-                                          int wb, const int (&kad)[D / 16],
+                                          float& m, float& l, float cs, uint32_t vm0,
+                                          uint32_t vm1, const int (&kad)[D / 16],
                                           const int (&vad)[D / 32]) {
   auto qk = [&](int n) {
     f32x16 acc = f32x16{};
@@ -155,24 +157,13 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
     return acc;
   };
   auto mask = [&](f32x16& sv, int n) {
-    if constexpr (MASK != kMaskNone) {
-      // tie the bounds to the scores so that the per-key tests are computed
+    if constexpr (MASKED) {
+      // tie the mask to the scores so that the per-key tests are computed
       // after the products, not hoisted above them with every result held live
-      int ha = hi_a, lb = lo_b, w = wb;
-      asm volatile("" : "+v"(ha), "+v"(lb), "+v"(w) : "v"(sv));
+      uint32_t vm = n == 0 ? vm0 : vm1;
+      asm volatile("" : "+v"(vm) : "v"(sv));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * n + 8 * (r >> 2) + (r & 3);
-        bool vis;
-        if constexpr (MASK == kMaskUpper) {
-          vis = off < ha;
-        } else if constexpr (MASK == kMaskRange) {
-          vis = (uint32_t)(off - lb) < (uint32_t)w;
-        } else {
-          vis = (off < ha) | ((uint32_t)(off - lb) < (uint32_t)w);
-        }
-        sv[r] = vis ? sv[r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) sv[r] = (vm >> (8 * (r >> 2) + (r & 3))) & 1u ? sv[r] : -INFINITY;
     }
   };
   // row max of the raw scores, in log2 units (the scale is positive, so it
@@ -407,26 +398,19 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
     if (need) {
       if (in_r1 && c0 + C::BN - 1 < w_full) {
-        tile_step<D, kMaskNone>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, 0, 0, kad, vad);
+        tile_step<D, false>(Ks, Vs, qf, o, m, l, p.scale_log2, 0u, 0u, kad, vad);
       } else {
-        // the row's visible intervals clipped to the staged range, relative
-        // to the lane's first key
+        // the row's visible intervals clipped to the staged range, as one bit
+        // mask per 32-key half (bit t: key t of the half past the lane's first
+        // key kb). One masked code path serves every partial tile: per-kind
+        // copies (upper bound, range, both) held 43 more VGPRs at d = 64.
         const int kb = c0 + 4 * hf;
         const int hi_a = min(hi1, lim_hi) - kb;
         const int lo_b = max(lo2, lim_lo) - kb;
-        const int wb = max(min(hi2, lim_hi) - kb - lo_b, 0);
-        const bool any_a = __builtin_amdgcn_ballot_w64(hi_a > 0) != 0;
-        const bool any_b = __builtin_amdgcn_ballot_w64(wb > 0) != 0;
-        if (!any_b) {
-          tile_step<D, kMaskUpper>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, 0, 0, kad,
-                                   vad);
-        } else if (!any_a) {
-          tile_step<D, kMaskRange>(Ks, Vs, qf, o, m, l, p.scale_log2, 0, lo_b, wb, kad,
-                                   vad);
-        } else {
-          tile_step<D, kMaskBoth>(Ks, Vs, qf, o, m, l, p.scale_log2, hi_a, lo_b, wb, kad,
-                                  vad);
-        }
+        const int hi_b = min(hi2, lim_hi) - kb;
+        const uint32_t vm0 = row_bits(0, hi_a) | row_bits(lo_b, hi_b);
+        const uint32_t vm1 = row_bits(-32, hi_a - 32) | row_bits(lo_b - 32, hi_b - 32);
+        tile_step<D, true>(Ks, Vs, qf, o, m, l, p.scale_log2, vm0, vm1, kad, vad);
       }
     }
 

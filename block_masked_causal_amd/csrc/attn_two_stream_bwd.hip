@@ -70,14 +70,6 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs p) {
   p.dsum[((size_t)b * p.Hq + h) * p.twoL + a] = acc;
 }
 
-// Bits [lo, hi) of a 32-bit mask, the range clamped to [0, 32).
-__device__ __forceinline__ uint32_t row_bits(int lo, int hi) {
-  lo = max(lo, 0);
-  hi = min(hi, 32);
-  if (hi <= lo) return 0u;
-  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : (1u << hi) - 1u;
-  return upto_hi & ~((1u << lo) - 1u);
-}
 
 // ------------------------------------------------------------------ dQ ------
 template <int D>
