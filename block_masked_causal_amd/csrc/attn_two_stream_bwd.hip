@@ -48,21 +48,27 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------------ D -------
+// D = rowsum(dO * O) per (b, a, h) row: D / 8 lanes per row, each reading 16
+// bytes of dO and of O (one row per 16-byte-per-lane load: coalesced), then
+// a butterfly over those lanes.
+template <int D>
+constexpr int dsum_rows_per_block() { return 256 / (D / 8); }
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs p) {
-  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;  // (b, a, h) in [b][2L][Hq] order
-  const size_t rows = (size_t)p.batch * p.twoL * p.Hq;
-  if (row >= rows) return;
-  const bf16_t* dor = p.dout + row * D;
-  const bf16_t* orr = p.o + row * D;
+  constexpr int LPR = D / 8;  // lanes per row
+  const size_t row = (size_t)blockIdx.x * dsum_rows_per_block<D>() + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  const size_t rows = (size_t)p.batch * p.twoL * p.Hq;  // (b, a, h) in [b][2L][Hq] order
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 x = *(const bf16x8*)(dor + 8 * c);
-    const bf16x8 y = *(const bf16x8*)(orr + 8 * c);
+  if (row < rows) {
+    const bf16x8 x = *(const bf16x8*)(p.dout + row * D + 8 * part);
+    const bf16x8 y = *(const bf16x8*)(p.o + row * D + 8 * part);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
   }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (row >= rows || part != 0) return;
   const int h = (int)(row % p.Hq);
   const size_t ba = row / p.Hq;
   const int a = (int)(ba % p.twoL);
@@ -691,8 +697,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
 template <int D>
 int launch_bwd(BwdArgs a, hipStream_t st) {
   const size_t rows = (size_t)a.batch * a.twoL * a.Hq;
-  hipLaunchKernelGGL(bwd_dsum_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
-                     a);
+  constexpr int rpb = dsum_rows_per_block<D>();
+  hipLaunchKernelGGL(bwd_dsum_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
+                     st, a);
   a.gh = D == 64 ? 1 : heads_per_wg(a.group);
   a.nhc = a.group / a.gh;
   a.rt = D == 64 ? 4 : 8 / a.gh;
