@@ -297,9 +297,8 @@ def test_full_size_block_cache_step_sampled_sequences():
     ref = oracle.attn_block_decode_rows(d.q.f32, d.k_new.f32, d.v_new.f32, d.k_cache.f32,
                                         d.v_cache.f32, d.block_table, d.cache_len, nrows, page,
                                         seqs=seqs)
-    og = from_dev(o)
-    for s in seqs:
-        assert max_abs(og[s, :nrows[s]], ref[s]) <= 2e-2, s
+    for s in seqs:  # rows past nrows[s] are not written: convert only the written ones
+        assert max_abs(from_dev(o[s, :nrows[s]]), ref[s]) <= 2e-2, s
     _, _, rl, froze = oracle.block_freeze(d.k_cache.f32, d.v_cache.f32, d.block_table,
                                           d.cache_len, d.k_new.f32, d.v_new.f32, u, Bc, page)
     rk, ru, rt, _, rn = oracle.block_sync_step(p, ids, tau, u, toks, Bc, "min")
