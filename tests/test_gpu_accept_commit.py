@@ -74,7 +74,7 @@ def test_tiny_fp32_config_acceptance_and_commit():
 
 
 @pytest.mark.parametrize("dtype,Hkv,D,page", [("bf16", 4, 128, 16), ("f32", 2, 64, 32),
-                                                ("bf16", 2, 8, 16),
+                                                ("bf16", 2, 8, 16), ("bf16", 4, 128, 48),
                                                 # V rows staged one per pass (8 KiB rows)
                                                 ("f32", 2, 2048, 16),
                                                 # rows too long to stage: element path

@@ -42,6 +42,10 @@ def run(seed, S, B, Hq, Hkv, D, lo, hi, page, seqs=None, lens=None):
     (2, 1, 2, 1, 128, 0, 40, 16),      # B = 1
     (2, 32, 4, 1, 64, 5, 90, 16),      # B = 32, 128 packed rows
     (3, 8, 14, 2, 64, 0, 1500, 32),    # d = 64 with two query tiles (56 rows)
+    # page sizes without a specialised instance: 48 (a page straddles the
+    # 512-key wave boundary) and 64
+    (4, 4, 28, 4, 128, 0, 2600, 48),
+    (3, 8, 14, 2, 64, 0, 2600, 64),
 ])
 def test_decode_matches_oracle(S, B, Hq, Hkv, D, lo, hi, page):
     err, st = run(3000 + S * 10 + B, S, B, Hq, Hkv, D, lo, hi, page)
