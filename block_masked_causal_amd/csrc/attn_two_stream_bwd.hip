@@ -14,8 +14,8 @@
 //  * bwd_dq_kernel: the forward's structure (one wave per 32 query rows, the
 //    visible K/V tiles staged in LDS); P is recomputed from lse, dP^T = V dO^T
 //    and dQ^T += K^T dS^T with dS^T fed from registers.
-//  * bwd_dkv_kernel: one wave per 32 keys (64 at d = 128) and one query
-//    head; it walks only the query blocks that can see its keys (each key's
+//  * bwd_dkv_kernel: one wave per 32 keys and one query head, two waves per
+//    SIMD; it walks only the query blocks that can see its keys (each key's
 //    visible rows are at most two intervals), accumulating dK^T and dV^T in
 //    registers. With a GQA group of one head it writes dK, dV directly;
 //    otherwise it writes fp32 partials per query head and
@@ -302,67 +302,62 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ dK, dV --
-// Workgroup: 4 waves over consecutive keys of one (batch, query head); wave w
-// owns KG groups of 32 keys, keys k0 + 32 (KG w + g) + j. The K rows of a
-// wave's keys sit in registers as B fragments, the workgroup's V rows in LDS.
-// The workgroup walks the 64-row query blocks that can see its keys through
-// double-buffered LDS stages holding Q, dO, lse and D. At d = 128 a wave owns
-// two key groups: every Q / dO fragment it reads from LDS (rows for S and dP,
-// transposed for dK and dV) then feeds both, halving the LDS bytes per MFMA
-// (with one group the kernel was bound by those reads).
+// Workgroup: NW waves over consecutive keys of one (batch, query head); wave w
+// owns the 32 keys k0 + 32 w + j. The K rows of a wave's keys sit in registers
+// as B fragments, the workgroup's V rows in LDS. The workgroup walks the
+// 64-row query blocks that can see its keys through double-buffered LDS stages
+// holding Q, dO, lse and D. Its dK^T and dV^T accumulators (32 keys x d each,
+// d / 2 registers per lane) leave room for two waves per SIMD at both head
+// sizes. At d = 128 a workgroup has 8 waves (256 keys): the stages and the
+// V tile then fill one CU's LDS with two waves on every SIMD.
 template <int D>
 struct DkvCfg {
-  static constexpr int KG = D == 128 ? 2 : 1;   // 32-key groups per wave
   static constexpr int QB = 64;                 // query rows per staged block (2 x 32)
   static constexpr int CPR = D / 8;
   static constexpr int QSZ = QB * D;            // Q (or dO) block, elements
   static constexpr int NBLK = QSZ / 512;        // 1 KiB blocks per Q (or dO) block
-  static constexpr int NW = 4;                  // waves per workgroup
-  static constexpr int KB = 32 * KG * NW;       // keys per workgroup
+  static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
+  static constexpr int KB = 32 * NW;            // keys per workgroup
   static constexpr int VSZ = KB * D;
 };
 
-// One 32-row query sub-block for one wave's KG key groups. Only the scores of
-// the rows whose bit is set in vm[g] count: bit t is the row t past the lane's
-// first row (row offsets 8 (r / 4) + r % 4 of accumulator r).
-template <int D, int KG>
+// One 32-row query sub-block for one wave's 32 keys. Only the scores of the
+// rows whose bit is set in vm count: bit t is the row t past the lane's first
+// row (row offsets 8 (r / 4) + r % 4 of accumulator r). Vs points at the
+// wave's own V rows. Read offsets (elements): the row reads of chunk c at
+// ro[0] + ((16 c) ^ ro[1]), the transposing reads of column group i, half e,
+// at to[e][0] + ((32 i) ^ to[e][1]) (one v_xad_u32 each; the XOR is the
+// swz_b permutation of the lane's row).
+template <int D>
 __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
                                           const bf16_t* __restrict__ Ds,
                                           const float* __restrict__ Ls,
                                           const float* __restrict__ Dl,
                                           const bf16_t* __restrict__ Vs,
-                                          const bf16x8 (&kf)[KG][D / 16],
-                                          f32x16 (&dk)[KG][D / 32], f32x16 (&dv)[KG][D / 32],
-                                          float cs, const uint32_t (&vm)[KG],
-                                          const int (&qad)[D / 16], const int (&qtr)[2][D / 32],
-                                          const int (&vad)[KG][D / 16], int hf) {
-  // S = Q K^T and dP = dO V^T: lane (j, hf) holds key 32 g + j and query rows
+                                          const bf16x8 (&kf)[D / 16],
+                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                          float cs, uint32_t vm, const int (&ro)[2],
+                                          const int (&to)[2][2], int hf) {
+  // S = Q K^T and dP = dO V^T: lane (j, hf) holds key j and query rows
   // 8 (r / 4) + 4 hf + r % 4 of the sub-block
-  f32x16 s[KG], dp[KG];
-#pragma unroll
-  for (int g = 0; g < KG; ++g) s[g] = dp[g] = f32x16{};
+  f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const bf16x8 qa = *(const bf16x8*)(Qs + qad[c]);
-#pragma unroll
-    for (int g = 0; g < KG; ++g) s[g] = mfma32(qa, kf[g][c], s[g]);
+    const int ad = ro[0] + ((16 * c) ^ ro[1]);
+    s = mfma32(*(const bf16x8*)(Qs + ad), kf[c], s);
   }
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const bf16x8 da = *(const bf16x8*)(Ds + qad[c]);
-#pragma unroll
-    for (int g = 0; g < KG; ++g) dp[g] = mfma32(da, *(const bf16x8*)(Vs + vad[g][c]), dp[g]);
+    const int ad = ro[0] + ((16 * c) ^ ro[1]);
+    dp = mfma32(*(const bf16x8*)(Ds + ad), *(const bf16x8*)(Vs + ad), dp);
   }
 #pragma unroll
-  for (int g = 0; g < KG; ++g) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 8 * (r >> 2) + (r & 3);
-      s[g][r] = (vm[g] >> off) & 1u ? s[g][r] : -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int off = 8 * (r >> 2) + (r & 3);
+    s[r] = (vm >> off) & 1u ? s[r] : -INFINITY;
   }
   // lse2 and D of the lane's 16 rows: 4 runs of 4 consecutive rows
-  bf16x8 pp[KG][2], ps[KG][2];
+  bf16x8 pp[2], ps[2];
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg) {
     const f32x4 l4 = *(const f32x4*)(Ls + 8 * gg + 4 * hf);
@@ -370,41 +365,35 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * gg + e;
-#pragma unroll
-      for (int g = 0; g < KG; ++g) {
-        const float pr = fast_exp2(fmaf(s[g][r], cs, -l4[e]));
-        pp[g][r >> 3][r & 7] = (bf16_t)pr;
-        ps[g][r >> 3][r & 7] = (bf16_t)(pr * (dp[g][r] - d4[e]));
-      }
+      const float pr = fast_exp2(fmaf(s[r], cs, -l4[e]));
+      pp[r >> 3][r & 7] = (bf16_t)pr;
+      ps[r >> 3][r & 7] = (bf16_t)(pr * (dp[r] - d4[e]));
     }
   }
   // dV^T += dO^T P and dK^T += Q^T dS: A from transposing reads of the dO / Q
-  // block (rows = query slots of the 16-row chunk kc), shared by the key
-  // groups; B from registers
+  // block (rows = query slots of the 16-row chunk kc); B from registers
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
+    const int t0 = to[0][0] + ((32 * i) ^ to[0][1]);
+    const int t1 = to[1][0] + ((32 * i) ^ to[1][1]);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const bf16x4 dlo = lds_read_tr(Ds + qtr[0][i] + 16 * kc * D);
-      const bf16x4 dhi = lds_read_tr(Ds + qtr[1][i] + 16 * kc * D);
+      const bf16x4 dlo = lds_read_tr(Ds + t0 + 16 * kc * D);
+      const bf16x4 dhi = lds_read_tr(Ds + t1 + 16 * kc * D);
       const bf16x8 da = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-#pragma unroll
-      for (int g = 0; g < KG; ++g) dv[g][i] = mfma32(da, pp[g][kc], dv[g][i]);
-      const bf16x4 qlo = lds_read_tr(Qs + qtr[0][i] + 16 * kc * D);
-      const bf16x4 qhi = lds_read_tr(Qs + qtr[1][i] + 16 * kc * D);
+      dv[i] = mfma32(da, pp[kc], dv[i]);
+      const bf16x4 qlo = lds_read_tr(Qs + t0 + 16 * kc * D);
+      const bf16x4 qhi = lds_read_tr(Qs + t1 + 16 * kc * D);
       const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-#pragma unroll
-      for (int g = 0; g < KG; ++g) dk[g][i] = mfma32(qa, ps[g][kc], dk[g][i]);
+      dk[i] = mfma32(qa, ps[kc], dk[i]);
     }
   }
 }
 
-// d = 64: two waves per SIMD. d = 128: one, so that the 2 x 2 x 4 accumulator
-// tiles (256 registers) live in accumulation registers beside the K fragments.
 template <int D>
-__global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_kernel(BwdArgs p) {
+__global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs p) {
   using C = DkvCfg<D>;
-  constexpr int KG = C::KG, NW = C::NW;
+  constexpr int NW = C::NW;
   // per stage: Q block, dO block, then lse2[QB] and D[QB]
   constexpr int STG_EL = 2 * C::QSZ + 4 * C::QB;  // elements (bf16 units); 2 QB floats
   __shared__ __attribute__((aligned(16))) bf16_t stage0[STG_EL];
@@ -424,19 +413,14 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
   const int hq = bh % p.Hq;
   const int kvh = hq / p.group;
   const int k0 = kbi * C::KB;
-  int key[KG];
-  bool key_ok[KG];
-  int lo1[KG], hi1[KG], lo2[KG], hi2[KG];
-#pragma unroll
-  for (int g = 0; g < KG; ++g) {
-    key[g] = k0 + 32 * (KG * w + g) + j;
-    key_ok[g] = key[g] < p.twoL;
-    // the lane's key and the query rows that see it
-    key_rows(min(key[g], p.twoL - 1), p.L, p.B, p.mask_mode, lo1[g], hi1[g], lo2[g], hi2[g]);
-    if (!key_ok[g]) {
-      hi1[g] = lo1[g];
-      hi2[g] = lo2[g];
-    }
+  // the lane's key and the query rows that see it
+  const int key = k0 + 32 * w + j;
+  const bool key_ok = key < p.twoL;
+  int lo1, hi1, lo2, hi2;
+  key_rows(min(key, p.twoL - 1), p.L, p.B, p.mask_mode, lo1, hi1, lo2, hi2);
+  if (!key_ok) {
+    hi1 = lo1;
+    hi2 = lo2;
   }
   // the workgroup's query rows: the union over its keys, as up to two ranges
   const int klast = min(k0 + C::KB, p.twoL) - 1;
@@ -472,13 +456,11 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
 
   // K rows of the lane's keys as B fragments (rows past the end read as
   // zeros); V rows of the workgroup's keys into LDS
-  bf16x8 kf[KG][D / 16];
+  bf16x8 kf[D / 16];
 #pragma unroll
-  for (int g = 0; g < KG; ++g)
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      kf[g][c] = __builtin_bit_cast(
-          bf16x8, buf_load16(rk, (uint32_t)((key[g] * rs + 16 * c + 8 * hf) * sizeof(bf16_t))));
+  for (int c = 0; c < D / 16; ++c)
+    kf[c] = __builtin_bit_cast(
+        bf16x8, buf_load16(rk, (uint32_t)((key * rs + 16 * c + 8 * hf) * sizeof(bf16_t))));
   {
     constexpr int VB = C::VSZ / 512;  // 1 KiB blocks of the V tile
 #pragma unroll
@@ -500,11 +482,14 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
   const rsrc_t rdo = make_rsrc(dobase + (size_t)hq * D, q_bytes);
   auto issue_block = [&](int it, bf16_t* st) {
     const int q0 = block_q0(it);
+    // at d = 128, rebuilt per call for the same reason as the read offsets below
+    int ln = lane;
+    if constexpr (D == 128) asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < (C::NBLK + NW - 1) / NW; ++i) {
       const int blk = w + NW * i;
       if (blk < C::NBLK) {
-        const int u = blk * 64 + lane;
+        const int u = blk * 64 + ln;
         const int row = u / C::CPR, slot = u % C::CPR;
         const uint32_t off = (uint32_t)(((q0 + row) * qs) * sizeof(bf16_t)) +
                              16 * (slot ^ swz_b<D>(row));
@@ -531,39 +516,34 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
     }
   };
 
-  // read offsets. Row reads of the Q / dO block: row i = lane % 32, chunk 2c + hf.
-  // V row reads: key row 32 (KG w + g) + j. Transposing reads of Q / dO: 16-lane
-  // group g reads rows 4 (g / 2) + lane % 16 / 4 (+ 8 e, + 16 kc) at columns
-  // 32 i + 16 (g % 2) + 4 (lane % 4).
-  int qad[D / 16], qtr[2][D / 32], vad[KG][D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    qad[c] = j * D + 8 * ((2 * c + hf) ^ swz_b<D>(j));
-#pragma unroll
-    for (int g = 0; g < KG; ++g) {
-      const int vr = 32 * (KG * w + g) + j;
-      vad[g][c] = vr * D + 8 * ((2 * c + hf) ^ swz_b<D>(vr));
-    }
-  }
+  // read offsets. Row reads of the Q / dO block (and of the wave's V rows,
+  // whose row j has the same permutation): row j, chunk (2c + hf) ^ swz_b(j).
+  // Transposing reads of Q / dO: 16-lane group g reads rows 4 (g / 2) +
+  // lane % 16 / 4 (+ 8 e, + 16 kc) at columns 32 i + 16 (g % 2) + 4 (lane % 4),
+  // chunk (4i + low) ^ swz_b(row). Both XORs split into a lane constant added
+  // to the chunk index XOR a lane constant (dkv_block).
+  int ro[2], to[2][2];
   {
+    const int sj = swz_b<D>(j);
+    ro[0] = j * D + 8 * (hf ^ (sj & 1));
+    ro[1] = 16 * (sj >> 1);
     const int low = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int row = 4 * hf + ((lane & 15) >> 2) + 8 * e;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-        qtr[e][i] = row * D + 8 * ((4 * i + low) ^ swz_b<D>(row)) + 4 * (lane & 1);
+      const int sr = swz_b<D>(row);
+      to[e][0] = row * D + 8 * (low ^ (sr & 3)) + 4 * (lane & 1);
+      to[e][1] = 32 * (sr >> 2);
     }
   }
+  const bf16_t* vrows = vtile + 32 * w * D;
 
-  f32x16 dk[KG][D / 32], dv[KG][D / 32];
+  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int g = 0; g < KG; ++g)
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      dk[g][i] = f32x16{};
-      dv[g][i] = f32x16{};
-    }
+  for (int i = 0; i < D / 32; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
 
   if (niter > 0) {
     issue_block(0, stage0);
@@ -571,9 +551,7 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
     store_ld(stage0);
   }
 #pragma unroll
-  for (int g = 0; g < KG; ++g)
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(kf[g][c]));
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(kf[c]));
   __syncthreads();
 
   auto iteration = [&](int it, auto stage_tag) {
@@ -591,17 +569,11 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int q0 = block_q0(it) + 32 * sb;
-      // each key group's visible rows as a bit mask over the rows past the
-      // lane's first row rb = q0 + 4 hf (bit t: row rb + t)
+      // the key's visible rows as a bit mask over the rows past the lane's
+      // first row rb = q0 + 4 hf (bit t: row rb + t)
       const int rb = q0 + 4 * hf;
-      uint32_t vm[KG];
-      bool see = false;
-#pragma unroll
-      for (int g = 0; g < KG; ++g) {
-        vm[g] = row_bits(lo1[g] - rb, hi1[g] - rb) | row_bits(lo2[g] - rb, hi2[g] - rb);
-        see = see | (min(hi1[g], q0 + 32) > max(lo1[g], q0)) |
-              (min(hi2[g], q0 + 32) > max(lo2[g], q0));
-      }
+      const uint32_t vm = row_bits(lo1 - rb, hi1 - rb) | row_bits(lo2 - rb, hi2 - rb);
+      const bool see = (min(hi1, q0 + 32) > max(lo1, q0)) | (min(hi2, q0 + 32) > max(lo2, q0));
       if (__builtin_amdgcn_ballot_w64(see) != 0) {
         const bf16_t* Qb = Qs + 32 * sb * D;
         const bf16_t* Db = Ds + 32 * sb * D;
@@ -610,8 +582,16 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
         // One code path serves every sub-block (a fully visible one has all
         // bits set): an unmasked copy beside it in the same loop made the
         // register allocation spill at d = 128 and ran slower at d = 64.
-        dkv_block<D, KG>(Qb, Db, Lb, Dlb, vtile, kf, dk, dv, p.scale_log2, vm, qad, qtr, vad,
-                         hf);
+        int rol[2] = {ro[0], ro[1]};
+        int tol[2][2] = {{to[0][0], to[0][1]}, {to[1][0], to[1][1]}};
+        // At d = 128 the six offset bases pass through an empty asm here, so
+        // the 16 read offsets are rebuilt next to their reads in every
+        // sub-block instead of being hoisted out of the loop: kept live, they
+        // pushed K fragments to scratch, reloaded every sub-block.
+        if constexpr (D == 128)
+          asm volatile("" : "+v"(rol[0]), "+v"(rol[1]), "+v"(tol[0][0]), "+v"(tol[0][1]),
+                       "+v"(tol[1][0]), "+v"(tol[1][1]));
+        dkv_block<D>(Qb, Db, Lb, Dlb, vrows, kf, dk, dv, p.scale_log2, vm, rol, tol, hf);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -624,38 +604,35 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 2 : 1) void bwd_dkv_k
   }
 
   // lane (j, hf) holds dK^T / dV^T rows d = 32 i + 8 (r / 4) + 4 hf + r % 4 of its key
+  if (!key_ok) return;
+  if (p.group > 1) {
+    float* dkr = p.dkp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
+    float* dvr = p.dvp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
 #pragma unroll
-  for (int g = 0; g < KG; ++g) {
-    if (!key_ok[g]) continue;
-    if (p.group > 1) {
-      float* dkr = p.dkp + (((size_t)b * p.twoL + key[g]) * p.Hq + hq) * D;
-      float* dvr = p.dvp + (((size_t)b * p.twoL + key[g]) * p.Hq + hq) * D;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          *(f32x4*)(dkr + 32 * i + 8 * gg + 4 * hf) =
-              f32x4{dk[g][i][4 * gg] * p.scale, dk[g][i][4 * gg + 1] * p.scale,
-                    dk[g][i][4 * gg + 2] * p.scale, dk[g][i][4 * gg + 3] * p.scale};
-          *(f32x4*)(dvr + 32 * i + 8 * gg + 4 * hf) =
-              f32x4{dv[g][i][4 * gg], dv[g][i][4 * gg + 1], dv[g][i][4 * gg + 2],
-                    dv[g][i][4 * gg + 3]};
-        }
-      continue;
-    }
-    bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key[g]) * p.Hkv + kvh) * D;
-    bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key[g]) * p.Hkv + kvh) * D;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
+    for (int i = 0; i < D / 32; ++i)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        const u32x2 pk = {pack_bf16x2(dk[g][i][4 * gg] * p.scale, dk[g][i][4 * gg + 1] * p.scale),
-                          pack_bf16x2(dk[g][i][4 * gg + 2] * p.scale, dk[g][i][4 * gg + 3] * p.scale)};
-        *(u32x2*)(dkr + 32 * i + 8 * gg + 4 * hf) = pk;
-        const u32x2 pv = {pack_bf16x2(dv[g][i][4 * gg], dv[g][i][4 * gg + 1]),
-                          pack_bf16x2(dv[g][i][4 * gg + 2], dv[g][i][4 * gg + 3])};
-        *(u32x2*)(dvr + 32 * i + 8 * gg + 4 * hf) = pv;
+        *(f32x4*)(dkr + 32 * i + 8 * gg + 4 * hf) =
+            f32x4{dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale,
+                  dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale};
+        *(f32x4*)(dvr + 32 * i + 8 * gg + 4 * hf) =
+            f32x4{dv[i][4 * gg], dv[i][4 * gg + 1], dv[i][4 * gg + 2],
+                  dv[i][4 * gg + 3]};
       }
+    return;
+  }
+  bf16_t* dkr = p.dk + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
+  bf16_t* dvr = p.dv + (((size_t)b * p.twoL + key) * p.Hkv + kvh) * D;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const u32x2 pk = {pack_bf16x2(dk[i][4 * gg] * p.scale, dk[i][4 * gg + 1] * p.scale),
+                        pack_bf16x2(dk[i][4 * gg + 2] * p.scale, dk[i][4 * gg + 3] * p.scale)};
+      *(u32x2*)(dkr + 32 * i + 8 * gg + 4 * hf) = pk;
+      const u32x2 pv = {pack_bf16x2(dv[i][4 * gg], dv[i][4 * gg + 1]),
+                        pack_bf16x2(dv[i][4 * gg + 2], dv[i][4 * gg + 3])};
+      *(u32x2*)(dvr + 32 * i + 8 * gg + 4 * hf) = pv;
     }
   }
 }
