@@ -9,11 +9,12 @@
 //     P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,
 //     dS = P * (dP - D),  D = rowsum(dO * O),
 //     dQ = scale dS K,    dK = scale dS^T Q.
-// Three kernels:
-//  * bwd_dsum_kernel: D per (batch, head, row).
+// Two kernels (and a reduce):
 //  * bwd_dq_kernel: the forward's structure (one wave per 32 query rows, the
-//    visible K/V tiles staged in LDS); P is recomputed from lse, dP^T = V dO^T
-//    and dQ^T += K^T dS^T with dS^T fed from registers.
+//    visible K/V tiles staged in LDS); each wave first forms D of its rows
+//    from its dO rows and O (and stores it for the next kernel); P is
+//    recomputed from lse, dP^T = V dO^T and dQ^T += K^T dS^T with dS^T fed
+//    from registers.
 //  * bwd_dkv_kernel: one wave per 32 keys and one query head, two waves per
 //    SIMD; it walks only the query blocks that can see its keys (each key's
 //    visible rows are at most two intervals), accumulating dK^T and dV^T in
@@ -36,7 +37,7 @@ struct BwdArgs {
   const bf16_t* o;
   const bf16_t* dout;
   const float* lse;  // [b, Hq, 2L], natural log
-  float* dsum;       // [b, Hq, 2L] workspace: rowsum(dO * O)
+  float* dsum;       // [b, Hq, 2L] workspace: rowsum(dO * O), from the dQ kernel
   float* dkp;        // [b, 2L, Hq, d] workspace: per-query-head dK (group > 1)
   float* dvp;        // [b, 2L, Hq, d] workspace: per-query-head dV (group > 1)
   bf16_t* dq;
@@ -46,36 +47,6 @@ struct BwdArgs {
   float scale, scale_log2;
   int nqt, gh, nhc, rt, nw;  // dQ kernel split, as in the forward
 };
-
-// ------------------------------------------------------------------ D -------
-// D = rowsum(dO * O) per (b, a, h) row: D / 8 lanes per row, each reading 16
-// bytes of dO and of O (one row per 16-byte-per-lane load: coalesced), then
-// a butterfly over those lanes.
-template <int D>
-constexpr int dsum_rows_per_block() { return 256 / (D / 8); }
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs p) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const size_t row = (size_t)blockIdx.x * dsum_rows_per_block<D>() + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  const size_t rows = (size_t)p.batch * p.twoL * p.Hq;  // (b, a, h) in [b][2L][Hq] order
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 x = *(const bf16x8*)(p.dout + row * D + 8 * part);
-    const bf16x8 y = *(const bf16x8*)(p.o + row * D + 8 * part);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
-  }
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row >= rows || part != 0) return;
-  const int h = (int)(row % p.Hq);
-  const size_t ba = row / p.Hq;
-  const int a = (int)(ba % p.twoL);
-  const int b = (int)(ba / p.twoL);
-  p.dsum[((size_t)b * p.Hq + h) * p.twoL + a] = acc;
-}
-
 
 // ------------------------------------------------------------------ dQ ------
 template <int D>
@@ -205,7 +176,24 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
   }
   const size_t rowoff = ((size_t)b * p.Hq + h) * p.twoL;
   const float lse2 = row_ok ? p.lse[rowoff + a] * kLog2e : 0.f;
-  const float dsum = row_ok ? p.dsum[rowoff + a] : 0.f;
+  // D = rowsum(dO * O) of the lane's row: its 8 chunks of 8 columns, then the
+  // other half of the row from the partner lane (rows past 2L read as zeros).
+  // Written for the dK/dV kernel, which runs after this one.
+  float dpart = 0.f;
+  {
+    const rsrc_t ro = make_rsrc(p.o + (size_t)b * p.twoL * qs + (size_t)h * D,
+                                (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t)));
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const uint32_t off = (uint32_t)((a * qs + 16 * c + 8 * hf) * sizeof(bf16_t));
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)dof[c][e], (float)ov[e], dpart);
+    }
+    dpart += __shfl_xor(dpart, 32);
+  }
+  const float dsum = row_ok ? dpart : 0.f;
+  if (row_ok && hf == 0) p.dsum[rowoff + a] = dsum;
 
   auto tile_c0 = [&](int it) { return it < n1 ? it * C::BN : r2_lo + (it - n1) * C::BN; };
 
@@ -673,10 +661,6 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
 
 template <int D>
 int launch_bwd(BwdArgs a, hipStream_t st) {
-  const size_t rows = (size_t)a.batch * a.twoL * a.Hq;
-  constexpr int rpb = dsum_rows_per_block<D>();
-  hipLaunchKernelGGL(bwd_dsum_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0,
-                     st, a);
   a.gh = D == 64 ? 1 : heads_per_wg(a.group);
   a.nhc = a.group / a.gh;
   a.rt = D == 64 ? 4 : 8 / a.gh;
