@@ -18,10 +18,11 @@
 //  * bwd_dkv_kernel: one wave per 32 keys and one query head, two waves per
 //    SIMD; it walks only the query blocks that can see its keys (each key's
 //    visible rows are at most two intervals), accumulating dK^T and dV^T in
-//    registers. With a GQA group of one head it writes dK, dV directly;
-//    otherwise it writes fp32 partials per query head and
-//    bwd_dkv_reduce_kernel sums the group's heads in a fixed order (no
-//    atomics: the result is deterministic).
+//    registers over one or more query heads of a GQA group. With a group of
+//    one head it writes dK, dV directly; otherwise it writes fp32 partials
+//    per workgroup's head set and bwd_dkv_reduce_kernel sums them in head
+//    order (no atomics: the result is deterministic).
+#include <cmath>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -46,6 +47,7 @@ struct BwdArgs {
   int batch, L, B, Hq, Hkv, twoL, group, mask_mode;
   float scale, scale_log2;
   int nqt, gh, nhc, rt, nw;  // dQ kernel split, as in the forward
+  int hpw;                   // query heads (of one GQA group) per dK/dV workgroup
 };
 
 // ------------------------------------------------------------------ dQ ------
@@ -290,11 +292,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ dK, dV --
-// Workgroup: NW waves over consecutive keys of one (batch, query head); wave w
-// owns the 32 keys k0 + 32 w + j. The K rows of a wave's keys sit in registers
-// as B fragments, the workgroup's V rows in LDS. The workgroup walks the
-// 64-row query blocks that can see its keys through double-buffered LDS stages
-// holding Q, dO, lse and D. Its dK^T and dV^T accumulators (32 keys x d each,
+// Workgroup: NW waves over consecutive keys of one batch and hpw query heads
+// of one GQA group; wave w owns the 32 keys k0 + 32 w + j. The K rows of a
+// wave's keys sit in registers as B fragments, the workgroup's V rows in LDS.
+// For each of its heads in turn, the workgroup walks the 64-row query blocks
+// that can see its keys through double-buffered LDS stages holding Q, dO, lse
+// and D, and the heads' dK^T and dV^T add up in the same registers. Its dK^T and dV^T accumulators (32 keys x d each,
 // d / 2 registers per lane) leave room for two waves per SIMD at both head
 // sizes. At d = 128 a workgroup has 8 waves (256 keys): the stages and the
 // V tile then fill one CU's LDS with two waves on every SIMD.
@@ -307,6 +310,9 @@ struct DkvCfg {
   static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
   static constexpr int KB = 32 * NW;            // keys per workgroup
   static constexpr int VSZ = KB * D;
+  // resident workgroups per CU: LDS-bound at d = 128 (132 KiB), register-bound
+  // at d = 64 (two waves per SIMD)
+  static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
 };
 
 // One 32-row query sub-block for one wave's 32 keys. Only the scores of the
@@ -394,12 +400,15 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
 
   // key blocks in increasing order (the clean keys near the start see the
   // most rows), the (batch, query head) pairs of one key block side by side
-  const int nbh = p.batch * p.Hq;
+  const int nsets = (p.group + p.hpw - 1) / p.hpw;  // head sets per KV head
+  const int nbh = p.batch * p.Hkv * nsets;
   const int kbi = blockIdx.x / nbh;
   const int bh = blockIdx.x % nbh;
-  const int b = bh / p.Hq;
-  const int hq = bh % p.Hq;
-  const int kvh = hq / p.group;
+  const int hs = bh % nsets;
+  const int kvh = (bh / nsets) % p.Hkv;
+  const int b = bh / (nsets * p.Hkv);
+  const int hq0 = kvh * p.group + hs * p.hpw;        // first query head
+  const int nh = min(p.hpw, p.group - hs * p.hpw);  // query heads, in order
   const int k0 = kbi * C::KB;
   // the lane's key and the query rows that see it
   const int key = k0 + 32 * w + j;
@@ -432,7 +441,8 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
   if (fb2 <= lb1) fb2 = lb1 + 1;  // never the same query block twice
   const int nb1 = lb1 - fb1 + 1;
   const int nb2 = lb2 >= fb2 ? lb2 - fb2 + 1 : 0;
-  const int niter = nb1 + nb2;
+  const int nq = nb1 + nb2;  // query blocks per head
+  const int niter = nq * nh;
 
   const size_t qs = (size_t)p.Hq * D, rs = (size_t)p.Hkv * D;
   const uint32_t q_bytes = (uint32_t)(((p.twoL - 1) * qs + D) * sizeof(bf16_t));
@@ -464,12 +474,18 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
   }
 
   // iteration it: query block it of the two ranges
-  auto block_q0 = [&](int it) { return (it < nb1 ? fb1 + it : fb2 + (it - nb1)) * C::QB; };
-  const size_t lrow = ((size_t)b * p.Hq + hq) * p.twoL;
-  const rsrc_t rq = make_rsrc(qbase + (size_t)hq * D, q_bytes);
-  const rsrc_t rdo = make_rsrc(dobase + (size_t)hq * D, q_bytes);
+  // iteration it: query block it % nq of head hq0 + it / nq (the blocks that
+  // see the keys are the same for every head)
+  auto block_q0 = [&](int it) {
+    const int ib = it % nq;
+    return (ib < nb1 ? fb1 + ib : fb2 + (ib - nb1)) * C::QB;
+  };
+  auto head_of = [&](int it) { return hq0 + it / nq; };
   auto issue_block = [&](int it, bf16_t* st) {
     const int q0 = block_q0(it);
+    const int hq = head_of(it);
+    const rsrc_t rq = make_rsrc(qbase + (size_t)hq * D, q_bytes);
+    const rsrc_t rdo = make_rsrc(dobase + (size_t)hq * D, q_bytes);
     // at d = 128, rebuilt per call for the same reason as the read offsets below
     int ln = lane;
     if constexpr (D == 128) asm volatile("" : "+v"(ln));
@@ -492,6 +508,7 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
   auto load_ld = [&](int it) {
     if (w == 0) {
       const int a = block_q0(it) + lane;
+      const size_t lrow = ((size_t)b * p.Hq + head_of(it)) * p.twoL;
       lval = a < p.twoL ? p.lse[lrow + a] * kLog2e : 0.f;
       dval = a < p.twoL ? p.dsum[lrow + a] : 0.f;
     }
@@ -594,8 +611,8 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
   // lane (j, hf) holds dK^T / dV^T rows d = 32 i + 8 (r / 4) + 4 hf + r % 4 of its key
   if (!key_ok) return;
   if (p.group > 1) {
-    float* dkr = p.dkp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
-    float* dvr = p.dvp + (((size_t)b * p.twoL + key) * p.Hq + hq) * D;
+    float* dkr = p.dkp + (((size_t)b * p.twoL + key) * p.Hq + hq0) * D;
+    float* dvr = p.dvp + (((size_t)b * p.twoL + key) * p.Hq + hq0) * D;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -625,8 +642,9 @@ __global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs 
   }
 }
 
-// dK, dV of a KV head = the sum of its query heads' partials, in head order.
-// One thread per (batch, key, KV head, 8 consecutive columns).
+// dK, dV of a KV head = the sum of its head sets' partials, in head order (a
+// set's partial sits in the slot of its first head). One thread per (batch,
+// key, KV head, 8 consecutive columns).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -641,7 +659,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
   float sk[8], sv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
-  for (int h = 0; h < p.group; ++h) {
+  for (int h = 0; h < p.group; h += p.hpw) {
     const f32x4 k0 = *(const f32x4*)(kp + (size_t)h * D), k1 = *(const f32x4*)(kp + (size_t)h * D + 4);
     const f32x4 v0 = *(const f32x4*)(vp + (size_t)h * D), v1 = *(const f32x4*)(vp + (size_t)h * D + 4);
 #pragma unroll
@@ -659,6 +677,29 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs p) {
                               pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7])};
 }
 
+// Query heads per dK/dV workgroup. A workgroup runs its heads one after the
+// other and sums them in registers: fewer fp32 partials are written and
+// reduced, and fewer workgroups pay the K/V load and the partial store. But
+// its work grows with them, and the launch ends no sooner than its heaviest
+// workgroup (the first keys, seen by about all 2L rows of each head). The
+// count is the largest whose heaviest workgroup stays within the mean work
+// per resident workgroup slot. Visible pairs per head: L (L + 1) under the
+// MARS mask, L (2L + 1) under causal-2L.
+template <int D>
+int dkv_heads_per_wg(const BwdArgs& a) {
+  using C = DkvCfg<D>;
+  const int ncu = mars_cu_count();
+  if (a.group <= 1 || ncu <= 0) return 1;
+  const double L = a.L;
+  const double pairs = a.mask_mode == 0 ? L * (L + 1) : L * (2 * L + 1);
+  // (64-row query block, key block) steps over all heads, per resident slot
+  const double per_slot =
+      pairs * a.batch * a.Hq / ((double)C::QB * C::KB) / ((double)ncu * C::WG_PER_CU);
+  const double heaviest = std::ceil((double)a.twoL / C::QB);  // steps of one head
+  const int h = (int)(per_slot / heaviest);
+  return h < 1 ? 1 : h > a.group ? a.group : h;
+}
+
 template <int D>
 int launch_bwd(BwdArgs a, hipStream_t st) {
   a.gh = D == 64 ? 1 : heads_per_wg(a.group);
@@ -668,7 +709,8 @@ int launch_bwd(BwdArgs a, hipStream_t st) {
   a.nqt = (a.twoL + 32 * a.rt - 1) / (32 * a.rt);
   const double nq = (double)a.batch * a.Hkv * a.nhc * a.nqt;
   const int nkb = (a.twoL + DkvCfg<D>::KB - 1) / DkvCfg<D>::KB;
-  const double nk = (double)a.batch * a.Hq * nkb;
+  a.hpw = dkv_heads_per_wg<D>(a);
+  const double nk = (double)a.batch * a.Hkv * ((a.group + a.hpw - 1) / a.hpw) * nkb;
   if (nq >= 2147483647.0 || nk >= 2147483647.0) return MARS_ERR_SHAPE;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)nq), dim3(64 * a.nw), 0, st, a);
   hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)nk), dim3(64 * DkvCfg<D>::NW), 0, st, a);

@@ -552,19 +552,11 @@ namespace {
 // into GN_TAIL-wide tiles, would still fit one round, they run that way and
 // finish well before a full round (the vocabulary order of the partials is
 // kept: main tiles first, then the tail's).
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return n;
-}
-
 // The GEMM's vocabulary tiling: main_tiles of GN entries, then tail_tiles of
 // GN_TAIL. Their sum is the number of confidence partials per row.
 void gemm_tiles(int V, int row_tiles, int* main_tiles, int* tail_tiles) {
   const int full = (V + GN - 1) / GN;
-  const int ncu = cu_count();
+  const int ncu = mars_cu_count();
   int m = full;
   if (row_tiles == 1 && ncu > 0 && full > ncu) {
     const int r = full % ncu;

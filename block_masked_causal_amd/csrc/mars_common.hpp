@@ -131,3 +131,12 @@ static inline int mars_launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? MARS_OK : MARS_ERR_LAUNCH;
 }
+
+// Compute units of the current device (0 when the query fails).
+static inline int mars_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}

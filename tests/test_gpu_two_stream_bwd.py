@@ -73,7 +73,8 @@ def check(errs, refs, ref_max):
 
 
 # (b, L, B, Hq, Hkv, d, mode) -> the oracle's max |dq|, max |dk|, max |dv| for the
-# seeded inputs of run(6000 + L, ...)
+# seeded inputs of run(6000 + L, ...); these and the FULL_* values below are printed by
+# tests/make_bwd_ref_max.py (CPU, oracle only)
 CASES = {
     (1, 256, 4, 4, 2, 64, 0): (2.146, 3.463, 6.766),
     (1, 200, 7, 2, 2, 64, 0): (1.702, 2.984, 4.474),
@@ -87,6 +88,7 @@ CASES = {
 }
 FULL_05B = (3.0405, 7.2636, 12.5279)
 FULL_7B = (3.6721, 7.2799, 13.3539)
+FULL_7B_CAUSAL = (2.8854, 6.2662, 10.9043)
 CASE_NOTES = ["several 128-row / 128-key blocks, GQA 2",
               "L not a multiple of 32: blocks straddle the streams", "B = 1", "B = L",
               "a single partial block", "causal over 2L", "batch 2, GQA 3", "GQA 4, d = 128",
@@ -125,3 +127,11 @@ def test_full_size_qwen7b_bwd_sampled_groups():
     groups, each 7 query heads over all 8192 rows (the launch the benchmark times)."""
     errs, refs = run(1003, 4, 4096, 16, 28, 4, 128, groups=[(0, 0), (3, 3)])
     check(errs, refs, FULL_7B)
+
+
+def test_full_size_qwen7b_causal_bwd_sampled_group():
+    """The 7B shape in causal-2L mode: one (batch, KV head) group. On a 256-CU GPU the
+    dK/dV launch gives each workgroup all 7 query heads of the group in turn (the MARS
+    case above gets head sets of 3, 3 and 1), so both multi-head forms are compared."""
+    errs, refs = run(1004, 4, 4096, 16, 28, 4, 128, mode=1, groups=[(2, 1)])
+    check(errs, refs, FULL_7B_CAUSAL)
