@@ -131,8 +131,12 @@ constexpr float kLazyRescale = 8.0f;
 // One 64-key tile for one wave (32 query rows): S^T = K Q^T, online softmax,
 // O^T += V^T P^T. Lane (j, hf) holds keys kb + 32n + 8(r/4) + (r%4) of its
 // row. kad[c] / vad[i] are the lane's K and V^T read offsets inside a tile.
-// MASKED: only the keys whose bit is set in vm0 (half 0) or vm1 (half 1)
-// count (bit 8 (r / 4) + r % 4 of a half is the lane's score r).
+// masked (wave-uniform): only the keys whose bit is set in vm0 (half 0) or
+// vm1 (half 1) count (bit 8 (r / 4) + r % 4 of a half is the lane's score r).
+// Full and partial tiles share this one body, with the per-key test under a
+// branch: as two inlined bodies, the two paths kept the output tuple in
+// different registers, and every full tile copied all of it out and back
+// (64 v_mov_b64 behind a wait for the last products) where they merged.
 //
 // The tile is worked as two 32-key halves in a software pipeline, so that a
 // wave always has matrix work next to its vector work: the scores of half 1
@@ -140,12 +144,12 @@ constexpr float kLazyRescale = 8.0f;
 // P V products run while half 1's probabilities are formed. Each half keeps
 // the lazy running maximum; when half 1 raises it, the output is rescaled
 // after half 0's products (which were formed with the old maximum).
-template <int D, bool MASKED>
+template <int D>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
                                           const bf16_t* __restrict__ Vs,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                          float& m, float& l, float cs, uint32_t vm0,
-                                          uint32_t vm1, const int (&kad)[D / 16],
+                                          float& m, float& l, float cs, bool masked,
+                                          uint32_t vm0, uint32_t vm1, const int (&kad)[D / 16],
                                           const int (&vad)[D / 32]) {
   auto qk = [&](int n) {
     f32x16 acc = f32x16{};
@@ -157,7 +161,7 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ Ks,
     return acc;
   };
   auto mask = [&](f32x16& sv, int n) {
-    if constexpr (MASKED) {
+    if (masked) {
       // tie the mask to the scores so that the per-key tests are computed
       // after the products, not hoisted above them with every result held live
       uint32_t vm = n == 0 ? vm0 : vm1;
@@ -397,9 +401,9 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
     const int t_lo = max(c0, lim_lo), t_hi = min(c0 + C::BN, lim_hi);
     const bool need = wave_live && ((t_lo < w1_hi) | ((t_lo < w2_hi) & (w2_lo < t_hi)));
     if (need) {
-      if (in_r1 && c0 + C::BN - 1 < w_full) {
-        tile_step<D, false>(Ks, Vs, qf, o, m, l, p.scale_log2, 0u, 0u, kad, vad);
-      } else {
+      const bool full = in_r1 && c0 + C::BN - 1 < w_full;  // wave-uniform
+      uint32_t vm0 = 0u, vm1 = 0u;
+      if (!full) {
         // the row's visible intervals clipped to the staged range, as one bit
         // mask per 32-key half (bit t: key t of the half past the lane's first
         // key kb). One masked code path serves every partial tile: per-kind
@@ -408,10 +412,10 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
         const int hi_a = min(hi1, lim_hi) - kb;
         const int lo_b = max(lo2, lim_lo) - kb;
         const int hi_b = min(hi2, lim_hi) - kb;
-        const uint32_t vm0 = row_bits(0, hi_a) | row_bits(lo_b, hi_b);
-        const uint32_t vm1 = row_bits(-32, hi_a - 32) | row_bits(lo_b - 32, hi_b - 32);
-        tile_step<D, true>(Ks, Vs, qf, o, m, l, p.scale_log2, vm0, vm1, kad, vad);
+        vm0 = row_bits(0, hi_a) | row_bits(lo_b, hi_b);
+        vm1 = row_bits(-32, hi_a - 32) | row_bits(lo_b - 32, hi_b - 32);
       }
+      tile_step<D>(Ks, Vs, qf, o, m, l, p.scale_log2, !full, vm0, vm1, kad, vad);
     }
 
     // the next stage has landed (the barrier waits for this wave's direct
