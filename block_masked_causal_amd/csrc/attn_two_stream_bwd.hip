@@ -88,11 +88,14 @@ __device__ __forceinline__ void dq_tile(const bf16_t* __restrict__ Ks,
       const bf16x8 va = *(const bf16x8*)(Vs + kad[c] + 32 * n * D);
       dp = mfma32(va, dof[c], dp);
     }
+    // the per-key test only where some lane's keys are not all visible (bits
+    // 8 (r / 4) + r % 4 are the ones in use)
+    if (__builtin_amdgcn_ballot_w64((vm[n] & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 8 * (r >> 2) + (r & 3);
-      s[r] = (vm[n] >> off) & 1u ? s[r] : -INFINITY;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s[r] = (vm[n] >> off) & 1u ? s[r] : -INFINITY;
+      }
     bf16x8 ds[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -345,11 +348,14 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
     const int ad = ro[0] + ((16 * c) ^ ro[1]);
     dp = mfma32(*(const bf16x8*)(Ds + ad), *(const bf16x8*)(Vs + ad), dp);
   }
+  // the per-row test only where some lane's rows are not all visible (bits
+  // 8 (r / 4) + r % 4 are the ones in use)
+  if (__builtin_amdgcn_ballot_w64((vm & 0x0F0F0F0Fu) != 0x0F0F0F0Fu) != 0)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int off = 8 * (r >> 2) + (r & 3);
-    s[r] = (vm >> off) & 1u ? s[r] : -INFINITY;
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + (r & 3);
+      s[r] = (vm >> off) & 1u ? s[r] : -INFINITY;
+    }
   // lse2 and D of the lane's 16 rows: 4 runs of 4 consecutive rows
   bf16x8 pp[2], ps[2];
 #pragma unroll
