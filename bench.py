@@ -165,8 +165,11 @@ def roofline(bound, achieved, peak, unit, traffic=None, algorithmic_bytes=None):
     return r
 
 
-def timed(torch, fn, reps=5, warm=2):
-    """Mean ms of `reps` back-to-back launches of fn (one event pair around them)."""
+def timed(torch, fn, reps=10, warm=5):
+    """Mean ms of `reps` back-to-back launches of fn (one event pair around them), after
+    `warm` untimed launches: the shader clock drops while the host builds the inputs,
+    and two warm launches of a 4 ms kernel left the first timed ones 5-8% slower than
+    the steady state."""
     for _ in range(warm):
         fn()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
