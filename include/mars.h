@@ -213,7 +213,10 @@ int mars_block_freeze(const void* k_rows, const void* v_rows, void* k_cache, voi
  * n_kv_heads, head_dim) bytes of device memory.
  * Errors: as mars_attn_two_stream; MARS_ERR_DTYPE for fp32; MARS_ERR_UNSUPPORTED
  * for other head sizes; MARS_ERR_WORKSPACE if the workspace is missing or
- * small. Deterministic: no atomics.
+ * small. Deterministic: no atomics, so repeated calls on one GPU give the same
+ * bits. (How many query heads one dK/dV workgroup sums in registers follows
+ * the GPU's compute-unit count, so the summation order of dk, dv can differ
+ * between GPUs of different sizes.)
  */
 int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v, const void* o,
                              const void* d_o, const float* lse, void* dq, void* dk, void* dv,
@@ -223,8 +226,9 @@ int mars_attn_two_stream_bwd(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, void* stream);
 
 /* Workspace bytes mars_attn_two_stream_bwd needs (0 on bad sizes): the rowsum
- * per (batch, query head, row), plus fp32 dK/dV partials per query head when
- * n_q_heads > n_kv_heads (they are summed per KV head in head order). */
+ * per (batch, query head, row), plus room for fp32 dK/dV partials of every query
+ * head when n_q_heads > n_kv_heads (one partial per set of consecutive query
+ * heads that a workgroup serves; they are summed per KV head in head order). */
 size_t mars_attn_two_stream_bwd_workspace_bytes(int32_t batch, int32_t L, int32_t n_q_heads,
                                                 int32_t n_kv_heads, int32_t head_dim);
 
