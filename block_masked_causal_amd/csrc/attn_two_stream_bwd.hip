@@ -16,7 +16,7 @@
 //    recomputed from lse, dP^T = V dO^T and dQ^T += K^T dS^T with dS^T fed
 //    from registers.
 //  * bwd_dkv_kernel: one wave per 32 keys and one query head, two waves per
-//    SIMD; it walks only the query blocks that can see its keys (each key's
+//    SIMD at d = 128 and three at d = 64; it walks only the query blocks that can see its keys (each key's
 //    visible rows are at most two intervals), accumulating dK^T and dV^T in
 //    registers over one or more query heads of a GQA group. With a group of
 //    one head it writes dK, dV directly; otherwise it writes fp32 partials
@@ -301,9 +301,10 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdArgs p) {
 // For each of its heads in turn, the workgroup walks the 64-row query blocks
 // that can see its keys through double-buffered LDS stages holding Q, dO, lse
 // and D, and the heads' dK^T and dV^T add up in the same registers. Its dK^T and dV^T accumulators (32 keys x d each,
-// d / 2 registers per lane) leave room for two waves per SIMD at both head
-// sizes. At d = 128 a workgroup has 8 waves (256 keys): the stages and the
-// V tile then fill one CU's LDS with two waves on every SIMD.
+// d / 2 registers per lane) leave room for two waves per SIMD at d = 128 and
+// three at d = 64. At d = 128 a workgroup has 8 waves (256 keys): the stages
+// and the V tile then fill one CU's LDS with two waves on every SIMD. At d = 64
+// three 4-wave workgroups share a CU (49 KiB of LDS each).
 template <int D>
 struct DkvCfg {
   static constexpr int QB = 64;                 // query rows per staged block (2 x 32)
@@ -313,9 +314,9 @@ struct DkvCfg {
   static constexpr int NW = D == 128 ? 8 : 4;   // waves per workgroup
   static constexpr int KB = 32 * NW;            // keys per workgroup
   static constexpr int VSZ = KB * D;
-  // resident workgroups per CU: LDS-bound at d = 128 (132 KiB), register-bound
-  // at d = 64 (two waves per SIMD)
-  static constexpr int WG_PER_CU = D == 128 ? 1 : 2;
+  // resident workgroups per CU: LDS-bound at d = 128 (132 KiB); three waves per
+  // SIMD at d = 64 (168 registers, 49 KiB of LDS each)
+  static constexpr int WG_PER_CU = D == 128 ? 1 : 3;
 };
 
 // One 32-row query sub-block for one wave's 32 keys. Only the scores of the
@@ -391,7 +392,7 @@ __device__ __forceinline__ void dkv_block(const bf16_t* __restrict__ Qs,
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * DkvCfg<D>::NW, 2) void bwd_dkv_kernel(BwdArgs p) {
+__global__ __launch_bounds__(64 * DkvCfg<D>::NW, D == 64 ? 3 : 2) void bwd_dkv_kernel(BwdArgs p) {
   using C = DkvCfg<D>;
   constexpr int NW = C::NW;
   // per stage: Q block, dO block, then lse2[QB] and D[QB]
