@@ -446,9 +446,10 @@ __global__ __launch_bounds__(512, 2) void two_stream_bf16_kernel(TwoStreamArgs p
 template <int D>
 int launch_bf16(TwoStreamArgs a, hipStream_t st) {
   using C = Cfg<D>;
-  // One head x 4 row tiles per workgroup at both head sizes: three 4-wave
-  // workgroups share a CU at d = 64, two at d = 128 (the kernel is bound by
-  // latency and needs the waves resident). At d = 128 this measured 8% faster
+  // One head x 4 row tiles per workgroup at both head sizes: four 4-wave
+  // workgroups share a CU at d = 64 (123 VGPRs, 32 KiB of LDS each), two at
+  // d = 128 (200 VGPRs; the kernel is bound by latency and needs the waves
+  // resident). At d = 128 this measured 8% faster
   // than packing the 7 GQA heads of a K/V head into one 7-wave workgroup,
   // which left one SIMD of every CU with a single wave; the heads of a K/V head
   // still run side by side on one XCD and share its L2.
